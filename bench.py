@@ -1,0 +1,291 @@
+"""Benchmark: effective bandwidth of a BMMC permutation on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one bmmc_execute of the planned permutation over the whole array
+(input resident in HBM).  Effective bandwidth = (bytes read + bytes written)
+/ time, with each element read once and written once ("A kernel that is
+correct": effective bandwidth; 2 x 4096^2 x 4 bytes for the transpose), GB =
+1e9.  The copy ceiling (bmmc_copy of the same bytes, same buffers, same
+protocol) is timed in the same run.
+
+Residency: by default the K steps rotate over enough input/output buffer
+pairs that the working set is at least 1 GiB, four times the 256 MB Infinity
+Cache, so every step streams from and to HBM; --warm reuses one pair (the
+pages' protocol of repeating one launch), which lets small arrays sit in the
+cache.
+
+Prints ONE JSON line.  The CPU baseline is the oracle (oracle/), timed on a
+bounded sample on the host cores, for context only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bmmc_affine_index_amd as bm  # noqa: E402
+from bmmc_affine_index_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 1000 * 1000
+WORKLOAD_NAMES = {
+    "c1a": "bmmc_random_n20_int32",
+    "c1b": "bitreverse_n20_int32",
+    "c2": "transpose4096x4096_fp32_n24",
+    "c3": "bitreverse_n28_int32",
+    "c4": "bmmc_random_n30_int32",
+    "c5": "random_bpc_n27_16B_records",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt")
+
+
+def kernel_source_digest() -> str:
+    """Digest of the sources that decide what the kernels read and write."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bmmc_affine_index_amd", "csrc")
+    for rel in sorted(["plan.cpp", "gf2.h", "kernels/tiled.hip", "kernels/chunk.hip",
+                       "kernels/copy.hip", "kernels/common.h"]):
+        with open(os.path.join(csrc, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    path = TRAFFIC_FILE % workload
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def lib_accepts(n: int):
+    def accept(rows):
+        h = bm.bmmc_plan_create(n, rows, 0, 4)
+        if h:
+            bm.bmmc_plan_destroy(h)
+        return bool(h)
+    return accept
+
+
+def time_loop(torch, fn, bufs, steps, warmup, stream):
+    """Warm up, then time exactly `steps` calls with events on `stream`."""
+    for k in range(warmup):
+        fn(*bufs[k % len(bufs)])
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        fn(*bufs[k % len(bufs)])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def per_launch_ms(torch, fn, bufs, reps, stream):
+    """Median/min/max of individually event-timed launches."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(*bufs[k % len(bufs)])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2], ms[0], ms[-1]
+
+
+def cpu_baseline(A, c, x, budget_s: float):
+    """The oracle, as it stands, on the host cores: repeated full-array
+    scatters (or index ranges for big arrays) for about budget_s seconds."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n = len(A)
+    N = 1 << n
+    elem = x.nbytes >> n
+    out = np.empty_like(x)
+    # one slice of at most 2^24 indices per call keeps each call short
+    span = min(N, 1 << 24)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        lo = (done * span) % N
+        oracle.apply_range(A, c, x, out, lo, lo + span, threads=threads)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 64:
+            break
+    moved = 2.0 * done * span * elem
+    return {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d oracle calls of 2^%d consecutive input indices each (%.1f s, "
+                      "%d threads), same matrix and data" % (done, span.bit_length() - 1, el,
+                                                             threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--perm", type=int, default=0, help="c5: permutation index 0..31")
+    ap.add_argument("--route", default="auto", choices=["auto", "naive", "two_pass", "fused"])
+    ap.add_argument("--tile-log2", type=int, default=0)
+    ap.add_argument("--iters-log2", type=int, default=0)
+    ap.add_argument("--no-swizzle", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="reuse one buffer pair")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    bm.lib()  # fails loudly when the HIP library is missing
+
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    n, elem = w.n, w.elem_bytes
+    A, c = wl.workload_matrix(name, accept=lib_accepts(n), perm_index=args.perm)
+    x = wl.workload_data(name)
+    nbytes = elem << n
+    route = {"auto": bm.ROUTE_AUTO, "naive": bm.ROUTE_NAIVE, "two_pass": bm.ROUTE_TWO_PASS,
+             "fused": bm.ROUTE_FUSED}[args.route]
+
+    t0 = time.perf_counter()
+    plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
+                   no_swizzle=args.no_swizzle, iters_log2=args.iters_log2)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    if name == "c4" and route == bm.ROUTE_TWO_PASS:
+        assert plan.info.passes == 2
+
+    pairs = 1 if args.warm else max(1, -(-(1 << 30) // (2 * nbytes)))
+    raw = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    ins = [raw] + [raw.clone() for _ in range(pairs - 1)]
+    outs = [torch.empty_like(raw) for _ in range(pairs)]
+    bufs = list(zip(ins, outs))
+    stream = torch.cuda.current_stream()
+    s_handle = int(stream.cuda_stream)
+
+    def step(i, o):
+        st = bm.bmmc_execute(plan.handle, i, o, s_handle)
+        if st != bm.OK:
+            raise bm.BmmcError(st, "bmmc_execute")
+
+    def copy(i, o):
+        st = bm.bmmc_copy(i, o, nbytes, s_handle)
+        if st != bm.OK:
+            raise bm.BmmcError(st, "bmmc_copy")
+
+    ms = time_loop(torch, step, bufs, args.steps, args.warmup, stream)
+    ms_copy = time_loop(torch, copy, bufs, args.steps, args.warmup, stream)
+    med, mn, mx = per_launch_ms(torch, step, bufs, 20, stream)
+    cmed, _, _ = per_launch_ms(torch, copy, bufs, 20, stream)
+
+    algo_bytes = 2.0 * nbytes
+    value = algo_bytes / (ms * 1e-3) / 1e9
+    copy_gbs = algo_bytes / (ms_copy * 1e-3) / 1e9
+
+    parity = "skipped"
+    if not args.no_check:
+        step(*bufs[0])
+        torch.cuda.synchronize()
+        got = outs[0].cpu().numpy().view(x.dtype).reshape(x.shape)
+        import oracle
+        if n <= 24:
+            want = oracle.apply(A, c, x, threads=max(1, min(16, os.cpu_count() or 1)))
+            ok = np.array_equal(got.view(np.uint8), want.view(np.uint8))
+            parity = "bit-exact vs oracle (all %d elements)" % (1 << n) if ok else "MISMATCH"
+        else:
+            rng = np.random.Generator(np.random.PCG64(1))
+            idx = rng.integers(0, 1 << n, size=1 << 20, dtype=np.uint64)
+            bad, _ = oracle.check_sampled(A, c, x, got, idx)
+            parity = ("bit-exact vs oracle (2^20 sampled elements)" if bad == 0
+                      else "MISMATCH (%d of 2^20 samples)" % bad)
+        del got
+        if parity.startswith("MISMATCH"):
+            print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
+
+    traffic = read_traffic(name)
+    passes = plan.info.passes
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(algo_bytes / (ms * 1e-3) / 1e9, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+    }
+    if passes > 1:
+        roofline["kernel"] = "both passes of the two-pass plan (one step)"
+
+    result = {
+        "metric": "effective GB/s (bytes read+written / time) and fraction of copy ceiling",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {1: "u8", 2: "u16", 4: "u32", 8: "u64", 16: "u128"}[plan.info.unit_bytes],
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[name] + ("_perm%d" % args.perm if name == "c5" else ""),
+            "n": n, "elem_bytes": elem, "bytes_per_step": int(algo_bytes),
+            "residency": ("one buffer pair, repeated (cache-warm)" if args.warm else
+                          "%d rotating buffer pairs, %.2f GiB working set (HBM)"
+                          % (pairs, 2 * pairs * nbytes / 2**30)),
+            "plan": plan.describe(),
+        },
+        "frac_of_copy": round(value / copy_gbs, 4),
+        "copy_ceiling_gbs": round(copy_gbs, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "launch_ms": {"median": round(med, 5), "min": round(mn, 5), "max": round(mx, 5),
+                      "copy_median": round(cmed, 5)},
+        "plan_create_us": round(plan_us, 1),
+        "parity": parity,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(A, c, x, args.cpu_budget)
+    print(json.dumps(result))
+    sys.stdout.flush()
+    if parity.startswith("MISMATCH"):
+        sys.exit(3)
+
+
+if __name__ == "__main__":
+    main()

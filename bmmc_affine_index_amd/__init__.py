@@ -1,1 +1,307 @@
-"""MI355X-native BMMC index permutations (placeholder; the binding follows)."""
+"""MI355X-native BMMC index permutations: out[A.i XOR c] = in[i].
+
+A thin ctypes binding over ``libbmmc.so`` (built from ``csrc/`` by
+``bmmc_affine_index_amd.build``).  The functions named like the C ABI
+(``bmmc_plan_create``, ``bmmc_execute``, ``bmmc_copy``, ...) only marshal
+arguments; every step of the permutation runs in the library's HIP kernels.
+There is no CPU fallback: if the library is missing, every call raises.
+
+Matrices are n row masks (``A[r]`` = mask of input bits feeding output bit r;
+bit 0 = least significant index bit), as in include/bmmc.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbmmc.so")
+
+# status codes (include/bmmc.h)
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_SINGULAR = 2
+ERR_UNSUPPORTED = 3
+ERR_ALIAS = 4
+ERR_OUT_OF_MEMORY = 5
+ERR_HIP = 6
+
+KIND_IDENTITY, KIND_BPC, KIND_TILED, KIND_GENERAL = 0, 1, 2, 3
+KIND_NAMES = {0: "identity", 1: "bpc", 2: "tiled", 3: "general"}
+ROUTE_AUTO, ROUTE_NAIVE, ROUTE_TWO_PASS, ROUTE_FUSED = 0, 1, 2, 3
+ROUTE_NAMES = {0: "auto", 1: "naive", 2: "two_pass", 3: "fused"}
+KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE = 0, 1, 2, 3
+
+MAX_N = 32
+MAX_BITS = 36
+MAX_TILE = 8
+MAX_PASSES = 2
+
+EXPORTED = (
+    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_copy",
+    "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
+    "bmmc_plan_get_factor", "bmmc_plan_get_pass",
+)
+
+
+class bmmc_plan_options(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int), ("tile_log2", ctypes.c_int),
+                ("no_swizzle", ctypes.c_int), ("iters_log2", ctypes.c_int)]
+
+
+class bmmc_plan_info(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("elem_bytes", ctypes.c_int), ("kind", ctypes.c_int),
+                ("route", ctypes.c_int), ("passes", ctypes.c_int),
+                ("unit_bytes", ctypes.c_int), ("unit_bits", ctypes.c_int),
+                ("tile_log2", ctypes.c_int), ("n_over", ctypes.c_int),
+                ("scratch_bytes", ctypes.c_size_t)]
+
+
+class bmmc_pass_desc(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("unit_log2", ctypes.c_int32),
+                ("nbits", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("chunk_log2", ctypes.c_int32), ("blk_bits", ctypes.c_int32),
+                ("iters_log2", ctypes.c_int32), ("unit_xor", ctypes.c_int32),
+                ("out_c", ctypes.c_uint64), ("lds_c", ctypes.c_uint32),
+                ("lds_bytes", ctypes.c_uint32),
+                ("in_blk", ctypes.c_uint64 * MAX_BITS), ("out_blk", ctypes.c_uint64 * MAX_BITS),
+                ("lds_blk", ctypes.c_uint32 * MAX_BITS),
+                ("in_h", ctypes.c_uint64 * MAX_TILE), ("out_g", ctypes.c_uint64 * MAX_TILE),
+                ("lds_wr_h", ctypes.c_uint32 * MAX_TILE),
+                ("lds_wr_lo", ctypes.c_uint32 * MAX_TILE),
+                ("lds_rd", ctypes.c_uint32 * (2 * MAX_TILE))]
+
+
+class BmmcError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = _status_text(status)
+        super().__init__("%s%s (status %d)" % (what + ": " if what else "", msg, status))
+
+
+_lib = None
+
+
+def library_loaded() -> bool:
+    return _lib is not None
+
+
+def lib():
+    """The loaded libbmmc.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libbmmc.so is missing at %s: build it with "
+            "`python -m bmmc_affine_index_amd.build` (there is no fallback path)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    L.bmmc_plan_create.argtypes = [ctypes.c_int, u64p, ctypes.c_uint64, ctypes.c_size_t]
+    L.bmmc_plan_create.restype = ctypes.c_void_p
+    L.bmmc_plan_create_ex.argtypes = [ctypes.c_int, u64p, ctypes.c_uint64, ctypes.c_size_t,
+                                      ctypes.POINTER(bmmc_plan_options)]
+    L.bmmc_plan_create_ex.restype = ctypes.c_void_p
+    L.bmmc_execute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    L.bmmc_execute.restype = ctypes.c_int
+    L.bmmc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.bmmc_copy.restype = ctypes.c_int
+    L.bmmc_plan_destroy.argtypes = [ctypes.c_void_p]
+    L.bmmc_plan_destroy.restype = None
+    L.bmmc_last_error.argtypes = []
+    L.bmmc_last_error.restype = ctypes.c_int
+    L.bmmc_status_string.argtypes = [ctypes.c_int]
+    L.bmmc_status_string.restype = ctypes.c_char_p
+    L.bmmc_plan_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(bmmc_plan_info)]
+    L.bmmc_plan_get_info.restype = ctypes.c_int
+    L.bmmc_plan_get_factor.argtypes = [ctypes.c_void_p, ctypes.c_int, u64p, u64p]
+    L.bmmc_plan_get_factor.restype = ctypes.c_int
+    L.bmmc_plan_get_pass.argtypes = [ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.POINTER(bmmc_pass_desc)]
+    L.bmmc_plan_get_pass.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().bmmc_status_string(int(status)).decode()
+    except Exception:  # library missing: still report the code
+        return "status"
+
+
+def _rows(A: Sequence[int]):
+    n = len(A)
+    arr = (ctypes.c_uint64 * max(n, 1))(*[int(a) for a in A])
+    return n, arr
+
+
+def _ptr(x) -> int:
+    """Device address of a torch tensor, or an int address as given."""
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    raise TypeError("expected a device tensor or an address")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream)
+        except ImportError:
+            pass
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# C-ABI names, marshalling only
+# ---------------------------------------------------------------------------
+
+def bmmc_plan_create(n: int, A: Sequence[int], c: int, elem_bytes: int) -> int:
+    """Plan handle (an address) or 0; the reason of a 0 is bmmc_last_error()."""
+    _, arr = _rows(A)
+    return lib().bmmc_plan_create(int(n), arr, int(c), int(elem_bytes)) or 0
+
+
+def bmmc_plan_create_ex(n: int, A: Sequence[int], c: int, elem_bytes: int,
+                        route: int = ROUTE_AUTO, tile_log2: int = 0, no_swizzle: int = 0,
+                        iters_log2: int = 0) -> int:
+    _, arr = _rows(A)
+    opt = bmmc_plan_options(route, tile_log2, no_swizzle, iters_log2)
+    return lib().bmmc_plan_create_ex(int(n), arr, int(c), int(elem_bytes),
+                                     ctypes.byref(opt)) or 0
+
+
+def bmmc_execute(plan: int, inp, out, stream=None) -> int:
+    return lib().bmmc_execute(plan, _ptr(inp), _ptr(out), _stream(stream))
+
+
+def bmmc_copy(inp, out, nbytes: int, stream=None) -> int:
+    return lib().bmmc_copy(_ptr(inp), _ptr(out), int(nbytes), _stream(stream))
+
+
+def bmmc_plan_destroy(plan: int) -> None:
+    if plan:
+        lib().bmmc_plan_destroy(plan)
+
+
+def bmmc_last_error() -> int:
+    return lib().bmmc_last_error()
+
+
+def bmmc_status_string(status: int) -> str:
+    return lib().bmmc_status_string(int(status)).decode()
+
+
+def bmmc_plan_get_info(plan: int) -> bmmc_plan_info:
+    info = bmmc_plan_info()
+    st = lib().bmmc_plan_get_info(plan, ctypes.byref(info))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_get_info")
+    return info
+
+
+def bmmc_plan_get_factor(plan: int, pass_index: int, n: int):
+    A = (ctypes.c_uint64 * n)()
+    c = ctypes.c_uint64()
+    st = lib().bmmc_plan_get_factor(plan, int(pass_index), A, ctypes.byref(c))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_get_factor")
+    return [int(a) for a in A], int(c.value)
+
+
+def bmmc_plan_get_pass(plan: int, pass_index: int) -> bmmc_pass_desc:
+    d = bmmc_pass_desc()
+    st = lib().bmmc_plan_get_pass(plan, int(pass_index), ctypes.byref(d))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_get_pass")
+    return d
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrapper
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owns a bmmc_plan; ``plan(inp, out)`` runs it on device tensors."""
+
+    def __init__(self, n: int, A: Sequence[int], c: int, elem_bytes: int,
+                 route: int = ROUTE_AUTO, tile_log2: int = 0, no_swizzle: bool = False,
+                 iters_log2: int = 0):
+        self.n, self.elem_bytes = int(n), int(elem_bytes)
+        self.A, self.c = [int(a) for a in A], int(c)
+        self.handle = bmmc_plan_create_ex(n, A, c, elem_bytes, route, tile_log2,
+                                          int(bool(no_swizzle)), iters_log2)
+        if not self.handle:
+            raise BmmcError(bmmc_last_error(), "bmmc_plan_create")
+        self.info = bmmc_plan_get_info(self.handle)
+
+    @property
+    def nbytes(self) -> int:
+        return self.elem_bytes << self.n
+
+    def passes(self):
+        return [bmmc_plan_get_pass(self.handle, k) for k in range(self.info.passes)]
+
+    def factors(self):
+        return [bmmc_plan_get_factor(self.handle, k, self.n) for k in range(self.info.passes)]
+
+    def __call__(self, inp, out, stream=None) -> None:
+        for t in (inp, out):
+            if hasattr(t, "is_cuda"):
+                if not t.is_cuda or not t.is_contiguous():
+                    raise ValueError("tensors must be contiguous device tensors")
+                if t.numel() * t.element_size() != self.nbytes:
+                    raise ValueError("tensor holds %d bytes, the plan moves %d"
+                                     % (t.numel() * t.element_size(), self.nbytes))
+        st = bmmc_execute(self.handle, inp, out, stream)
+        if st != OK:
+            raise BmmcError(st, "bmmc_execute")
+
+    def close(self) -> None:
+        if getattr(self, "handle", 0):
+            bmmc_plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def describe(self) -> dict:
+        i = self.info
+        return {"n": i.n, "elem_bytes": i.elem_bytes, "kind": KIND_NAMES[i.kind],
+                "route": ROUTE_NAMES[i.route], "passes": i.passes, "unit_bytes": i.unit_bytes,
+                "unit_bits": i.unit_bits, "tile_log2": i.tile_log2, "n_over": i.n_over,
+                "scratch_bytes": i.scratch_bytes}
+
+
+def copy(inp, out, nbytes: Optional[int] = None, stream=None) -> None:
+    if nbytes is None:
+        nbytes = inp.numel() * inp.element_size()
+    st = bmmc_copy(inp, out, nbytes, stream)
+    if st != OK:
+        raise BmmcError(st, "bmmc_copy")
+
+
+def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw):
+    """out[A.i XOR c] = inp[i] over the first axis of a contiguous device
+    tensor with 2^n rows (a row is one element)."""
+    import torch
+    n = len(A)
+    if inp.shape[0] != (1 << n):
+        raise ValueError("first axis must have 2^n entries")
+    elem = inp.numel() * inp.element_size() >> n
+    if out is None:
+        out = torch.empty_like(inp)
+    Plan(n, A, c, elem, **plan_kw)(inp, out, stream)
+    return out

@@ -1,0 +1,108 @@
+// chunk.hip -- passes that move whole chunks without LDS (gfx950).
+//
+// Two users:
+//  * the segment relabel of a two-pass plan, and complement-only maps
+//    (A = I, c != 0): chunks of up to 16 bytes move as units; the complement's
+//    low bits permute the units inside a chunk ("Efficient GPU Implementation
+//    of Affine Index Permutations on Arrays", introduction: the first of the
+//    two tiled factors is applied first; its factor T2 here keeps every
+//    2^t-unit segment contiguous, so reads and writes are both coalesced);
+//  * the naive pass, with one-unit chunks: each lane reads consecutive input
+//    and scatters to A.i XOR c (the appendix's naive bit-reversal kernel
+//    computes the output address from the input address the same way;
+//    reading in order keeps the loads coalesced and leaves the scatter to the
+//    stores).
+//
+// The output offset of chunk index x is XOR over its set bits of out_blk[k],
+// XOR out_c: the lane's low 8 bits are folded once per thread, the rest is
+// wave-uniform.
+#include "../launch.h"
+#include "common.h"
+
+namespace bmmc {
+
+constexpr int kChunkNTL = 8;   // 256 threads
+constexpr int kChunkCPTL = 2;  // 4 chunks per thread
+
+template <int UL, int WL>
+__global__ void __launch_bounds__(1 << kChunkNTL)
+    bmmc_chunk_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                      const bmmc_pass_desc d, uint64_t blk0) {
+    constexpr int U = 1 << UL;
+    constexpr int W = 1 << WL;
+    constexpr int CB = U << WL;
+    constexpr int CPT = 1 << kChunkCPTL;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nchunks = uint64_t(1) << d.blk_bits;
+    const uint64_t first = (blk0 + blockIdx.x) << (kChunkNTL + kChunkCPTL);
+    const uint64_t lane_off = dev::xor_bits_lane<kChunkNTL>(d.out_blk, tid);
+
+    dev::Chunk<CB> v[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint64_t x = first + ((uint64_t)k << kChunkNTL) + tid;
+        if (x < nchunks) v[k] = dev::gload<CB>(in + x * CB);
+    }
+    const uint32_t ux = (uint32_t)d.unit_xor;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint64_t xu = first + ((uint64_t)k << kChunkNTL);
+        const uint64_t x = xu + tid;
+        if (x >= nchunks) continue;
+        dev::Chunk<CB> c = v[k];
+        if constexpr (WL > 0) {
+            // unit e of the output chunk is unit e XOR ux of the input chunk:
+            // one butterfly stage per set bit of ux (ux is wave-uniform)
+#pragma unroll
+            for (int b = 0; b < WL; ++b) {
+                if ((ux >> b) & 1u) {
+                    dev::Chunk<CB> r;
+                    dev::zero(r);
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        dev::put_unit<CB, U>(r, e, dev::get_unit<CB, U>(c, e ^ (1 << b)));
+                    c = r;
+                }
+            }
+        }
+        const uint64_t off = dev::xor_bits_uniform(d.out_blk, xu) ^ lane_off ^ d.out_c;
+        dev::gstore<CB>(out + off, c);
+    }
+}
+
+namespace {
+
+template <int UL, int WL>
+int launch_chunk_t(const bmmc_pass_desc &d, const uint8_t *in, uint8_t *out, hipStream_t s) {
+    const uint64_t nchunks = uint64_t(1) << d.blk_bits;
+    const uint64_t per = uint64_t(1) << (kChunkNTL + kChunkCPTL);
+    const uint64_t blocks = (nchunks + per - 1) / per;
+    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL>), dim3((uint32_t)nb), dim3(1 << kChunkNTL),
+                           0, s, in, out, d, b0);
+    }
+    return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+}
+
+template <int UL, int WL>
+int dispatch_chunk(int ul, int wl, const bmmc_pass_desc &d, const uint8_t *in, uint8_t *out,
+                   hipStream_t s) {
+    if constexpr (UL > 4) {
+        return BMMC_ERR_UNSUPPORTED;
+    } else if constexpr (UL + WL > 4) {
+        return dispatch_chunk<UL + 1, 0>(ul, wl, d, in, out, s);
+    } else {
+        if (ul == UL && wl == WL) return launch_chunk_t<UL, WL>(d, in, out, s);
+        return dispatch_chunk<UL, WL + 1>(ul, wl, d, in, out, s);
+    }
+}
+
+}  // namespace
+
+int launch_chunk(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
+    return dispatch_chunk<0, 0>(d.unit_log2, d.chunk_log2, d, static_cast<const uint8_t *>(in),
+                                static_cast<uint8_t *>(out), s);
+}
+
+}  // namespace bmmc

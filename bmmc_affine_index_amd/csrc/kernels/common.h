@@ -1,0 +1,171 @@
+// common.h -- device helpers shared by the permutation kernels (gfx950).
+//
+// Data is moved as opaque "chunks" of 1..16 bytes: one global load or store
+// per lane per chunk (dwordx4 for 16-byte chunks).  A chunk holds 2^wl units;
+// the tile kernel reads units back from LDS one at a time and reassembles a
+// chunk in output order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../../include/bmmc.h"
+
+namespace bmmc {
+namespace dev {
+
+template <int BYTES> struct Chunk;
+template <> struct Chunk<16> { uint32_t w[4]; };
+template <> struct Chunk<8> { uint32_t w[2]; };
+template <> struct Chunk<4> { uint32_t w[1]; };
+template <> struct Chunk<2> { uint16_t h; };
+template <> struct Chunk<1> { uint8_t b; };
+
+template <int BYTES> struct Unit;
+template <> struct Unit<16> { uint32_t w[4]; };
+template <> struct Unit<8> { uint32_t w[2]; };
+template <> struct Unit<4> { uint32_t w[1]; };
+template <> struct Unit<2> { uint16_t h; };
+template <> struct Unit<1> { uint8_t b; };
+
+// ---- global memory ------------------------------------------------------
+template <int BYTES> __device__ __forceinline__ Chunk<BYTES> gload(const uint8_t *p);
+template <> __device__ __forceinline__ Chunk<16> gload<16>(const uint8_t *p) {
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    return Chunk<16>{{v.x, v.y, v.z, v.w}};
+}
+template <> __device__ __forceinline__ Chunk<8> gload<8>(const uint8_t *p) {
+    uint2 v = *reinterpret_cast<const uint2 *>(p);
+    return Chunk<8>{{v.x, v.y}};
+}
+template <> __device__ __forceinline__ Chunk<4> gload<4>(const uint8_t *p) {
+    return Chunk<4>{{*reinterpret_cast<const uint32_t *>(p)}};
+}
+template <> __device__ __forceinline__ Chunk<2> gload<2>(const uint8_t *p) {
+    return Chunk<2>{*reinterpret_cast<const uint16_t *>(p)};
+}
+template <> __device__ __forceinline__ Chunk<1> gload<1>(const uint8_t *p) {
+    return Chunk<1>{*p};
+}
+
+template <int BYTES> __device__ __forceinline__ void gstore(uint8_t *p, const Chunk<BYTES> &c);
+template <> __device__ __forceinline__ void gstore<16>(uint8_t *p, const Chunk<16> &c) {
+    *reinterpret_cast<uint4 *>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+}
+template <> __device__ __forceinline__ void gstore<8>(uint8_t *p, const Chunk<8> &c) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(c.w[0], c.w[1]);
+}
+template <> __device__ __forceinline__ void gstore<4>(uint8_t *p, const Chunk<4> &c) {
+    *reinterpret_cast<uint32_t *>(p) = c.w[0];
+}
+template <> __device__ __forceinline__ void gstore<2>(uint8_t *p, const Chunk<2> &c) {
+    *reinterpret_cast<uint16_t *>(p) = c.h;
+}
+template <> __device__ __forceinline__ void gstore<1>(uint8_t *p, const Chunk<1> &c) {
+    *p = c.b;
+}
+
+// ---- LDS ----------------------------------------------------------------
+template <int BYTES> __device__ __forceinline__ void lds_store(uint8_t *p, const Chunk<BYTES> &c) {
+    if constexpr (BYTES == 16)
+        *reinterpret_cast<uint4 *>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+    else if constexpr (BYTES == 8)
+        *reinterpret_cast<uint2 *>(p) = make_uint2(c.w[0], c.w[1]);
+    else if constexpr (BYTES == 4)
+        *reinterpret_cast<uint32_t *>(p) = c.w[0];
+    else if constexpr (BYTES == 2)
+        *reinterpret_cast<uint16_t *>(p) = c.h;
+    else
+        *p = c.b;
+}
+
+template <int U> __device__ __forceinline__ Unit<U> lds_load_unit(const uint8_t *p) {
+    if constexpr (U == 16) {
+        uint4 v = *reinterpret_cast<const uint4 *>(p);
+        return Unit<16>{{v.x, v.y, v.z, v.w}};
+    } else if constexpr (U == 8) {
+        uint2 v = *reinterpret_cast<const uint2 *>(p);
+        return Unit<8>{{v.x, v.y}};
+    } else if constexpr (U == 4) {
+        return Unit<4>{{*reinterpret_cast<const uint32_t *>(p)}};
+    } else if constexpr (U == 2) {
+        return Unit<2>{*reinterpret_cast<const uint16_t *>(p)};
+    } else {
+        return Unit<1>{*p};
+    }
+}
+
+// Place unit number e (0 <= e < CB/U) of a chunk.  The chunk must start
+// zeroed when units are narrower than a dword.
+template <int CB, int U>
+__device__ __forceinline__ void put_unit(Chunk<CB> &c, int e, const Unit<U> &u) {
+    if constexpr (U >= 4) {
+#pragma unroll
+        for (int i = 0; i < U / 4; ++i) c.w[e * (U / 4) + i] = u.w[i];
+    } else if constexpr (CB >= 4) {
+        const int byte = e * U;
+        uint32_t v;
+        if constexpr (U == 2) v = (uint32_t)u.h;
+        else v = (uint32_t)u.b;
+        c.w[byte / 4] |= v << (8 * (byte % 4));
+    } else if constexpr (CB == 2) {
+        // U == 1, two bytes
+        c.h |= (uint16_t)((uint32_t)u.b << (8 * e));
+    } else {
+        c.b = u.b;
+    }
+}
+
+template <int CB, int U>
+__device__ __forceinline__ Unit<U> get_unit(const Chunk<CB> &c, int e) {
+    if constexpr (U >= 4) {
+        Unit<U> u;
+#pragma unroll
+        for (int i = 0; i < U / 4; ++i) u.w[i] = c.w[e * (U / 4) + i];
+        return u;
+    } else if constexpr (CB >= 4) {
+        const int byte = e * U;
+        uint32_t v = c.w[byte / 4] >> (8 * (byte % 4));
+        if constexpr (U == 2) return Unit<2>{(uint16_t)v};
+        else return Unit<1>{(uint8_t)v};
+    } else if constexpr (CB == 2) {
+        return Unit<1>{(uint8_t)(c.h >> (8 * e))};
+    } else {
+        return Unit<1>{c.b};
+    }
+}
+
+template <int CB> __device__ __forceinline__ void zero(Chunk<CB> &c) {
+    if constexpr (CB >= 4) {
+#pragma unroll
+        for (int i = 0; i < CB / 4; ++i) c.w[i] = 0;
+    } else if constexpr (CB == 2) {
+        c.h = 0;
+    } else {
+        c.b = 0;
+    }
+}
+
+// XOR of the table entries selected by the set bits of a wave-uniform value.
+template <typename T>
+__device__ __forceinline__ T xor_bits_uniform(const T *tab, uint64_t v) {
+    T acc = 0;
+    while (v) {
+        int k = __builtin_ctzll(v);
+        v &= v - 1;
+        acc ^= tab[k];
+    }
+    return acc;
+}
+
+// XOR of the first NB table entries selected by the bits of a per-lane value.
+template <int NB, typename T>
+__device__ __forceinline__ T xor_bits_lane(const T *tab, uint32_t v) {
+    T acc = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) acc ^= ((v >> k) & 1u) ? tab[k] : T(0);
+    return acc;
+}
+
+}  // namespace dev
+}  // namespace bmmc

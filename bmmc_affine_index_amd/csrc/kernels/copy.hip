@@ -1,0 +1,69 @@
+// copy.hip -- the ceiling: an identity-order copy with the permutation
+// kernels' vector width and launch shape ("A kernel that is correct": a copy
+// moves the same bytes as a transpose in the easiest order, and its measured
+// bandwidth, not the datasheet's, is the ceiling to compare against).
+#include "../launch.h"
+#include "common.h"
+
+namespace bmmc {
+
+constexpr int kCopyNTL = 8;   // 256 threads
+constexpr int kCopyCPTL = 2;  // 4 x 16 bytes per thread
+
+__global__ void __launch_bounds__(1 << kCopyNTL)
+    bmmc_copy_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, uint64_t n16,
+                     uint64_t blk0) {
+    constexpr int CPT = 1 << kCopyCPTL;
+    const uint64_t first = ((blk0 + blockIdx.x) << (kCopyNTL + kCopyCPTL)) + threadIdx.x;
+    dev::Chunk<16> v[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint64_t x = first + ((uint64_t)k << kCopyNTL);
+        if (x < n16) v[k] = dev::gload<16>(in + x * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint64_t x = first + ((uint64_t)k << kCopyNTL);
+        if (x < n16) dev::gstore<16>(out + x * 16, v[k]);
+    }
+}
+
+// Bytes that do not fill a 16-byte vector, or unaligned buffers.
+__global__ void __launch_bounds__(256)
+    bmmc_copy_bytes_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                           uint64_t nbytes, uint64_t blk0) {
+    const uint64_t x = (blk0 + blockIdx.x) * 256u + threadIdx.x;
+    if (x < nbytes) out[x] = in[x];
+}
+
+int launch_copy(const void *in_v, void *out_v, size_t nbytes, hipStream_t s) {
+    const uint8_t *in = static_cast<const uint8_t *>(in_v);
+    uint8_t *out = static_cast<uint8_t *>(out_v);
+    const bool aligned = (((uintptr_t)in | (uintptr_t)out) & 15u) == 0;
+    uint64_t done = 0;
+    if (aligned) {
+        const uint64_t n16 = nbytes / 16;
+        const uint64_t per = uint64_t(1) << (kCopyNTL + kCopyCPTL);
+        const uint64_t blocks = (n16 + per - 1) / per;
+        for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+            const uint64_t nb =
+                blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL(bmmc_copy_kernel, dim3((uint32_t)nb), dim3(1 << kCopyNTL), 0, s,
+                               in, out, n16, b0);
+        }
+        done = n16 * 16;
+    }
+    const uint64_t rest = nbytes - done;
+    if (rest) {
+        const uint64_t blocks = (rest + 255) / 256;
+        for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+            const uint64_t nb =
+                blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL(bmmc_copy_bytes_kernel, dim3((uint32_t)nb), dim3(256), 0, s,
+                               in + done, out + done, rest, b0);
+        }
+    }
+    return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+}
+
+}  // namespace bmmc

@@ -1,0 +1,163 @@
+// tiled.hip -- the LDS-staged tile pass for gfx950.
+//
+// One workgroup moves one tile (or 2^IT tiles) of 2^(2T) units: the 2^T input
+// segments (rows) of the tile are read with coalesced vector loads, staged in
+// LDS through an XOR swizzle, and read back in output order so that every
+// store writes whole output segments ("Efficient GPU Implementation of Affine
+// Index Permutations on Arrays": tiled BMMCs run almost as fast as a copy,
+// fully coalesced and bank-conflict free; appendix: the tiled and banks
+// bit-reversal kernels stage a 32 x 32 tile in shared memory between a
+// coalesced read and a coalesced write).
+//
+// Differences from the pages' kernels, for gfx950:
+//  * one generic kernel for every (A, c): the planner passes XOR tables of
+//    column contributions instead of generating a kernel per permutation; an
+//    address costs one XOR per chunk beyond the wave-uniform part;
+//  * 64-lane waves move 16-byte chunks (dwordx4 global access, b128 LDS
+//    writes), and tiles are 64 x 64 units for 4-byte units (256-byte
+//    segments);
+//  * the LDS swizzle is an XOR of row bits into the chunk index, chosen per
+//    plan so that the output-order reads hit distinct banks.
+#include "../launch.h"
+#include "common.h"
+
+namespace bmmc {
+
+template <int UL, int T, int IT> struct TiledCfg {
+    static constexpr int U = 1 << UL;
+    static constexpr int WL = (4 - UL) < T ? (4 - UL) : T;  // log2 units per chunk
+    static constexpr int W = 1 << WL;
+    static constexpr int CB = U << WL;                      // chunk bytes
+    static constexpr int CPSL = T - WL;                     // log2 chunks per row
+    static constexpr int CHL = 2 * T - WL;                  // log2 chunks per tile
+    static constexpr int NTL = CHL < 8 ? CHL : 8;           // log2 threads
+    static constexpr int NT = 1 << NTL;
+    static constexpr int RPPL = NTL - CPSL;                 // log2 rows per pass
+    static constexpr int JL = T - RPPL;                     // log2 passes per tile
+    static constexpr int J = 1 << JL;
+    static constexpr int TILE = U << (2 * T);               // bytes per tile
+    static constexpr int LDS = TILE << IT;
+    static_assert(RPPL >= 0 && JL >= 0, "tile geometry");
+};
+
+template <int UL, int T, int IT>
+__global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
+    bmmc_tiled_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                      const bmmc_pass_desc d, uint64_t blk0) {
+    using C = TiledCfg<UL, T, IT>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t q = tid & ((1u << C::CPSL) - 1);  // chunk within a row / segment
+    const uint32_t hl = tid >> C::CPSL;              // low row (segment) bits
+
+    // per-lane parts of the addresses
+    const uint64_t in_lane = dev::xor_bits_lane<C::RPPL>(d.in_h, hl) ^ (uint64_t)(q * C::CB);
+    const uint32_t wr_lane = dev::xor_bits_lane<C::RPPL>(d.lds_wr_h, hl) ^
+                             dev::xor_bits_lane<C::CPSL>(d.lds_wr_lo + C::WL, q);
+    const uint64_t out_lane = dev::xor_bits_lane<C::RPPL>(d.out_g, hl) ^ (uint64_t)(q * C::CB);
+    const uint32_t rd_lane = dev::xor_bits_lane<C::CPSL>(d.lds_rd + C::WL, q) ^
+                             dev::xor_bits_lane<C::RPPL>(d.lds_rd + T, hl);
+
+    const uint64_t tile0 = (blk0 + blockIdx.x) << IT;
+
+    dev::Chunk<C::CB> v[1 << IT][C::J];
+#pragma unroll
+    for (int s = 0; s < (1 << IT); ++s) {
+        const uint64_t base = dev::xor_bits_uniform(d.in_blk, tile0 | (uint64_t)s);
+#pragma unroll
+        for (int j = 0; j < C::J; ++j) {
+            const uint64_t in_j = base ^ dev::xor_bits_lane<C::JL>(d.in_h + C::RPPL, (uint32_t)j);
+            v[s][j] = dev::gload<C::CB>(in + (in_j ^ in_lane));
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < (1 << IT); ++s) {
+#pragma unroll
+        for (int j = 0; j < C::J; ++j) {
+            const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.lds_wr_h + C::RPPL, (uint32_t)j);
+            dev::lds_store<C::CB>(lds + s * C::TILE + (wr_j ^ wr_lane), v[s][j]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < (1 << IT); ++s) {
+        const uint64_t blk = tile0 | (uint64_t)s;
+        const uint64_t obase = dev::xor_bits_uniform(d.out_blk, blk) ^ d.out_c;
+        const uint32_t rbase = dev::xor_bits_uniform(d.lds_blk, blk) ^ d.lds_c;
+#pragma unroll
+        for (int j = 0; j < C::J; ++j) {
+            const uint64_t out_j =
+                obase ^ dev::xor_bits_lane<C::JL>(d.out_g + C::RPPL, (uint32_t)j);
+            const uint32_t rd_j =
+                rbase ^ dev::xor_bits_lane<C::JL>(d.lds_rd + T + C::RPPL, (uint32_t)j) ^ rd_lane;
+            dev::Chunk<C::CB> ch;
+            dev::zero(ch);
+#pragma unroll
+            for (int e = 0; e < C::W; ++e) {
+                const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.lds_rd, (uint32_t)e);
+                dev::put_unit<C::CB, C::U>(
+                    ch, e, dev::lds_load_unit<C::U>(lds + s * C::TILE + (rd_j ^ rd_e)));
+            }
+            dev::gstore<C::CB>(out + (out_j ^ out_lane), ch);
+        }
+    }
+}
+
+namespace {
+
+constexpr int kMaxT[5] = {8, 7, 7, 6, 6};
+constexpr int kMaxIT = 3;
+
+struct TiledArgs {
+    const bmmc_pass_desc *d;
+    const uint8_t *in;
+    uint8_t *out;
+    hipStream_t s;
+};
+
+template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
+    using C = TiledCfg<UL, T, IT>;
+    const uint64_t blocks = uint64_t(1) << (a.d->blk_bits - IT);
+    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT>), dim3((uint32_t)nb), dim3(C::NT), 0,
+                           a.s, a.in, a.out, *a.d, b0);
+    }
+    return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+}
+
+template <int UL, int T, int IT> constexpr bool valid_cfg() {
+    return UL <= 4 && T >= 1 && T <= kMaxT[UL] && IT <= kMaxIT &&
+           (TiledCfg<UL, T, IT>::LDS <= 65536);
+}
+
+// Walks the compiled (UL, T, IT) space; `launch` = false only answers
+// whether the configuration exists.
+template <int UL, int T, int IT>
+int dispatch(int ul, int t, int it, const TiledArgs *a) {
+    if constexpr (UL > 4) {
+        return BMMC_ERR_UNSUPPORTED;
+    } else if constexpr (T > kMaxT[UL]) {
+        return dispatch<UL + 1, 1, 0>(ul, t, it, a);
+    } else if constexpr (IT > kMaxIT || !valid_cfg<UL, T, IT>()) {
+        return dispatch<UL, T + 1, 0>(ul, t, it, a);
+    } else {
+        if (ul == UL && t == T && it == IT) return a ? launch_one<UL, T, IT>(*a) : BMMC_OK;
+        return dispatch<UL, T, IT + 1>(ul, t, it, a);
+    }
+}
+
+}  // namespace
+
+bool tiled_supported(int unit_log2, int t, int iters_log2) {
+    return dispatch<0, 1, 0>(unit_log2, t, iters_log2, nullptr) == BMMC_OK;
+}
+
+int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
+    if (d.iters_log2 > d.blk_bits) return BMMC_ERR_INVALID_ARG;
+    TiledArgs a{&d, static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), s};
+    return dispatch<0, 1, 0>(d.unit_log2, d.t, d.iters_log2, &a);
+}
+
+}  // namespace bmmc

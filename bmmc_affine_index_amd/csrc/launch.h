@@ -1,0 +1,25 @@
+// launch.h -- host entry points of the kernel families (defined in kernels/).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bmmc.h"
+
+namespace bmmc {
+
+// LDS-staged tile pass (BMMC_KERNEL_TILED).
+int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s);
+// Chunk moves (BMMC_KERNEL_CHUNK) and the one-unit naive pass (BMMC_KERNEL_NAIVE).
+int launch_chunk(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s);
+// Identity-order copy of nbytes.
+int launch_copy(const void *in, void *out, size_t nbytes, hipStream_t s);
+
+// Whether the tile kernel is compiled for this unit size, side and iteration count.
+bool tiled_supported(int unit_log2, int t, int iters_log2);
+
+// Largest grid (in workgroups) of one launch; bigger passes are split.
+constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 30;
+
+}  // namespace bmmc

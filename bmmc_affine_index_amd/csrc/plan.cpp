@@ -1,0 +1,593 @@
+// plan.cpp -- the host planner: F2 algebra from a BMMC (A, c) to kernel tables.
+//
+// Source: "Efficient GPU Implementation of Affine Index Permutations on
+// Arrays" (FHPNC'23).  The page's method sections (tiling, bank conflicts,
+// iterations, the tiled-BMMC class and its factorisation) are lost from the
+// extracted text; their results survive in the introduction, evaluation and
+// appendix.  What survives fixes the following, and this file builds on it:
+//  * a BMMC is y = A.x XOR c over F2 with A invertible (introduction);
+//  * tiled BMMCs include every BPC and one tile pass moves them coalesced
+//    (introduction, contributions); any BMMC factors as A = T1.T2 into two
+//    tiled BMMCs, applied T2 first (introduction);
+//  * n_over counts the low input bits that land in the low output bits, and a
+//    random BMMC's factors behave differently from a random BPC there
+//    (evaluation, the naive-kernel column of Figure 9);
+//  * the iterated variant amortises index work over several tiles
+//    (evaluation; appendix, the iterated bit-reversal kernel).
+// The reconstruction (tile test, factorisation, fused single pass) is
+// written from the F2 algebra; each step says what it guarantees.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+namespace bmmc {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Unit normalisation.
+//
+// The byte-level map of an array of 2^n elements of 2^e bytes is
+// diag(I_e, A) with complement c << e.  Every further low bit that the map
+// leaves in place (identity row, column used by no other row, complement bit
+// 0) just widens the run of bytes that moves as one block.  The kernels move
+// "units" of 2^k bytes, k <= 4 (one 16-byte vector), over the remaining
+// nb = n + e - k index bits.
+// ---------------------------------------------------------------------------
+struct UnitMap {
+    int ulog2 = 0;  // log2 bytes of a unit
+    int nb = 0;     // index bits at unit granularity
+    Mat A;          // nb x nb
+    u64 c = 0;
+};
+
+UnitMap normalize(int n, const Mat &A, u64 c, int e) {
+    const int nb = n + e;
+    Mat Ab = Mat::zeros(nb, nb);
+    for (int r = 0; r < e; ++r) Ab.r[r] = u64(1) << r;
+    for (int r = 0; r < n; ++r) Ab.r[e + r] = A.r[r] << e;
+    const u64 cb = c << e;
+    int k = e;
+    while (k < 4 && k < nb) {
+        if (Ab.r[k] != (u64(1) << k) || ((cb >> k) & 1u)) break;
+        bool used = false;
+        for (int r = k + 1; r < nb; ++r)
+            if ((Ab.r[r] >> k) & 1u) { used = true; break; }
+        if (used) break;
+        ++k;
+    }
+    UnitMap m;
+    m.ulog2 = k;
+    m.nb = nb - k;
+    m.A = Mat::zeros(m.nb, m.nb);
+    for (int r = 0; r < m.nb; ++r) m.A.r[r] = Ab.r[r + k] >> k;
+    m.c = cb >> k;
+    return m;
+}
+
+// Number of low index bits s such that A = diag(I_s, Q): the map moves
+// 2^s-unit segments as wholes.
+int low_identity_bits(const Mat &A) {
+    int s = 0;
+    while (s < A.rows) {
+        if (A.r[s] != (u64(1) << s)) break;
+        bool used = false;
+        for (int r = s + 1; r < A.rows; ++r)
+            if ((A.r[r] >> s) & 1u) { used = true; break; }
+        if (used) break;
+        ++s;
+    }
+    return s;
+}
+
+int popcount(u64 v) { return __builtin_popcountll(v); }
+
+// n_over = t - rank(A[t:, 0:t]): the dimension of the low input space that
+// stays in the low output bits.
+int n_over_of(const Mat &A, int t) {
+    if (t <= 0 || t >= A.rows) return t > 0 ? t : 0;
+    Mat sub = Mat::zeros(A.rows - t, t);
+    for (int i = t; i < A.rows; ++i) sub.r[i - t] = A.r[i] & low_mask(t);
+    return t - rank(sub);
+}
+
+// The tile test.  With B = A^{-1}, column j < t of B is the input index that
+// lands on output index e_j.  A tile made of the 2^t input segments spanned
+// by the low t bits and a set H of t higher bits covers whole output segments
+// iff every such column lies in span(low t bits, H), i.e. iff the rows r >= t
+// that column j < t uses lie in H.  Returns that row set S; A is tiled at t
+// iff |S| <= t (then any H containing S works).
+u64 tile_rows(const Mat &B, int t) {
+    u64 S = 0;
+    for (int r = t; r < B.rows; ++r)
+        if (B.r[r] & low_mask(t)) S |= u64(1) << r;
+    return S;
+}
+
+// Pad the required row set S to t rows.  With `near_out`, prefer input bits
+// whose image is a single output bit in [t, 2t) (keeps a BPC tile's output
+// segments close together); then take the lowest free bits.
+u64 pad_rows(const Mat &A, u64 S, int t, bool near_out) {
+    u64 H = S;
+    for (int pass = near_out ? 0 : 1; pass < 2 && popcount(H) < t; ++pass) {
+        for (int j = t; j < A.rows && popcount(H) < t; ++j) {
+            if ((H >> j) & 1u) continue;
+            if (pass == 0) {
+                u64 col = A.col(j);
+                bool single = col && !(col & (col - 1));
+                if (!single) continue;
+                int o = __builtin_ctzll(col);
+                if (o < t || o >= 2 * t) continue;
+            }
+            H |= u64(1) << j;
+        }
+    }
+    return H;
+}
+
+// The pages' factorisation route, rebuilt from the algebra: with B = A^{-1},
+// take an independent subset of the high parts of B's first t columns and
+// complete it by unit vectors to a basis Q_hh of the high coordinates.  With
+// Q = diag(I_t, Q_hh): T2 = Q^{-1} only relabels 2^t-unit segments, and
+// T1 = A.Q has its tile rows inside {t, ..., 2t-1}, because Q^{-1} maps each
+// such high part into the span of the first chosen vectors.  A = T1.T2.
+bool factorize(const Mat &A, int t, Mat &T1, Mat &T2) {
+    const int n = A.rows;
+    Mat B;
+    if (!inverse(A, B)) return false;
+    Basis chosen;
+    std::vector<u64> qcols;
+    for (int j = 0; j < t; ++j) {
+        u64 v = B.col(j) & ~low_mask(t);
+        if (chosen.add(v)) qcols.push_back(v);
+    }
+    Basis all = chosen;
+    for (int m = t; m < n; ++m)
+        if (all.add(u64(1) << m)) qcols.push_back(u64(1) << m);
+    if ((int)qcols.size() != n - t) return false;
+    Mat Q = Mat::identity(n);
+    for (int k = 0; k < n - t; ++k) Q.set_col(t + k, qcols[k]);
+    if (!inverse(Q, T2)) return false;
+    T1 = mul(A, Q);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// LDS bank model used to choose the tile swizzle.  A wave's LDS access is
+// served in groups of lanes that together touch at most `banks` dwords; a
+// group takes as many cycles as the largest number of distinct dwords that
+// fall into one bank.  gfx950's exact bank count and grouping are measured
+// with the LDS bank-conflict counter; the planner minimises the cost under
+// both a 32-bank and a 64-bank model so that either is conflict-free when
+// possible.
+// ---------------------------------------------------------------------------
+int bank_cycles(const uint32_t *addr, int lanes, int bytes, int banks) {
+    int per = bytes >= 4 ? (4 * banks) / bytes : banks;
+    if (per > 64) per = 64;
+    if (per < 1) per = 1;
+    const int words = bytes >= 4 ? bytes / 4 : 1;
+    int total = 0;
+    uint32_t seen[64][64];
+    int count[64];
+    for (int g0 = 0; g0 < lanes; g0 += per) {
+        for (int b = 0; b < banks; ++b) count[b] = 0;
+        int mx = 0;
+        for (int l = g0; l < lanes && l < g0 + per; ++l) {
+            for (int w = 0; w < words; ++w) {
+                const uint32_t dw = addr[l] / 4 + (uint32_t)w;
+                const int b = (int)(dw % (uint32_t)banks);
+                bool dup = false;  // same dword: a broadcast, no extra cycle
+                for (int i = 0; i < count[b]; ++i)
+                    if (seen[b][i] == dw) { dup = true; break; }
+                if (dup || count[b] >= 64) continue;
+                seen[b][count[b]++] = dw;
+                mx = std::max(mx, count[b]);
+            }
+        }
+        total += std::max(mx, 1);
+    }
+    return total;
+}
+
+u64 splitmix(u64 &s) {
+    u64 z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+struct TileGeom {
+    int ulog2, t, wl;  // unit, tile side, log2 units per vector chunk
+    int cpsl;          // log2 chunks per segment (tile row)
+    int ntl;           // log2 threads per workgroup
+    int rppl;          // log2 rows handled per pass by the workgroup
+};
+
+TileGeom tile_geom(int ulog2, int t) {
+    TileGeom g;
+    g.ulog2 = ulog2;
+    g.t = t;
+    g.wl = std::min(4 - ulog2, t);
+    g.cpsl = t - g.wl;
+    int chunks_l = 2 * t - g.wl;
+    g.ntl = std::min(8, chunks_l);
+    g.rppl = g.ntl - g.cpsl;
+    return g;
+}
+
+}  // namespace
+
+int max_tile_log2(int ulog2) {
+    static const int t[5] = {8, 7, 7, 6, 6};
+    return (ulog2 >= 0 && ulog2 <= 4) ? t[ulog2] : 0;
+}
+
+namespace {
+
+int default_tile_log2(int ulog2) {
+    static const int t[5] = {8, 7, 6, 5, 5};
+    return t[ulog2];
+}
+
+// Build the tile pass for unit map (A, c) with tile rows W (t vectors in the
+// high coordinates, independent).  The tile of block b is the coset
+// K.b XOR span(low t bits) XOR span(W); because W contains the high parts of
+// B's first t columns, the tile's image is 2^t whole output segments.
+int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W,
+                int iters_log2, bool swizzle, bmmc_pass_desc *d) {
+    const int nb = A.rows;
+    if ((int)W.size() != t || 2 * t > nb) return BMMC_ERR_INVALID_ARG;
+    const u64 lo_t = low_mask(t);
+    Basis wb;
+    for (u64 w : W) {
+        if (w & lo_t) return BMMC_ERR_INVALID_ARG;
+        if (!wb.add(w)) return BMMC_ERR_INVALID_ARG;
+    }
+    // Block bits: high coordinates that are no pivot of W; together with W
+    // they form a basis of the high coordinates.
+    std::vector<int> R;
+    const u64 piv = wb.pivot_mask();
+    for (int r = t; r < nb; ++r)
+        if (!((piv >> r) & 1u)) R.push_back(r);
+    if ((int)R.size() != nb - 2 * t) return BMMC_ERR_INVALID_ARG;
+    const int blk_bits = (int)R.size();
+    if (iters_log2 > blk_bits) iters_log2 = blk_bits;
+
+    // Output segments of the tile: a basis G of the high parts of A's image
+    // of the tile's local space.
+    Basis gb;
+    for (int j = 0; j < t; ++j) gb.add(A.apply(u64(1) << j) & ~lo_t);
+    for (int k = 0; k < t; ++k) gb.add(A.apply(W[k]) & ~lo_t);
+    if (gb.size() != t) return BMMC_ERR_INVALID_ARG;
+
+    // M: local input coordinates (lo bits 0..t-1, row bits t..2t-1) ->
+    // local output coordinates (position in segment, segment index g).
+    Mat M = Mat::zeros(2 * t, 2 * t);
+    for (int j = 0; j < 2 * t; ++j) {
+        u64 v = j < t ? A.apply(u64(1) << j) : A.apply(W[j - t]);
+        u64 hi = v & ~lo_t;
+        if (gb.reduce(hi) != 0) return BMMC_ERR_INVALID_ARG;
+        M.set_col(j, (v & lo_t) | (gb.coords(hi) << t));
+    }
+    Mat Minv;
+    if (!inverse(M, Minv)) return BMMC_ERR_INVALID_ARG;
+
+    const TileGeom g = tile_geom(ulog2, t);
+    const int lanes = std::min(64, 1 << g.ntl);
+    const int cps = 1 << g.cpsl;
+
+    // Two free choices make the output-order LDS reads conflict-free:
+    //  * the order of the tile's output segments: the lanes of a read take
+    //    the first rppl coordinates of g, so the planner picks which
+    //    coordinates of G those are (`gperm`);
+    //  * the LDS layout: the slot of local (lo, h) is
+    //    (h << t) | (P.lo XOR S.h), with P an invertible map of the chunk
+    //    index inside a row and S (t x t) an XOR swizzle by row; both keep
+    //    the units of a chunk together, so the write of a chunk stays one
+    //    vector access.  Sx holds S's t columns followed by P's t columns.
+    auto slot = [&](u64 u, const std::vector<u64> &Sx) -> u64 {
+        u64 lo = u & lo_t, h = u >> t, s = 0;
+        for (int k = 0; k < t; ++k) {
+            if ((h >> k) & 1u) s ^= Sx[k];
+            if ((lo >> k) & 1u) s ^= Sx[t + k];
+        }
+        return (h << t) | s;
+    };
+    // read columns: input-local vector of each output-local coordinate
+    auto read_cols = [&](const std::vector<int> &gperm) {
+        std::vector<u64> rc(2 * t);
+        for (int k = 0; k < t; ++k) rc[k] = Minv.col(k);
+        for (int k = 0; k < t; ++k) rc[t + k] = Minv.col(t + gperm[k]);
+        return rc;
+    };
+    auto cost = [&](const std::vector<u64> &rc, const std::vector<u64> &Sx) {
+        uint32_t wa[64], ra[64];
+        for (int l = 0; l < lanes; ++l) {
+            u64 q = (u64)(l & (cps - 1)), hl = (u64)(l >> g.cpsl);
+            // write phase: chunk q of row hl
+            wa[l] = (uint32_t)(slot((hl << t) | (q << g.wl), Sx) << ulog2);
+            // read phase: unit q*w of output segment hl
+            u64 src = 0;
+            for (int b = 0; b < g.cpsl; ++b)
+                if ((q >> b) & 1u) src ^= rc[g.wl + b];
+            for (int b = 0; b < g.rppl; ++b)
+                if ((hl >> b) & 1u) src ^= rc[t + b];
+            ra[l] = (uint32_t)(slot(src, Sx) << ulog2);
+        }
+        int cw = bank_cycles(wa, lanes, 1 << (ulog2 + g.wl), 32) +
+                 bank_cycles(wa, lanes, 1 << (ulog2 + g.wl), 64);
+        int cr = 2 * bank_cycles(ra, lanes, 1 << ulog2, 32) +
+                 4 * bank_cycles(ra, lanes, 1 << ulog2, 64);
+        return cr + cw;
+    };
+    std::vector<int> gperm(t);
+    for (int k = 0; k < t; ++k) gperm[k] = k;
+    std::vector<u64> S(2 * t, 0);
+    for (int k = 0; k < t; ++k) S[t + k] = u64(1) << k;  // P = identity
+    if (swizzle && t > g.wl) {
+        const u64 colmask = lo_t & ~low_mask(g.wl);
+        // lower bound: one cycle per lane group on each model
+        int ideal = 0;
+        {
+            const int rbytes = 1 << ulog2, wbytes = 1 << (ulog2 + g.wl);
+            for (int banks : {32, 64}) {
+                int rb = rbytes >= 4 ? rbytes : 4, wb = wbytes >= 4 ? wbytes : 4;
+                ideal += (banks == 32 ? 2 : 4) *
+                         std::max(1, (lanes * rb + 4 * banks - 1) / (4 * banks));
+                ideal += std::max(1, (lanes * wb + 4 * banks - 1) / (4 * banks));
+            }
+        }
+        u64 seed = 0x5EEDull ^ ((u64)t << 8) ^ (u64)ulog2;
+        for (int k = 0; k < 2 * t; ++k) seed = seed * 31 + Minv.r[k];
+        int best_cost = 1 << 30;
+        std::vector<int> best_perm = gperm;
+        std::vector<u64> best_S = S, cand(2 * t);
+        auto random_p = [&](std::vector<u64> &Sx) {
+            // random invertible map of the chunk-index bits (wl..t-1); the
+            // unit bits inside a chunk stay fixed
+            for (;;) {
+                Mat Pm = Mat::zeros(t, t);
+                for (int k = 0; k < t; ++k)
+                    Pm.set_col(k, k < g.wl ? (u64(1) << k) : (splitmix(seed) & colmask));
+                if (rank(Pm) == t) {
+                    for (int k = 0; k < t; ++k) Sx[t + k] = Pm.col(k);
+                    return;
+                }
+            }
+        };
+        // candidate lane coordinates of g: every rppl-subset, taken first
+        const int rl = std::min(g.rppl, t);
+        std::vector<int> pick(rl);
+        for (int k = 0; k < rl; ++k) pick[k] = k;
+        int budget = 1200;  // cost evaluations
+        for (bool more = true; more && best_cost > ideal && budget > 0;) {
+            std::vector<int> perm(pick.begin(), pick.end());
+            for (int k = 0; k < t; ++k)
+                if (std::find(pick.begin(), pick.end(), k) == pick.end()) perm.push_back(k);
+            const std::vector<u64> rc = read_cols(perm);
+            auto consider = [&](const std::vector<u64> &Sx) {
+                --budget;
+                int cc = cost(rc, Sx);
+                if (cc < best_cost) { best_cost = cc; best_perm = perm; best_S = Sx; }
+            };
+            for (int k = 0; k < t; ++k) { cand[k] = 0; cand[t + k] = u64(1) << k; }
+            consider(cand);
+            // the diagonal skew: row h shifts by h (restricted to chunk bits)
+            for (int k = 0; k < t; ++k) cand[k] = (u64(1) << k) & colmask;
+            consider(cand);
+            for (int tries = 0; tries < 96 && best_cost > ideal && budget > 0; ++tries) {
+                for (int k = 0; k < t; ++k) cand[k] = splitmix(seed) & colmask;
+                if (tries & 1) random_p(cand);
+                else for (int k = 0; k < t; ++k) cand[t + k] = u64(1) << k;
+                consider(cand);
+            }
+            // next rl-subset of {0..t-1} in lexicographic order
+            int i = rl - 1;
+            while (i >= 0 && pick[i] == t - rl + i) --i;
+            if (i < 0) {
+                more = false;
+            } else {
+                ++pick[i];
+                for (int k = i + 1; k < rl; ++k) pick[k] = pick[k - 1] + 1;
+            }
+        }
+        gperm = best_perm;
+        S = best_S;
+    }
+    const std::vector<u64> rcols = read_cols(gperm);
+
+    std::memset(d, 0, sizeof(*d));
+    d->kernel = BMMC_KERNEL_TILED;
+    d->unit_log2 = ulog2;
+    d->nbits = nb;
+    d->t = t;
+    d->chunk_log2 = g.wl;
+    d->blk_bits = blk_bits;
+    d->iters_log2 = iters_log2;
+    d->lds_bytes = (uint32_t)((u64(1) << (2 * t + ulog2)) << iters_log2);
+    for (int k = 0; k < blk_bits; ++k) {
+        u64 x = u64(1) << R[k];
+        u64 z = A.apply(x);
+        d->in_blk[k] = x << ulog2;
+        d->out_blk[k] = (z & ~lo_t) << ulog2;
+        d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_t), S) << ulog2);
+    }
+    for (int k = 0; k < t; ++k) {
+        d->in_h[k] = W[k] << ulog2;
+        d->out_g[k] = gb.vec[gperm[k]] << ulog2;
+        d->lds_wr_h[k] = (uint32_t)(slot(u64(1) << (t + k), S) << ulog2);
+        d->lds_wr_lo[k] = (uint32_t)(slot(u64(1) << k, S) << ulog2);
+    }
+    for (int k = 0; k < 2 * t; ++k) d->lds_rd[k] = (uint32_t)(slot(rcols[k], S) << ulog2);
+    d->out_c = (c & ~lo_t) << ulog2;
+    d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
+    return BMMC_OK;
+}
+
+// Chunk pass: A = diag(I_s, Q) with s >= chunk bits; each chunk of 2^wl units
+// moves as a whole, with the complement's low bits permuting units inside it.
+// Also used, with one-unit chunks, for the naive pass (any A).
+void build_chunk(const Mat &A, u64 c, int ulog2, int wl, int kernel, bmmc_pass_desc *d) {
+    std::memset(d, 0, sizeof(*d));
+    const int nb = A.rows;
+    d->kernel = kernel;
+    d->unit_log2 = ulog2;
+    d->nbits = nb;
+    d->chunk_log2 = wl;
+    d->blk_bits = nb - wl;
+    for (int k = 0; k < nb - wl; ++k) d->out_blk[k] = A.apply(u64(1) << (k + wl)) << ulog2;
+    d->out_c = (c & ~low_mask(wl)) << ulog2;
+    d->unit_xor = (int32_t)(c & low_mask(wl));
+}
+
+void build_copy(int nb, int ulog2, bmmc_pass_desc *d) {
+    std::memset(d, 0, sizeof(*d));
+    d->kernel = BMMC_KERNEL_COPY;
+    d->unit_log2 = ulog2;
+    d->nbits = nb;
+}
+
+// Element-level view of a unit-level factor: the d low element-index bits that
+// the unit absorbed stay in place.
+void to_element_level(const Mat &T, u64 c, int dlow, int n, uint64_t *rows, uint64_t *c_out) {
+    for (int r = 0; r < n; ++r)
+        rows[r] = r < dlow ? (u64(1) << r) : (T.r[r - dlow] << dlow);
+    *c_out = c << dlow;
+}
+
+}  // namespace
+
+int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
+               const bmmc_plan_options *opt, bmmc_plan *p) {
+    bmmc_plan_options o = {};
+    if (opt) o = *opt;
+    if (n < 1 || n > BMMC_MAX_N || !Arows) return BMMC_ERR_INVALID_ARG;
+    if (elem_bytes == 0 || elem_bytes > 16 || (elem_bytes & (elem_bytes - 1)))
+        return BMMC_ERR_INVALID_ARG;
+    if (o.route < BMMC_ROUTE_AUTO || o.route > BMMC_ROUTE_FUSED) return BMMC_ERR_INVALID_ARG;
+    if (o.tile_log2 < 0 || o.tile_log2 > BMMC_MAX_TILE || o.iters_log2 < 0 || o.iters_log2 > 4)
+        return BMMC_ERR_INVALID_ARG;
+    const int e = __builtin_ctzll((u64)elem_bytes);
+    if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
+    const u64 hi = ~low_mask(n);
+    Mat A = Mat::zeros(n, n);
+    for (int r = 0; r < n; ++r) {
+        if (Arows[r] & hi) return BMMC_ERR_INVALID_ARG;
+        A.r[r] = Arows[r];
+    }
+    if (c & hi) return BMMC_ERR_INVALID_ARG;
+    Mat Ainv;
+    if (!inverse(A, Ainv)) return BMMC_ERR_SINGULAR;
+
+    p->n = n;
+    p->elem_bytes = (int)elem_bytes;
+    std::memcpy(p->A, Arows, sizeof(uint64_t) * (size_t)n);
+    p->c = c;
+
+    const UnitMap m = normalize(n, A, c, e);
+    const int dlow = m.ulog2 - e;
+    bmmc_plan_info &info = p->info;
+    info = bmmc_plan_info{};
+    info.n = n;
+    info.elem_bytes = (int)elem_bytes;
+    info.unit_bytes = 1 << m.ulog2;
+    info.unit_bits = m.nb;
+
+    int t = o.tile_log2 ? o.tile_log2 : default_tile_log2(m.ulog2);
+    t = std::min(t, max_tile_log2(m.ulog2));
+    t = std::min(t, m.nb / 2);
+    while (t > 0 && ((u64(1) << (2 * t + m.ulog2)) << o.iters_log2) > kMaxLdsBytes) --t;
+
+    // classification
+    const bool ident = m.nb == 0 || m.A.is_identity();
+    Mat B;
+    if (m.nb > 0) inverse(m.A, B);
+    const u64 S = (m.nb > 0 && t > 0) ? tile_rows(B, t) : 0;
+    if (ident) info.kind = BMMC_KIND_IDENTITY;
+    else if (is_permutation_matrix(m.A)) info.kind = BMMC_KIND_BPC;
+    else if (t > 0 && popcount(S) <= t) info.kind = BMMC_KIND_TILED;
+    else info.kind = BMMC_KIND_GENERAL;
+    info.n_over = (m.nb > 0 && t > 0) ? n_over_of(m.A, t) : 0;
+
+    auto single = [&](int route) {
+        p->npasses = 1;
+        info.passes = 1;
+        info.route = route;
+        to_element_level(m.A, m.c, dlow, n, p->factor_A[0], &p->factor_c[0]);
+    };
+
+    // identity order: the copy kernel
+    if (ident && m.c == 0) {
+        build_copy(m.nb, m.ulog2, &p->pass[0]);
+        single(BMMC_ROUTE_FUSED);
+        return BMMC_OK;
+    }
+    // naive: forced, or too few bits for a tile
+    if (o.route == BMMC_ROUTE_NAIVE || t < 1) {
+        build_chunk(m.A, m.c, m.ulog2, 0, BMMC_KERNEL_NAIVE, &p->pass[0]);
+        single(BMMC_ROUTE_NAIVE);
+        return BMMC_OK;
+    }
+    // whole segments move: chunk kernel, no LDS
+    const int sid = low_identity_bits(m.A);
+    if (sid >= t) {
+        const int wl = std::min(4 - m.ulog2, sid);
+        build_chunk(m.A, m.c, m.ulog2, wl, BMMC_KERNEL_CHUNK, &p->pass[0]);
+        single(BMMC_ROUTE_FUSED);
+        return BMMC_OK;
+    }
+    const bool swz = !o.no_swizzle;
+    if (info.kind != BMMC_KIND_GENERAL) {
+        u64 H = pad_rows(m.A, S, t, true);
+        std::vector<u64> W;
+        for (int r = t; r < m.nb; ++r)
+            if ((H >> r) & 1u) W.push_back(u64(1) << r);
+        int st = build_tiled(m.A, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[0]);
+        if (st != BMMC_OK) return st;
+        info.tile_log2 = t;
+        single(BMMC_ROUTE_FUSED);
+        return BMMC_OK;
+    }
+    if (o.route == BMMC_ROUTE_TWO_PASS) {
+        Mat T1, T2;
+        if (!factorize(m.A, t, T1, T2)) return BMMC_ERR_INVALID_ARG;
+        // pass 0: T2 relabels segments (complement 0)
+        const int wl = std::min(4 - m.ulog2, t);
+        build_chunk(T2, 0, m.ulog2, wl, BMMC_KERNEL_CHUNK, &p->pass[0]);
+        // pass 1: T1 is tiled with rows inside {t, ..., 2t-1}
+        Mat T1inv;
+        inverse(T1, T1inv);
+        u64 H = pad_rows(T1, tile_rows(T1inv, t), t, false);
+        if (popcount(H) != t) return BMMC_ERR_INVALID_ARG;
+        std::vector<u64> W;
+        for (int r = t; r < m.nb; ++r)
+            if ((H >> r) & 1u) W.push_back(u64(1) << r);
+        int st = build_tiled(T1, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[1]);
+        if (st != BMMC_OK) return st;
+        p->npasses = 2;
+        info.passes = 2;
+        info.route = BMMC_ROUTE_TWO_PASS;
+        info.tile_log2 = t;
+        info.scratch_bytes = (size_t)elem_bytes << n;
+        to_element_level(T2, 0, dlow, n, p->factor_A[0], &p->factor_c[0]);
+        to_element_level(T1, m.c, dlow, n, p->factor_A[1], &p->factor_c[1]);
+        return BMMC_OK;
+    }
+    // fused single pass: tile rows span the high parts of B's first t
+    // columns (reduced basis), padded with unit vectors.
+    Basis vb;
+    for (int j = 0; j < t; ++j) vb.add(B.col(j) & ~low_mask(t));
+    std::vector<u64> W = vb.vec;
+    Basis wb = vb;
+    for (int r = t; r < m.nb && (int)W.size() < t; ++r)
+        if (wb.add(u64(1) << r)) W.push_back(u64(1) << r);
+    int st = build_tiled(m.A, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[0]);
+    if (st != BMMC_OK) return st;
+    info.tile_log2 = t;
+    single(BMMC_ROUTE_FUSED);
+    return BMMC_OK;
+}
+
+}  // namespace bmmc

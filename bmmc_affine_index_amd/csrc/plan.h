@@ -1,0 +1,40 @@
+// plan.h -- internal plan representation and the host planner.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/bmmc.h"
+#include "gf2.h"
+
+struct bmmc_plan {
+    int n = 0;
+    int elem_bytes = 0;
+    uint64_t A[BMMC_MAX_N] = {};
+    uint64_t c = 0;
+    bmmc_plan_info info = {};
+    int npasses = 0;
+    bmmc_pass_desc pass[BMMC_MAX_PASSES] = {};
+    // element-level factor of each pass (n rows) and its complement
+    uint64_t factor_A[BMMC_MAX_PASSES][BMMC_MAX_N] = {};
+    uint64_t factor_c[BMMC_MAX_PASSES] = {};
+    // scratch for two-pass plans, allocated on first execute
+    mutable std::mutex scratch_mu;
+    mutable void *scratch = nullptr;
+    mutable int scratch_device = -1;
+};
+
+namespace bmmc {
+
+// Build a plan: validation, inversion, classification, route choice and the
+// kernel tables of every pass.  Host-only; returns a BMMC_* status.
+int build_plan(int n, const uint64_t *A, uint64_t c, size_t elem_bytes,
+               const bmmc_plan_options *opt, bmmc_plan *p);
+
+// Largest tile side (log2 units) the tile kernel is compiled for at a unit
+// size of 2^unit_log2 bytes, and the LDS byte budget of one workgroup.
+int max_tile_log2(int unit_log2);
+constexpr uint32_t kMaxLdsBytes = 65536;
+
+}  // namespace bmmc

@@ -1,0 +1,193 @@
+/*
+ * bmmc.h -- C ABI of the MI355X (gfx950) BMMC permutation library.
+ *
+ * A BMMC ("bit matrix multiply and complement") permutation of an array of
+ * 2^n elements moves element i to index A.i XOR c, where the index is read as
+ * a bit vector in F2^n (bit 0 = least significant bit), A is an invertible
+ * n x n matrix over F2 and c is an n-bit vector ("Efficient GPU
+ * Implementation of Affine Index Permutations on Arrays", FHPNC'23,
+ * introduction: the BMMC definition; invertibility of A is what makes the map
+ * a permutation).  Bit-reversal, power-of-two matrix transposes (rotations of
+ * the index bits), bit permutations with complement (BPC) and arbitrary affine
+ * maps over F2 are all such permutations.
+ *
+ *     out[A.i XOR c] = in[i]      for every i in [0, 2^n)
+ *
+ * The scatter direction matches that page's appendix kernels, which derive
+ * the output address from the input address.
+ *
+ * Matrix layout: A is passed as n row masks, A[r] holding output bit r's
+ * inputs; bit j of A[r] is the entry A_rj.  So y_r = parity(A[r] & i) ^ c_r.
+ *
+ * Every function is extern "C" and takes plain pointers and sizes.  Device
+ * pointers are HIP device allocations on the current device; `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream).  No call aborts:
+ * each returns a status (or NULL plus bmmc_last_error()).
+ */
+#ifndef BMMC_H
+#define BMMC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define BMMC_OK 0
+#define BMMC_ERR_INVALID_ARG 1   /* n, elem_bytes, stray bits, NULL, alignment */
+#define BMMC_ERR_SINGULAR 2      /* A is not invertible over F2 */
+#define BMMC_ERR_UNSUPPORTED 3   /* a valid request this build cannot run */
+#define BMMC_ERR_ALIAS 4         /* the in and out byte ranges overlap */
+#define BMMC_ERR_OUT_OF_MEMORY 5 /* scratch allocation failed */
+#define BMMC_ERR_HIP 6           /* a HIP runtime call or kernel launch failed */
+
+/* ---- classification of A (at the granularity the kernels move) --------- */
+#define BMMC_KIND_IDENTITY 0 /* A = I: a copy, or a complement-only XOR */
+#define BMMC_KIND_BPC 1      /* A is a permutation matrix: BP (c = 0) or BPC */
+#define BMMC_KIND_TILED 2    /* one tile pass with index-aligned tile rows */
+#define BMMC_KIND_GENERAL 3  /* anything else */
+
+/* ---- routes a plan may take -------------------------------------------- */
+#define BMMC_ROUTE_AUTO 0     /* planner's choice (fused single pass) */
+#define BMMC_ROUTE_NAIVE 1    /* one unit per lane, scattered stores */
+#define BMMC_ROUTE_TWO_PASS 2 /* general A as two tiled factors: segment relabel T2, then T1 */
+#define BMMC_ROUTE_FUSED 3    /* every A in one tile pass (tile rows need not be index-aligned) */
+
+/* ---- kernels a pass may run -------------------------------------------- */
+#define BMMC_KERNEL_COPY 0  /* identity order */
+#define BMMC_KERNEL_CHUNK 1 /* chunks move as units: segment relabel / complement only */
+#define BMMC_KERNEL_TILED 2 /* LDS-staged tile pass */
+#define BMMC_KERNEL_NAIVE 3 /* one unit per lane */
+
+#define BMMC_MAX_N 32      /* largest index width accepted */
+#define BMMC_MAX_BITS 36   /* index bits at byte-merged unit granularity */
+#define BMMC_MAX_TILE 8    /* largest tile side, log2 units */
+#define BMMC_MAX_PASSES 2
+
+/* Options for bmmc_plan_create_ex.  Zero-initialise, then set fields; a zero
+ * field means "planner's choice". */
+typedef struct bmmc_plan_options {
+    int route;      /* BMMC_ROUTE_* */
+    int tile_log2;  /* tile side in units (log2); 0 = planner's choice */
+    int no_swizzle; /* 1 = plain row-major LDS tile (bank-conflict ablation) */
+    int iters_log2; /* log2 of tiles per workgroup; 0 = one */
+} bmmc_plan_options;
+
+/* What a plan does, for tests and benchmarks. */
+typedef struct bmmc_plan_info {
+    int n;              /* index bits as given */
+    int elem_bytes;     /* element size as given */
+    int kind;           /* BMMC_KIND_* of the unit-level matrix */
+    int route;          /* BMMC_ROUTE_* actually taken (never AUTO) */
+    int passes;         /* kernel launches per bmmc_execute (1 or 2) */
+    int unit_bytes;     /* bytes moved as one unit: elem_bytes times the
+                           largest run of low index bits the map keeps */
+    int unit_bits;      /* index bits at unit granularity */
+    int tile_log2;      /* tile side (log2 units) of the tiled pass, 0 if none */
+    int n_over;         /* t - rank of A[t:, 0:t]: low input bits that stay low */
+    size_t scratch_bytes; /* device scratch a two-pass plan allocates */
+} bmmc_plan_info;
+
+/* Kernel tables of one pass.  All offsets are byte offsets; every table entry
+ * is XORed in when the corresponding index bit is 1, which is how the kernels
+ * evaluate A.x XOR c without a per-element matrix-vector product (the map is
+ * affine, so the address of any element is the XOR of the contributions of
+ * its block, row and lane bits).
+ *
+ * TILED: block b (bit k of the block index, the low iters_log2 bits iterated
+ * inside one workgroup) starts at input offset XOR_k in_blk[k]; tile row h
+ * (t bits) adds in_h; a row is 2^t contiguous units.  The tile is staged in
+ * LDS at address XOR_k lds_wr_h[k] over the row bits XOR XOR_k lds_wr_lo[k]
+ * over the bits of the unit's position in its row.  Output segment g (t bits) of the tile lies at XOR_k out_blk[k]
+ * XOR out_c XOR out_g(g); its unit at position y (t bits) is read from LDS
+ * address lds_rd(y, g) XOR lds_blk(b) XOR lds_c, with lds_rd indexed by y's
+ * bits (0..t-1) then g's bits (t..2t-1).
+ * CHUNK: chunk index bit k moves the output by out_blk[k]; out_c is the
+ * constant; unit_xor permutes the units inside a chunk (unit e goes to
+ * e XOR unit_xor).  The input chunk is read at chunk_index * chunk_bytes.
+ * NAIVE: unit index bit k moves the output by out_blk[k]; out_c constant.
+ * COPY: nothing but nbits/unit_log2. */
+typedef struct bmmc_pass_desc {
+    int32_t kernel;      /* BMMC_KERNEL_* */
+    int32_t unit_log2;   /* log2 bytes of one unit */
+    int32_t nbits;       /* index bits at unit granularity */
+    int32_t t;           /* tile side / segment length, log2 units (TILED) */
+    int32_t chunk_log2;  /* log2 units per vector chunk */
+    int32_t blk_bits;    /* block-index bits (TILED), chunk-index bits (CHUNK),
+                            unit-index bits (NAIVE) */
+    int32_t iters_log2;  /* tiles per workgroup, log2 (TILED) */
+    int32_t unit_xor;    /* in-chunk unit permutation (CHUNK) */
+    uint64_t out_c;
+    uint32_t lds_c;
+    uint32_t lds_bytes;  /* LDS bytes per workgroup (TILED) */
+    uint64_t in_blk[BMMC_MAX_BITS];
+    uint64_t out_blk[BMMC_MAX_BITS];
+    uint32_t lds_blk[BMMC_MAX_BITS];
+    uint64_t in_h[BMMC_MAX_TILE];
+    uint64_t out_g[BMMC_MAX_TILE];
+    uint32_t lds_wr_h[BMMC_MAX_TILE];
+    uint32_t lds_wr_lo[BMMC_MAX_TILE];
+    uint32_t lds_rd[2 * BMMC_MAX_TILE];
+} bmmc_pass_desc;
+
+typedef struct bmmc_plan bmmc_plan; /* opaque; immutable after creation */
+
+/* Plan the permutation out[A.i XOR c] = in[i] of 2^n elements of elem_bytes
+ * bytes.  Host-only: validates (1 <= n <= 32, elem_bytes in {1,2,4,8,16},
+ * no bits of A[r] or c at positions >= n, total bytes <= 2^36), inverts A over
+ * F2 (singular -> BMMC_ERR_SINGULAR), classifies it (identity, BPC, tiled,
+ * general), factorises a general A into at most two tiled factors when the
+ * two-pass route is chosen ("Efficient GPU Implementation of Affine Index
+ * Permutations on Arrays", introduction: any BMMC is a product T1.T2 of two
+ * tiled BMMCs, applied T2 first), and builds each pass's kernel tables.
+ * Makes no GPU call.  Copies A; the caller keeps ownership of its array.
+ * Returns NULL on failure, with the reason in bmmc_last_error(). */
+bmmc_plan *bmmc_plan_create(int n, const uint64_t *A, uint64_t c, size_t elem_bytes);
+
+/* As bmmc_plan_create, with options (NULL = defaults). */
+bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem_bytes,
+                               const bmmc_plan_options *opt);
+
+/* Run the plan on `stream`, asynchronously: out[A.i XOR c] = in[i].
+ * `in` and `out` are device pointers to 2^n * elem_bytes bytes each, aligned
+ * to 16 bytes (to the array size if smaller), and must not overlap
+ * (BMMC_ERR_ALIAS).  A two-pass plan allocates its scratch buffer (the size
+ * of one array) on its first call and keeps it until bmmc_plan_destroy;
+ * calls of one two-pass plan on different streams must not overlap in time.
+ * Launch failures return BMMC_ERR_HIP; faults inside a kernel surface at the
+ * caller's next synchronisation, as HIP reports them. */
+int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream);
+
+/* The ceiling: copy nbytes from `in` to `out` (device pointers, no overlap)
+ * with the same vector width and launch style as the permutation kernels,
+ * asynchronously on `stream` ("A kernel that is correct": the copy moves the
+ * same bytes in the easiest order and is the ceiling a card can reach). */
+int bmmc_copy(const void *in, void *out, size_t nbytes, void *stream);
+
+/* Free a plan and its scratch buffer.  NULL is accepted. */
+void bmmc_plan_destroy(bmmc_plan *plan);
+
+/* Status of the last bmmc_plan_create(_ex) on this thread. */
+int bmmc_last_error(void);
+
+/* A static English string for a status code. */
+const char *bmmc_status_string(int status);
+
+/* Describe a plan (host-only). */
+int bmmc_plan_get_info(const bmmc_plan *plan, bmmc_plan_info *info);
+
+/* The matrix and complement that pass `pass` applies, at element granularity
+ * (n rows); the passes compose to the planned (A, c).  Host-only. */
+int bmmc_plan_get_factor(const bmmc_plan *plan, int pass, uint64_t *A_out, uint64_t *c_out);
+
+/* The kernel tables of pass `pass` (layout above), so that a host replay can
+ * check addressing, coalescing and LDS banks without a GPU.  Host-only. */
+int bmmc_plan_get_pass(const bmmc_plan *plan, int pass, bmmc_pass_desc *desc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BMMC_H */

@@ -1,0 +1,228 @@
+"""Host replay of a plan's kernel tables (test helper, numpy only).
+
+Replays every (workgroup, thread, pass, unit) of each kernel exactly as the
+HIP kernels combine the tables of ``bmmc_pass_desc`` (include/bmmc.h), and
+checks on the way that
+  * every input unit is read once and every output unit written once,
+  * every LDS slot of a tile is written once and read once, in range,
+  * each wave's global access covers whole, aligned segments (coalescing),
+then returns the source unit of every output unit.  Comparing the permuted
+data with the oracle checks the planner without a GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE = 0, 1, 2, 3
+
+
+def _xor_table(vals: np.ndarray, table, nbits: int) -> np.ndarray:
+    vals = np.asarray(vals, dtype=np.uint64)
+    acc = np.zeros(vals.shape, dtype=np.uint64)
+    for k in range(nbits):
+        bit = (vals >> np.uint64(k)) & np.uint64(1)
+        acc ^= np.where(bit == 1, np.uint64(table[k]), np.uint64(0))
+    return acc
+
+
+def tiled_geometry(unit_log2: int, t: int):
+    wl = min(4 - unit_log2, t)
+    cpsl = t - wl
+    chl = 2 * t - wl
+    ntl = min(8, chl)
+    rppl = ntl - cpsl
+    jl = t - rppl
+    return dict(wl=wl, cpsl=cpsl, ntl=ntl, rppl=rppl, jl=jl)
+
+
+class ReplayError(AssertionError):
+    pass
+
+
+def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
+    """Source unit index of each output unit for one TILED pass."""
+    ul, t, nb = d.unit_log2, d.t, d.nbits
+    U = 1 << ul
+    g = tiled_geometry(ul, t)
+    wl, cpsl, ntl, rppl, jl = g["wl"], g["cpsl"], g["ntl"], g["rppl"], g["jl"]
+    W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
+    TILE = U << (2 * t)
+    blk_bits = d.blk_bits
+    nblk = 1 << blk_bits
+    if d.lds_bytes != TILE << d.iters_log2:
+        raise ReplayError("lds_bytes does not match the tile geometry")
+    total_units = 1 << nb
+
+    b = np.arange(nblk, dtype=np.uint64)[:, None, None]
+    tid = np.arange(NT, dtype=np.uint64)[None, :, None]
+    j = np.arange(J, dtype=np.uint64)[None, None, :]
+    q = tid & np.uint64((1 << cpsl) - 1)
+    hl = tid >> np.uint64(cpsl)
+    h = (j << np.uint64(rppl)) | hl  # tile row (input segment) index
+
+    in_off = (_xor_table(b, d.in_blk, blk_bits) ^ _xor_table(h, d.in_h, t)
+              ^ (q * np.uint64(CB)))
+    wr = _xor_table(h, d.lds_wr_h, t) ^ _xor_table(q, [d.lds_wr_lo[wl + k] for k in range(cpsl)],
+                                                   cpsl)
+    in_off, wr = np.broadcast_arrays(in_off, wr)
+    if np.any(in_off % np.uint64(CB)) or np.any(wr % np.uint64(CB)):
+        raise ReplayError("misaligned chunk")
+    if np.any(wr + np.uint64(CB) > np.uint64(TILE)):
+        raise ReplayError("LDS write out of range")
+    if np.any(in_off + np.uint64(CB) > np.uint64(total_units * U)):
+        raise ReplayError("global read out of range")
+
+    # LDS of every block, holding source unit indices
+    lds = np.full((nblk, TILE // U), -1, dtype=np.int64)
+    bidx = np.broadcast_to(np.arange(nblk)[:, None, None], in_off.shape)
+    for e in range(W):
+        slot = (wr // np.uint64(U) + np.uint64(e)).astype(np.int64)
+        src = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
+        if np.any(lds[bidx, slot] != -1):
+            raise ReplayError("LDS slot written twice")
+        lds[bidx, slot] = src
+    if np.any(lds < 0):
+        raise ReplayError("LDS slot never written")
+    read_in = np.zeros(total_units, dtype=np.int64)
+    np.add.at(read_in, lds.reshape(-1), 1)
+    if np.any(read_in != 1):
+        raise ReplayError("input unit not read exactly once")
+
+    gseg = h  # output segment index within the tile, same lane split
+    out_off = (_xor_table(b, d.out_blk, blk_bits) ^ np.uint64(d.out_c)
+               ^ _xor_table(gseg, d.out_g, t) ^ (q * np.uint64(CB)))
+    rbase = (_xor_table(b, d.lds_blk, blk_bits) ^ np.uint64(d.lds_c)
+             ^ _xor_table(gseg, [d.lds_rd[t + k] for k in range(t)], t)
+             ^ _xor_table(q, [d.lds_rd[wl + k] for k in range(cpsl)], cpsl))
+    out_off, rbase = np.broadcast_arrays(out_off, rbase)
+    if np.any(out_off % np.uint64(CB)):
+        raise ReplayError("misaligned output chunk")
+    if np.any(out_off + np.uint64(CB) > np.uint64(total_units * U)):
+        raise ReplayError("global write out of range")
+    result = np.full(total_units, -1, dtype=np.int64)
+    reads = np.zeros((nblk, TILE // U), dtype=np.int64)
+    for e in range(W):
+        rd = rbase ^ _xor_table(np.uint64(e), d.lds_rd, wl)
+        if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(TILE)):
+            raise ReplayError("LDS read misaligned or out of range")
+        slot = (rd // np.uint64(U)).astype(np.int64)
+        np.add.at(reads, (bidx, slot), 1)
+        dst = (out_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
+        if np.any(result[dst] != -1):
+            raise ReplayError("output unit written twice")
+        result[dst] = lds[bidx, slot]
+    if np.any(reads != 1):
+        raise ReplayError("LDS slot not read exactly once")
+    if np.any(result < 0):
+        raise ReplayError("output unit never written")
+
+    if check_coalescing:
+        seg = np.uint64(U << t)
+        # lanes with the same row bits cover one whole aligned segment
+        for arr in (in_off, out_off):
+            a = arr.reshape(nblk, NT >> cpsl, 1 << cpsl, J)
+            starts = a.min(axis=2)
+            if np.any(starts % seg):
+                raise ReplayError("segment not aligned")
+            rel = np.sort(a - starts[:, :, None, :], axis=2)
+            want = (np.arange(1 << cpsl, dtype=np.uint64) * np.uint64(CB))[None, None, :, None]
+            if not np.array_equal(rel, np.broadcast_to(want, rel.shape)):
+                raise ReplayError("a wave's access is not whole segments")
+    return result
+
+
+def replay_chunk(d) -> np.ndarray:
+    ul, nb, wl = d.unit_log2, d.nbits, d.chunk_log2
+    U, W = 1 << ul, 1 << wl
+    nchunks = 1 << d.blk_bits
+    x = np.arange(nchunks, dtype=np.uint64)
+    off = _xor_table(x, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)
+    if np.any(off % np.uint64(U * W)):
+        raise ReplayError("misaligned chunk store")
+    result = np.full(1 << nb, -1, dtype=np.int64)
+    for e in range(W):
+        dst = (off // np.uint64(U) + np.uint64(e)).astype(np.int64)
+        src = (x * np.uint64(W) + np.uint64(e ^ d.unit_xor)).astype(np.int64)
+        if np.any(dst >= (1 << nb)) or np.any(result[dst] != -1):
+            raise ReplayError("chunk store out of range or twice")
+        result[dst] = src
+    if np.any(result < 0):
+        raise ReplayError("output unit never written")
+    return result
+
+
+def replay_pass(d) -> np.ndarray:
+    if d.kernel == KERNEL_TILED:
+        return replay_tiled(d)
+    if d.kernel in (KERNEL_CHUNK, KERNEL_NAIVE):
+        return replay_chunk(d)
+    if d.kernel == KERNEL_COPY:
+        return np.arange(1 << d.nbits, dtype=np.int64)
+    raise ReplayError("unknown kernel %d" % d.kernel)
+
+
+def run_plan_on_host(plan, data: np.ndarray) -> np.ndarray:
+    """Apply every pass of ``plan`` (a bmmc_affine_index_amd.Plan) to a host
+    array by replaying the kernel tables; returns the permuted copy."""
+    raw = np.ascontiguousarray(data).view(np.uint8).reshape(-1)
+    cur = raw
+    for d in plan.passes():
+        U = 1 << d.unit_log2
+        units = cur.reshape(-1, U)
+        src = replay_pass(d)
+        cur = units[src].reshape(-1)
+    return cur.view(data.dtype).reshape(data.shape)
+
+
+def bank_cycles(addr, nbytes: int, banks: int) -> int:
+    """Cycles of one wave LDS access under the planner's bank model."""
+    per = (4 * banks) // nbytes if nbytes >= 4 else banks
+    per = max(1, min(64, per))
+    total = 0
+    addr = [int(a) for a in addr]
+    for g0 in range(0, len(addr), per):
+        words = set()
+        for a in addr[g0:g0 + per]:
+            for w in range(max(1, nbytes // 4)):
+                words.add(a // 4 + w)
+        cnt = {}
+        for w in words:
+            cnt[w % banks] = cnt.get(w % banks, 0) + 1
+        total += max(cnt.values()) if cnt else 1
+    return total
+
+
+def tiled_read_addresses(d):
+    """LDS byte addresses of wave 0's first output-order read (unit 0)."""
+    g = tiled_geometry(d.unit_log2, d.t)
+    lanes = min(64, 1 << g["ntl"])
+    out = []
+    for l in range(lanes):
+        q, hl = l & ((1 << g["cpsl"]) - 1), l >> g["cpsl"]
+        a = 0
+        for k in range(g["cpsl"]):
+            if (q >> k) & 1:
+                a ^= d.lds_rd[g["wl"] + k]
+        for k in range(g["rppl"]):
+            if (hl >> k) & 1:
+                a ^= d.lds_rd[d.t + k]
+        out.append(a)
+    return out
+
+
+def tiled_write_addresses(d):
+    g = tiled_geometry(d.unit_log2, d.t)
+    lanes = min(64, 1 << g["ntl"])
+    CB = 1 << (d.unit_log2 + g["wl"])
+    out = []
+    for l in range(lanes):
+        q, hl = l & ((1 << g["cpsl"]) - 1), l >> g["cpsl"]
+        a = 0
+        for k in range(g["cpsl"]):
+            if (q >> k) & 1:
+                a ^= d.lds_wr_lo[g["wl"] + k]
+        for k in range(g["rppl"]):
+            if (hl >> k) & 1:
+                a ^= d.lds_wr_h[k]
+        out.append(a)
+    return out

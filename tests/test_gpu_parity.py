@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every comparison is bit-exact (bytes).  Outputs are pre-filled with a
+sentinel so that a missed write cannot pass.  Small cases cover every kind,
+route, element size, tile side and iteration count, including the edge cases
+n = 1 and n = 2t; the five workloads run at full size with the launch
+configuration the benchmark times, checked in full where the host can hold
+the oracle's output and on sampled indices beyond that.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import bmmc_affine_index_amd as bm
+from bmmc_affine_index_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5
+HOST_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(A, c, x, **plan_kw):
+    """Permute host array x on the GPU; returns (host result, plan)."""
+    torch = _torch()
+    n = len(A)
+    raw = np.ascontiguousarray(x).view(np.uint8).reshape(-1)
+    elem = raw.size >> n
+    P = bm.Plan(n, A, c, elem, **plan_kw)
+    d_in = torch.from_numpy(raw.copy()).to("cuda:0")
+    d_out = torch.full_like(d_in, SENTINEL)
+    P(d_in, d_out)
+    torch.cuda.synchronize()
+    got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
+    return got, P
+
+
+def _inv(n, seed):
+    return wl.random_bmmc(n, seed, lambda r: oracle.rank(r) == n)
+
+
+def _matrix(kind, n, seed):
+    if kind == "bitrev":
+        return wl.bit_reverse_matrix(n), 0
+    if kind == "transpose":
+        return wl.transpose_matrix(n // 2, n - n // 2), 0
+    if kind == "bpc":
+        return wl.random_bpc(n, seed)
+    if kind == "complement":
+        return wl.identity_matrix(n), ((1 << n) - 1) & (0x5A5A5A5A5 ^ seed)
+    if kind == "identity":
+        return wl.identity_matrix(n), 0
+    return _inv(n, seed)
+
+
+# --------------------------------------------------------------------------
+# small cases: every route and element size
+# --------------------------------------------------------------------------
+
+SMALL = []
+for e in (1, 2, 4, 8, 16):
+    for n in (1, 2, 3, 5, 8, 11, 12, 14, 17):
+        for kind in ("bitrev", "bpc", "general", "complement"):
+            SMALL.append((kind, n, e, {}))
+    for kind in ("transpose", "identity"):
+        SMALL.append((kind, 16, e, {}))
+    SMALL.append(("general", 16, e, dict(route=bm.ROUTE_TWO_PASS)))
+    SMALL.append(("general", 13, e, dict(route=bm.ROUTE_NAIVE)))
+for t in (1, 2, 3, 4, 5, 6, 7):
+    SMALL.append(("general", 16, 4, dict(tile_log2=t)))
+    SMALL.append(("bpc", 16, 4, dict(tile_log2=t)))
+for it in (1, 2, 3):
+    SMALL.append(("general", 18, 4, dict(iters_log2=it)))
+    SMALL.append(("bitrev", 18, 4, dict(iters_log2=it)))
+    SMALL.append(("bpc", 18, 16, dict(iters_log2=it)))
+SMALL.append(("general", 15, 4, dict(no_swizzle=1)))
+SMALL.append(("bitrev", 12, 4, dict(tile_log2=6)))  # n = 2t: a single tile
+SMALL.append(("general", 12, 4, dict(tile_log2=6)))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "%s-n%d-e%d-%s" % (
+    c[0], c[1], c[2], "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
+def test_small_parity(case):
+    kind, n, e, kw = case
+    A, c = _matrix(kind, n, 7000 + 37 * n + e)
+    x = wl.fill_random_bytes(n, e, seed=n * 131 + e)
+    got, P = _run(A, c, x, **kw)
+    want = oracle.apply(A, c, x)
+    assert np.array_equal(got, want), P.describe()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_general_sweep(seed):
+    """Random sizes and matrices over both general routes."""
+    rng = np.random.Generator(np.random.PCG64(99 + seed))
+    n = int(rng.integers(4, 21))
+    e = int(rng.choice([1, 2, 4, 8, 16]))
+    A, c = _inv(n, 8000 + seed)
+    x = wl.fill_random_bytes(n, e, seed=seed)
+    want = oracle.apply(A, c, x)
+    for route in (bm.ROUTE_AUTO, bm.ROUTE_TWO_PASS):
+        got, P = _run(A, c, x, route=route)
+        assert np.array_equal(got, want), P.describe()
+
+
+def test_copy_ceiling_kernel():
+    torch = _torch()
+    for nbytes in (0, 1, 15, 16, 4096 + 7, (1 << 20) + 48, 3 << 20):
+        src = torch.randint(0, 256, (max(nbytes, 1),), dtype=torch.uint8, device="cuda:0")
+        dst = torch.full_like(src, SENTINEL)
+        bm.copy(src, dst, nbytes)
+        torch.cuda.synchronize()
+        assert torch.equal(src[:nbytes], dst[:nbytes])
+        if nbytes < src.numel():
+            assert int(dst[nbytes:].eq(SENTINEL).all()) == 1
+
+
+def test_two_pass_plan_reused_and_streams():
+    """A two-pass plan reuses its scratch across calls and runs on a side stream."""
+    torch = _torch()
+    n = 18
+    A, c = _inv(n, 4242)
+    P = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    s = torch.cuda.Stream()
+    for k in range(3):
+        x = wl.fill_random_bytes(n, 4, seed=k).view(np.uint32).reshape(-1)
+        d_in = torch.from_numpy(x.view(np.int32).copy()).to("cuda:0")
+        d_out = torch.full_like(d_in, -1)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            P(d_in, d_out, stream=s)
+        s.synchronize()
+        assert np.array_equal(d_out.cpu().numpy().view(np.uint32), oracle.apply(A, c, x))
+
+
+def test_execute_rejects_alias_on_device():
+    torch = _torch()
+    P = bm.Plan(12, wl.bit_reverse_matrix(12), 0, 4)
+    buf = torch.zeros(2 << 12, dtype=torch.int32, device="cuda:0")
+    assert bm.bmmc_execute(P.handle, buf, buf[100:], None) == bm.ERR_ALIAS
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size
+# --------------------------------------------------------------------------
+
+def _device_run(name, A, c, x, **plan_kw):
+    torch = _torch()
+    n = wl.WORKLOADS[name].n
+    raw = x.reshape(-1).view(np.uint8)
+    P = bm.Plan(n, A, c, raw.size >> n, **plan_kw)
+    d_in = torch.from_numpy(raw).to("cuda:0")
+    d_out = torch.full_like(d_in, SENTINEL)
+    P(d_in, d_out)
+    torch.cuda.synchronize()
+    got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
+    del d_in, d_out
+    torch.cuda.empty_cache()
+    return got, P
+
+
+def _lib_accepts(n):
+    def accept(rows):
+        h = bm.bmmc_plan_create(n, rows, 0, 4)
+        if h:
+            bm.bmmc_plan_destroy(h)
+        return bool(h)
+    return accept
+
+
+def _sample_idx(n, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = rng.integers(0, 1 << n, size=count, dtype=np.uint64)
+    # the ends of the array and the segment edges are always included
+    edges = np.array([0, 1, (1 << n) - 1, (1 << n) - 2, 63, 64, 4095, 4096], dtype=np.uint64)
+    return np.concatenate([edges[edges < (1 << n)], idx])
+
+
+@pytest.mark.parametrize("name", ["c1a", "c1b", "c2"])
+def test_workload_full_check(name):
+    n = wl.WORKLOADS[name].n
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == n)
+    # the oracle's choice of the random matrix is the library's choice too
+    if name == "c1a":
+        assert np.array_equal(A, wl.workload_matrix(name, accept=_lib_accepts(n))[0])
+    x = wl.workload_data(name)
+    want = oracle.apply(A, c, x, threads=HOST_THREADS)
+    routes = [{}] + ([dict(route=bm.ROUTE_TWO_PASS)] if name == "c1a" else [])
+    for kw in routes:
+        _note("%s %s" % (name, kw))
+        got, P = _device_run(name, A, c, x, **kw)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), P.describe()
+    if name == "c2":
+        # the transpose of the 4096 x 4096 fp32 matrix, as two loops would give it
+        assert np.array_equal(got.view(np.uint32),
+                              x.reshape(4096, 4096).T.reshape(-1).view(np.uint32))
+
+
+def test_workload_c3_bitrev28_full():
+    name = "c3"
+    A, c = wl.workload_matrix(name)
+    x = wl.workload_data(name)
+    _note("c3: oracle")
+    want = oracle.apply(A, c, x, threads=HOST_THREADS)
+    _note("c3: gpu")
+    got, P = _device_run(name, A, c, x)
+    assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
+    assert np.array_equal(got, want), P.describe()
+
+
+def test_workload_c4_general30():
+    name = "c4"
+    n = 30
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == n)
+    x = wl.workload_data(name)
+    _note("c4: oracle")
+    want = oracle.apply(A, c, x, threads=HOST_THREADS)
+    for kw in ({}, dict(route=bm.ROUTE_TWO_PASS)):
+        _note("c4 %s" % kw)
+        got, P = _device_run(name, A, c, x, **kw)
+        assert P.info.kind == bm.KIND_GENERAL
+        bad, first = oracle.check_sampled(A, c, x, got, _sample_idx(n, 1 << 20, 30))
+        assert bad == 0, (first, P.describe())
+        assert np.array_equal(got, want), P.describe()
+        del got
+
+
+def test_workload_c5_random_bpc_records():
+    torch = _torch()
+    name = "c5"
+    n = 27
+    x = wl.workload_data(name)
+    d_in = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    d_out = torch.empty_like(d_in)
+    for k in range(32):
+        A, c = wl.workload_matrix(name, perm_index=k)
+        _note("c5 perm %d" % k)
+        P = bm.Plan(n, A, c, 16)
+        assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        torch.cuda.synchronize()
+        got = d_out.cpu().numpy().view(np.float32).reshape(x.shape)
+        if k in (0, 31):
+            want = oracle.apply(A, c, x, threads=HOST_THREADS)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), P.describe()
+            del want
+        else:
+            bad, first = oracle.check_sampled(A, c, x, got, _sample_idx(n, 1 << 18, k))
+            assert bad == 0, (k, first, P.describe())
+        del got

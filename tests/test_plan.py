@@ -1,0 +1,338 @@
+"""CPU tests of the C-ABI library: exports, argument checks, the planner's F2
+algebra (classification, tile test, factorisation) and a host replay of every
+kernel table against the oracle.  No GPU call is made."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import bmmc_affine_index_amd as bm
+from bmmc_affine_index_amd import workloads as wl
+
+from emulate import (ReplayError, bank_cycles, run_plan_on_host, tiled_read_addresses,
+                     tiled_write_addresses)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _inv(n, seed):
+    return wl.random_bmmc(n, seed, lambda r: oracle.rank(r) == n)
+
+
+# --------------------------------------------------------------------------
+# The library and its exports
+# --------------------------------------------------------------------------
+
+def test_library_exports_every_header_function():
+    header = open(os.path.join(ROOT, "include", "bmmc.h")).read()
+    names = set(re.findall(r"^\S[^;()]*?\b(bmmc_\w+)\s*\(", header, flags=re.M))
+    assert names == set(bm.EXPORTED)
+    L = bm.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_struct_sizes_match_header_layout():
+    import ctypes
+    # 8 int32 + u64 + 2 u32 + 2*36 u64 + 36 u32 + 2*8 u64 + 2*8 u32 + 16 u32
+    expect = 8 * 4 + 8 + 2 * 4 + 2 * 36 * 8 + 36 * 4 + 2 * 8 * 8 + 2 * 8 * 4 + 16 * 4
+    assert ctypes.sizeof(bm.bmmc_pass_desc) == expect
+
+
+# --------------------------------------------------------------------------
+# Argument validation (returns before any GPU call)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,A,c,e,status", [
+    (0, [], 0, 4, bm.ERR_INVALID_ARG),
+    (33, [1 << r for r in range(33)], 0, 4, bm.ERR_INVALID_ARG),
+    (3, [1, 2, 4], 0, 3, bm.ERR_INVALID_ARG),
+    (3, [1, 2, 4], 0, 32, bm.ERR_INVALID_ARG),
+    (3, [1, 2, 4], 0, 0, bm.ERR_INVALID_ARG),
+    (3, [1, 2, 8], 0, 4, bm.ERR_INVALID_ARG),       # stray bit in A
+    (3, [1, 2, 4], 8, 4, bm.ERR_INVALID_ARG),       # stray bit in c
+    (3, [1, 2, 3], 0, 4, bm.ERR_SINGULAR),
+    (32, [1 << r for r in range(32)], 0, 32, bm.ERR_INVALID_ARG),
+    (32, [1 << r for r in range(32)], 0, 32, bm.ERR_INVALID_ARG),
+])
+def test_plan_create_errors(n, A, c, e, status):
+    h = bm.bmmc_plan_create(n, A, c, e)
+    assert h == 0
+    assert bm.bmmc_last_error() == status
+    assert bm.bmmc_status_string(status)
+
+
+def test_plan_create_largest_sizes():
+    # the largest arrays: 2^32 elements of 16 bytes (2^36 bytes), general A
+    A, c = _inv(32, 32)
+    for e in (4, 16):
+        h = bm.bmmc_plan_create(32, A, c, e)
+        assert h != 0, bm.bmmc_last_error()
+        info = bm.bmmc_plan_get_info(h)
+        assert info.unit_bits + (info.unit_bytes.bit_length() - 1) == 32 + (e.bit_length() - 1)
+        bm.bmmc_plan_destroy(h)
+
+
+def test_execute_argument_errors_without_gpu():
+    p = bm.Plan(10, wl.bit_reverse_matrix(10), 0, 4)
+    assert bm.bmmc_execute(p.handle, 0, 4096, None) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_execute(0, 4096, 8192, None) == bm.ERR_INVALID_ARG
+    # misaligned
+    assert bm.bmmc_execute(p.handle, 1 << 20 | 4, 1 << 24, None) == bm.ERR_INVALID_ARG
+    # overlapping ranges (the array is 4 KiB)
+    assert bm.bmmc_execute(p.handle, 1 << 20, (1 << 20) + 2048, None) == bm.ERR_ALIAS
+    assert bm.bmmc_copy(1 << 20, (1 << 20) + 16, 64, None) == bm.ERR_ALIAS
+    assert bm.bmmc_copy(0, 1 << 20, 64, None) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_copy(0, 0, 0, None) == bm.OK
+    for k in (-1, 1):
+        with pytest.raises(bm.BmmcError):
+            bm.bmmc_plan_get_pass(p.handle, k)
+
+
+def test_destroy_null_is_safe():
+    bm.bmmc_plan_destroy(0)
+
+
+# --------------------------------------------------------------------------
+# Classification
+# --------------------------------------------------------------------------
+
+def test_classification_of_named_cases():
+    P = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4)
+    assert P.info.kind == bm.KIND_BPC and P.info.passes == 1
+    assert P.info.unit_bytes == 4 and P.info.tile_log2 == 6
+    P = bm.Plan(24, wl.transpose_matrix(12, 12), 0, 4)
+    assert P.info.kind == bm.KIND_BPC and P.info.passes == 1
+    P = bm.Plan(12, wl.identity_matrix(12), 0, 4)
+    assert P.info.kind == bm.KIND_IDENTITY and P.passes()[0].kernel == bm.KERNEL_COPY
+    P = bm.Plan(12, wl.identity_matrix(12), 0xABC, 4)
+    assert P.info.kind == bm.KIND_IDENTITY and P.passes()[0].kernel == bm.KERNEL_CHUNK
+    A, c = _inv(20, 20)
+    P = bm.Plan(20, A, c, 4)
+    assert P.info.kind == bm.KIND_GENERAL and P.info.passes == 1
+    P = bm.Plan(20, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    assert P.info.passes == 2 and P.info.route == bm.ROUTE_TWO_PASS
+    assert P.info.scratch_bytes == 4 << 20
+
+
+def test_unit_merging():
+    # low bits that stay in place widen the unit up to 16 bytes
+    n = 10
+    perm = list(range(2)) + list(np.random.default_rng(1).permutation(np.arange(2, n)))
+    A = wl.bit_permutation_matrix(perm)
+    P = bm.Plan(n, A, 0, 4)
+    assert P.info.unit_bytes == 16 and P.info.unit_bits == n - 2
+    # a complement bit in the low bits stops the merge
+    P = bm.Plan(n, A, 1, 4)
+    assert P.info.unit_bytes == 4
+
+
+def test_bpc_is_always_tiled():
+    """Every BPC is a tiled BMMC (one pass)."""
+    for seed in range(40):
+        n = 8 + seed % 20
+        A, c = wl.random_bpc(n, seed)
+        P = bm.Plan(n, A, c, 4)
+        assert P.info.kind in (bm.KIND_BPC, bm.KIND_IDENTITY)
+        assert P.info.passes == 1
+
+
+def _bruteforce_tiled(A, n, t):
+    """Is there a set H of t high bits such that every coset of
+    span(low t bits, H) maps onto whole output segments?"""
+    from itertools import combinations
+    N = 1 << n
+    ys = np.array([oracle.map_index(A, 0, i) for i in range(N)], dtype=np.int64)
+    for H in combinations(range(t, n), t):
+        mask = (1 << t) - 1
+        for h in H:
+            mask |= 1 << h
+        ok = True
+        # representatives of the cosets: indices with zero bits in the mask
+        for base in range(N):
+            if base & mask:
+                continue
+            members = [base]
+            for b in range(n):
+                if (mask >> b) & 1:
+                    members += [m | (1 << b) for m in members]
+            segs = {}
+            for m in members:
+                y = ys[m]
+                segs.setdefault(y >> t, set()).add(y & ((1 << t) - 1))
+            if any(len(v) != (1 << t) for v in segs.values()):
+                ok = False
+                break
+        if ok:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("n,t", [(6, 2), (7, 2), (8, 3)])
+def test_tile_test_matches_bruteforce(n, t):
+    rng = np.random.Generator(np.random.PCG64(n * 10 + t))
+    agree = tiled = 0
+    for k in range(25):
+        if k % 3 == 0:
+            A, c = wl.random_bpc(n, 500 + k)
+        else:
+            A, c = _inv(n, 600 + k + 100 * n)
+        # 16-byte elements: no unit merging, so the unit map is A itself
+        P = bm.Plan(n, A, 0, 16, tile_log2=t)
+        got = P.info.kind in (bm.KIND_BPC, bm.KIND_TILED, bm.KIND_IDENTITY)
+        want = _bruteforce_tiled(A, n, t)
+        assert got == want, (A, t)
+        agree += 1
+        tiled += want
+    assert agree == 25 and 0 < tiled < 25
+
+
+# --------------------------------------------------------------------------
+# Factorisation
+# --------------------------------------------------------------------------
+
+def _dense(A, n):
+    return ((np.asarray(A, dtype=np.uint64)[:, None] >> np.arange(n, dtype=np.uint64)) & 1
+            ).astype(np.int64)
+
+
+@pytest.mark.parametrize("n,seed", [(14, 1), (16, 2), (20, 20), (24, 4), (30, 30)])
+def test_two_pass_factors_multiply_back(n, seed):
+    A, c = _inv(n, seed)
+    P = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    # a random A is not tiled once n > 2t, so it needs both factors
+    assert P.info.kind == bm.KIND_GENERAL
+    assert P.info.passes == 2
+    (A2, c2), (A1, c1) = P.factors()
+    prod = (_dense(A1, n) @ _dense(A2, n)) % 2
+    assert np.array_equal(prod, _dense(A, n))
+    assert c2 == 0
+    # A1.c2 XOR c1 = c  (c2 = 0)
+    assert c1 == c
+    t = P.info.tile_log2
+    # T2 keeps every 2^t-element segment together: low t rows and columns are identity
+    D2 = _dense(A2, n)
+    assert np.array_equal(D2[:t, :t], np.eye(t, dtype=np.int64))
+    assert not D2[:t, t:].any() and not D2[t:, :t].any()
+    # T1's tile rows lie in {t, ..., 2t-1}: its inverse's first t columns
+    # have no high rows outside that range
+    B1 = _dense(oracle.inverse(A1), n)
+    assert not B1[2 * t:, :t].any()
+    # each factor is a single tiled pass
+    for k, d in enumerate(P.passes()):
+        assert d.kernel == (bm.KERNEL_CHUNK if k == 0 else bm.KERNEL_TILED)
+
+
+# --------------------------------------------------------------------------
+# Host replay of the kernel tables against the oracle
+# --------------------------------------------------------------------------
+
+def _cases():
+    cases = []
+    for e in (1, 2, 4, 8, 16):
+        cases.append(("bitrev", 12, e, dict()))
+        cases.append(("transpose", 12, e, dict()))
+        cases.append(("bpc", 13, e, dict()))
+        cases.append(("general", 12, e, dict()))
+        cases.append(("general", 12, e, dict(route=bm.ROUTE_TWO_PASS)))
+        cases.append(("general", 11, e, dict(route=bm.ROUTE_NAIVE)))
+        cases.append(("complement", 10, e, dict()))
+    for t in (1, 2, 3, 4, 5):
+        cases.append(("general", 12, 4, dict(tile_log2=t)))
+        cases.append(("bpc", 12, 4, dict(tile_log2=t)))
+    for it in (1, 2, 3):
+        cases.append(("general", 16, 4, dict(iters_log2=it)))
+        cases.append(("bitrev", 16, 4, dict(iters_log2=it)))
+    cases.append(("general", 14, 4, dict(no_swizzle=1)))
+    cases.append(("general", 5, 4, dict()))
+    cases.append(("general", 2, 4, dict()))
+    cases.append(("general", 1, 4, dict()))
+    cases.append(("bitrev", 1, 1, dict()))
+    cases.append(("bitrev", 3, 16, dict()))
+    cases.append(("general", 18, 4, dict()))
+    return cases
+
+
+def _matrix(kind, n, seed):
+    if kind == "bitrev":
+        return wl.bit_reverse_matrix(n), 0
+    if kind == "transpose":
+        return wl.transpose_matrix(n // 2, n - n // 2), 0
+    if kind == "bpc":
+        return wl.random_bpc(n, seed)
+    if kind == "complement":
+        return wl.identity_matrix(n), (0x2AAAAAAAA + seed) & ((1 << n) - 1)
+    return _inv(n, seed)
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "%s-n%d-e%d-%s" % (
+    c[0], c[1], c[2], "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
+def test_replay_matches_oracle(case):
+    kind, n, e, kw = case
+    A, c = _matrix(kind, n, 1000 + n + e)
+    P = bm.Plan(n, A, c, e, **kw)
+    x = wl.fill_random_bytes(n, e, seed=n * 31 + e)
+    got = run_plan_on_host(P, x)
+    want = oracle.apply(A, c, x)
+    assert np.array_equal(got, want), P.describe()
+
+
+def test_replay_full_size_transpose_tables():
+    """The 4096 x 4096 fp32 transpose plan, replayed over all 4096 tiles."""
+    A, c = wl.workload_matrix("c2")
+    P = bm.Plan(24, A, c, 4)
+    x = wl.workload_data("c2")
+    got = run_plan_on_host(P, x)
+    assert np.array_equal(got.view(np.uint32), x.reshape(4096, 4096).T.reshape(-1).view(np.uint32))
+
+
+def test_replay_detects_planted_table_errors():
+    from emulate import replay_pass
+    A, c = _inv(12, 5)
+    P = bm.Plan(12, A, c, 4)
+    # a read map that is no longer a bijection reads a slot twice
+    d = P.passes()[0]
+    d.lds_rd[3] = d.lds_rd[2]
+    with pytest.raises(ReplayError):
+        replay_pass(d)
+    # a still-bijective but wrong map is caught by the comparison with the oracle
+    d = P.passes()[0]
+    d.lds_rd[3] ^= d.lds_rd[2]
+    x = np.arange(1 << 12, dtype=np.int32)
+    got = x[replay_pass(d)]
+    assert not np.array_equal(got, oracle.apply(A, c, x))
+
+
+# --------------------------------------------------------------------------
+# LDS banks under the planner's model
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,n,e", [("bitrev", 20, 4), ("transpose", 24, 4),
+                                      ("general", 20, 4), ("general", 30, 4),
+                                      ("bpc", 27, 16), ("bitrev", 28, 4)])
+def test_swizzle_makes_reads_conflict_free(kind, n, e):
+    A, c = _matrix(kind, n, 7)
+    P = bm.Plan(n, A, c, e)
+    d = P.passes()[-1]
+    assert d.kernel == bm.KERNEL_TILED
+    U = 1 << d.unit_log2
+    ra = tiled_read_addresses(d)
+    wa = tiled_write_addresses(d)
+    CB = U << min(4 - d.unit_log2, d.t)
+    lanes = len(ra)
+    for banks in (32, 64):
+        ideal_r = -(-lanes * max(U, 4) // (4 * banks))
+        ideal_w = -(-lanes * CB // (4 * banks))
+        # conflict-free for a full-wave 64-bank LDS; at most 2-way when the
+        # LDS serves half-waves over 32 banks (the lanes of one half do not
+        # span both low bank bits for some bit permutations)
+        assert bank_cycles(ra, U, banks) <= ideal_r * (1 if banks == 64 else 2), \
+            (banks, P.describe())
+        assert bank_cycles(wa, CB, banks) == ideal_w
+    # the plain layout is conflicted for the transpose (the ablation)
+    if kind == "transpose":
+        P0 = bm.Plan(n, A, c, e, no_swizzle=1)
+        r0 = tiled_read_addresses(P0.passes()[0])
+        assert bank_cycles(r0, U, 64) > bank_cycles(ra, U, 64)
