@@ -134,7 +134,7 @@ def cpu_baseline(A, c, x, budget_s: float):
         oracle.apply_range(A, c, x, out, lo, lo + span, threads=threads)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 64:
+        if el >= budget_s or done >= 100000:
             break
     moved = 2.0 * done * span * elem
     return {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--tile-log2", type=int, default=0)
     ap.add_argument("--iters-log2", type=int, default=0)
     ap.add_argument("--no-swizzle", action="store_true")
+    ap.add_argument("--launch", default="auto", choices=["auto", "one_tile", "persistent"])
+    ap.add_argument("--grid-log2", type=int, default=0)
+    ap.add_argument("--walk", default="auto", choices=["auto", "ranges", "interleaved"])
     ap.add_argument("--warm", action="store_true", help="reuse one buffer pair")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -183,8 +186,12 @@ def main():
              "fused": bm.ROUTE_FUSED}[args.route]
 
     t0 = time.perf_counter()
+    launch = {"auto": bm.LAUNCH_AUTO, "one_tile": bm.LAUNCH_ONE_TILE,
+              "persistent": bm.LAUNCH_PERSISTENT}[args.launch]
     plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
-                   no_swizzle=args.no_swizzle, iters_log2=args.iters_log2)
+                   no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
+                   grid_log2=args.grid_log2,
+                   walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk])
     plan_us = (time.perf_counter() - t0) * 1e6
     if name == "c4" and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2

@@ -47,7 +47,7 @@ bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem
         for (int k = 0; k < p->npasses; ++k) {
             const bmmc_pass_desc &d = p->pass[k];
             if (d.kernel == BMMC_KERNEL_TILED &&
-                !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2))
+                !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2, d.launch))
                 st = BMMC_ERR_UNSUPPORTED;
         }
     }

@@ -40,66 +40,138 @@ template <int UL, int T, int IT> struct TiledCfg {
     static_assert(RPPL >= 0 && JL >= 0, "tile geometry");
 };
 
+// Per-lane address parts, fixed for the whole launch.
+struct LaneParts {
+    uint64_t in_lane, out_lane;
+    uint32_t wr_lane, rd_lane;
+};
+
+template <class C, int T>
+__device__ __forceinline__ LaneParts lane_parts(const bmmc_pass_desc &d, uint32_t tid) {
+    const uint32_t q = tid & ((1u << C::CPSL) - 1);  // chunk within a row / segment
+    const uint32_t hl = tid >> C::CPSL;              // low row (segment) bits
+    LaneParts p;
+    p.in_lane = dev::xor_bits_lane<C::RPPL>(d.in_h, hl) ^ (uint64_t)(q * C::CB);
+    p.wr_lane = dev::xor_bits_lane<C::RPPL>(d.lds_wr_h, hl) ^
+                dev::xor_bits_lane<C::CPSL>(d.lds_wr_lo + C::WL, q);
+    p.out_lane = dev::xor_bits_lane<C::RPPL>(d.out_g, hl) ^ (uint64_t)(q * C::CB);
+    p.rd_lane = dev::xor_bits_lane<C::CPSL>(d.lds_rd + C::WL, q) ^
+                dev::xor_bits_lane<C::RPPL>(d.lds_rd + T, hl);
+    return p;
+}
+
+// Issue the global loads of one tile (rows j * 2^RPPL + lane row bits).
+template <class C, int T>
+__device__ __forceinline__ void load_tile(dev::Chunk<C::CB> (&v)[C::J], const uint8_t *in,
+                                          uint64_t in_base, const bmmc_pass_desc &d,
+                                          const LaneParts &p) {
+#pragma unroll
+    for (int j = 0; j < C::J; ++j) {
+        const uint64_t in_j = in_base ^ dev::xor_bits_lane<C::JL>(d.in_h + C::RPPL, (uint32_t)j);
+        v[j] = dev::gload<C::CB>(in + (in_j ^ p.in_lane));
+    }
+}
+
+// Write the tile's chunks to LDS through the swizzle.
+template <class C, int T>
+__device__ __forceinline__ void stage_tile(uint8_t *tile_lds, const dev::Chunk<C::CB> (&v)[C::J],
+                                           const bmmc_pass_desc &d, const LaneParts &p) {
+#pragma unroll
+    for (int j = 0; j < C::J; ++j) {
+        const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.lds_wr_h + C::RPPL, (uint32_t)j);
+        dev::lds_store<C::CB>(tile_lds + (wr_j ^ p.wr_lane), v[j]);
+    }
+}
+
+// Read the tile back in output order and store whole output segments.
+template <class C, int T>
+__device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds, uint64_t obase,
+                                           uint32_t rbase, const bmmc_pass_desc &d,
+                                           const LaneParts &p) {
+#pragma unroll
+    for (int j = 0; j < C::J; ++j) {
+        const uint64_t out_j = obase ^ dev::xor_bits_lane<C::JL>(d.out_g + C::RPPL, (uint32_t)j);
+        const uint32_t rd_j =
+            rbase ^ dev::xor_bits_lane<C::JL>(d.lds_rd + T + C::RPPL, (uint32_t)j) ^ p.rd_lane;
+        dev::Chunk<C::CB> ch;
+        dev::zero(ch);
+#pragma unroll
+        for (int e = 0; e < C::W; ++e) {
+            const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.lds_rd, (uint32_t)e);
+            dev::put_unit<C::CB, C::U>(ch, e, dev::lds_load_unit<C::U>(tile_lds + (rd_j ^ rd_e)));
+        }
+        dev::gstore<C::CB>(out + (out_j ^ p.out_lane), ch);
+    }
+}
+
+// One workgroup per tile, or per 2^IT tiles whose loads are all issued
+// before the barrier (the pages' iterated variant).
 template <int UL, int T, int IT>
 __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
     bmmc_tiled_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                       const bmmc_pass_desc d, uint64_t blk0) {
     using C = TiledCfg<UL, T, IT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
-
-    const uint32_t tid = threadIdx.x;
-    const uint32_t q = tid & ((1u << C::CPSL) - 1);  // chunk within a row / segment
-    const uint32_t hl = tid >> C::CPSL;              // low row (segment) bits
-
-    // per-lane parts of the addresses
-    const uint64_t in_lane = dev::xor_bits_lane<C::RPPL>(d.in_h, hl) ^ (uint64_t)(q * C::CB);
-    const uint32_t wr_lane = dev::xor_bits_lane<C::RPPL>(d.lds_wr_h, hl) ^
-                             dev::xor_bits_lane<C::CPSL>(d.lds_wr_lo + C::WL, q);
-    const uint64_t out_lane = dev::xor_bits_lane<C::RPPL>(d.out_g, hl) ^ (uint64_t)(q * C::CB);
-    const uint32_t rd_lane = dev::xor_bits_lane<C::CPSL>(d.lds_rd + C::WL, q) ^
-                             dev::xor_bits_lane<C::RPPL>(d.lds_rd + T, hl);
-
+    const LaneParts p = lane_parts<C, T>(d, threadIdx.x);
     const uint64_t tile0 = (blk0 + blockIdx.x) << IT;
 
     dev::Chunk<C::CB> v[1 << IT][C::J];
 #pragma unroll
-    for (int s = 0; s < (1 << IT); ++s) {
-        const uint64_t base = dev::xor_bits_uniform(d.in_blk, tile0 | (uint64_t)s);
+    for (int s = 0; s < (1 << IT); ++s)
+        load_tile<C, T>(v[s], in, dev::xor_bits_uniform(d.in_blk, tile0 | (uint64_t)s), d, p);
 #pragma unroll
-        for (int j = 0; j < C::J; ++j) {
-            const uint64_t in_j = base ^ dev::xor_bits_lane<C::JL>(d.in_h + C::RPPL, (uint32_t)j);
-            v[s][j] = dev::gload<C::CB>(in + (in_j ^ in_lane));
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < (1 << IT); ++s) {
-#pragma unroll
-        for (int j = 0; j < C::J; ++j) {
-            const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.lds_wr_h + C::RPPL, (uint32_t)j);
-            dev::lds_store<C::CB>(lds + s * C::TILE + (wr_j ^ wr_lane), v[s][j]);
-        }
-    }
+    for (int s = 0; s < (1 << IT); ++s) stage_tile<C, T>(lds + s * C::TILE, v[s], d, p);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s) {
         const uint64_t blk = tile0 | (uint64_t)s;
-        const uint64_t obase = dev::xor_bits_uniform(d.out_blk, blk) ^ d.out_c;
-        const uint32_t rbase = dev::xor_bits_uniform(d.lds_blk, blk) ^ d.lds_c;
-#pragma unroll
-        for (int j = 0; j < C::J; ++j) {
-            const uint64_t out_j =
-                obase ^ dev::xor_bits_lane<C::JL>(d.out_g + C::RPPL, (uint32_t)j);
-            const uint32_t rd_j =
-                rbase ^ dev::xor_bits_lane<C::JL>(d.lds_rd + T + C::RPPL, (uint32_t)j) ^ rd_lane;
-            dev::Chunk<C::CB> ch;
-            dev::zero(ch);
-#pragma unroll
-            for (int e = 0; e < C::W; ++e) {
-                const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.lds_rd, (uint32_t)e);
-                dev::put_unit<C::CB, C::U>(
-                    ch, e, dev::lds_load_unit<C::U>(lds + s * C::TILE + (rd_j ^ rd_e)));
-            }
-            dev::gstore<C::CB>(out + (out_j ^ out_lane), ch);
+        drain_tile<C, T>(out, lds + s * C::TILE, dev::xor_bits_uniform(d.out_blk, blk) ^ d.out_c,
+                         dev::xor_bits_uniform(d.lds_blk, blk) ^ d.lds_c, d, p);
+    }
+}
+
+// Persistent: 2^grid_log2 workgroups; workgroup w walks 2^r tiles in Gray
+// order, either its own block range (w * 2^r XOR gray(k)) or interleaved
+// with the others (gray(k) * 2^grid_log2 XOR w), so consecutive tiles of a
+// workgroup differ in one block bit and the wave-uniform bases change by one
+// table entry each.  The LDS holds
+// two tiles: while tile k is read back and stored, the loads of tile k+1 are
+// already in flight.  One barrier per tile suffices: a buffer is rewritten
+// two tiles later, after every thread has passed the barrier that follows
+// its reads.
+template <int UL, int T>
+__global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
+    bmmc_tiled_persistent_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                                 const bmmc_pass_desc d) {
+    using C = TiledCfg<UL, T, 0>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE];
+    const LaneParts p = lane_parts<C, T>(d, threadIdx.x);
+    const int r = d.blk_bits - d.grid_log2;
+    const bool interleaved = d.walk == BMMC_WALK_INTERLEAVED;
+    const uint64_t first = interleaved ? (uint64_t)blockIdx.x : ((uint64_t)blockIdx.x << r);
+    const int shift = interleaved ? d.grid_log2 : 0;  // the walked block bits start here
+    const uint64_t count = uint64_t(1) << r;
+
+    uint64_t in_base = dev::xor_bits_uniform(d.in_blk, first);
+    uint64_t out_base = dev::xor_bits_uniform(d.out_blk, first) ^ d.out_c;
+    uint32_t rd_base = dev::xor_bits_uniform(d.lds_blk, first) ^ d.lds_c;
+
+    dev::Chunk<C::CB> v[C::J];
+    load_tile<C, T>(v, in, in_base, d, p);
+    for (uint64_t k = 0; k < count; ++k) {
+        uint8_t *buf = lds + (k & 1) * C::TILE;
+        stage_tile<C, T>(buf, v, d, p);
+        __syncthreads();
+        const bool more = k + 1 < count;
+        const int bit = more ? shift + __builtin_ctzll(k + 1) : 0;
+        if (more) {
+            in_base ^= d.in_blk[bit];
+            load_tile<C, T>(v, in, in_base, d, p);
+        }
+        drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
+        if (more) {
+            out_base ^= d.out_blk[bit];
+            rd_base ^= d.lds_blk[bit];
         }
     }
 }
@@ -118,6 +190,15 @@ struct TiledArgs {
 
 template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     using C = TiledCfg<UL, T, IT>;
+    if (a.d->launch == BMMC_LAUNCH_PERSISTENT) {
+        if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
+            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
+                               dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out, *a.d);
+            return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+        } else {
+            return BMMC_ERR_UNSUPPORTED;
+        }
+    }
     const uint64_t blocks = uint64_t(1) << (a.d->blk_bits - IT);
     for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
         const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
@@ -150,12 +231,22 @@ int dispatch(int ul, int t, int it, const TiledArgs *a) {
 
 }  // namespace
 
-bool tiled_supported(int unit_log2, int t, int iters_log2) {
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
+    if (launch == BMMC_LAUNCH_PERSISTENT &&
+        (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
+         (uint64_t(2) << (2 * t + unit_log2)) > 131072))
+        return false;
     return dispatch<0, 1, 0>(unit_log2, t, iters_log2, nullptr) == BMMC_OK;
 }
 
 int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
-    if (d.iters_log2 > d.blk_bits) return BMMC_ERR_INVALID_ARG;
+    if (d.iters_log2 > d.blk_bits || d.grid_log2 > d.blk_bits || d.grid_log2 < 0)
+        return BMMC_ERR_INVALID_ARG;
+    if (d.launch != BMMC_LAUNCH_PERSISTENT && d.launch != BMMC_LAUNCH_ONE_TILE)
+        return BMMC_ERR_INVALID_ARG;
+    if (d.launch == BMMC_LAUNCH_PERSISTENT && d.walk != BMMC_WALK_RANGES &&
+        d.walk != BMMC_WALK_INTERLEAVED)
+        return BMMC_ERR_INVALID_ARG;
     TiledArgs a{&d, static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), s};
     return dispatch<0, 1, 0>(d.unit_log2, d.t, d.iters_log2, &a);
 }

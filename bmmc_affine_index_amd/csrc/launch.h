@@ -16,8 +16,9 @@ int launch_chunk(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t
 // Identity-order copy of nbytes.
 int launch_copy(const void *in, void *out, size_t nbytes, hipStream_t s);
 
-// Whether the tile kernel is compiled for this unit size, side and iteration count.
-bool tiled_supported(int unit_log2, int t, int iters_log2);
+// Whether the tile kernel is compiled for this unit size, side, iteration
+// count and launch style.
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch);
 
 // Largest grid (in workgroups) of one launch; bigger passes are split.
 constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 30;

@@ -235,8 +235,16 @@ int default_tile_log2(int ulog2) {
 // high coordinates, independent).  The tile of block b is the coset
 // K.b XOR span(low t bits) XOR span(W); because W contains the high parts of
 // B's first t columns, the tile's image is 2^t whole output segments.
+struct LaunchChoice {
+    int iters_log2;  // one-tile launch: tiles staged together
+    int persistent;  // 1: persistent launch
+    int grid_log2;   // persistent: log2 workgroups requested
+    int walk;        // persistent: BMMC_WALK_RANGES or BMMC_WALK_INTERLEAVED
+};
+
 int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W,
-                int iters_log2, bool swizzle, bmmc_pass_desc *d) {
+                const LaunchChoice &lc, bool swizzle, bmmc_pass_desc *d) {
+    int iters_log2 = lc.iters_log2;
     const int nb = A.rows;
     if ((int)W.size() != t || 2 * t > nb) return BMMC_ERR_INVALID_ARG;
     const u64 lo_t = low_mask(t);
@@ -405,8 +413,19 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     d->t = t;
     d->chunk_log2 = g.wl;
     d->blk_bits = blk_bits;
-    d->iters_log2 = iters_log2;
-    d->lds_bytes = (uint32_t)((u64(1) << (2 * t + ulog2)) << iters_log2);
+    const u64 tile_bytes = u64(1) << (2 * t + ulog2);
+    if (lc.persistent && 2 * tile_bytes <= kMaxPersistentLdsBytes) {
+        // persistent: two LDS tiles (double buffer), no staged iterations
+        d->launch = BMMC_LAUNCH_PERSISTENT;
+        d->iters_log2 = 0;
+        d->grid_log2 = std::max(0, std::min(lc.grid_log2, blk_bits));
+        d->walk = lc.walk;
+        d->lds_bytes = (uint32_t)(2 * tile_bytes);
+    } else {
+        d->launch = BMMC_LAUNCH_ONE_TILE;
+        d->iters_log2 = iters_log2;
+        d->lds_bytes = (uint32_t)(tile_bytes << iters_log2);
+    }
     for (int k = 0; k < blk_bits; ++k) {
         u64 x = u64(1) << R[k];
         u64 z = A.apply(x);
@@ -467,8 +486,19 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     if (elem_bytes == 0 || elem_bytes > 16 || (elem_bytes & (elem_bytes - 1)))
         return BMMC_ERR_INVALID_ARG;
     if (o.route < BMMC_ROUTE_AUTO || o.route > BMMC_ROUTE_FUSED) return BMMC_ERR_INVALID_ARG;
-    if (o.tile_log2 < 0 || o.tile_log2 > BMMC_MAX_TILE || o.iters_log2 < 0 || o.iters_log2 > 4)
+    if (o.tile_log2 < 0 || o.tile_log2 > BMMC_MAX_TILE || o.iters_log2 < 0 || o.iters_log2 > 3)
         return BMMC_ERR_INVALID_ARG;
+    if (o.launch < BMMC_LAUNCH_AUTO || o.launch > BMMC_LAUNCH_PERSISTENT || o.grid_log2 < 0 ||
+        o.grid_log2 > 24)
+        return BMMC_ERR_INVALID_ARG;
+    if (o.launch == BMMC_LAUNCH_PERSISTENT && o.iters_log2 > 0) return BMMC_ERR_INVALID_ARG;
+    if (o.walk < BMMC_WALK_AUTO || o.walk > BMMC_WALK_INTERLEAVED) return BMMC_ERR_INVALID_ARG;
+    LaunchChoice lc;
+    lc.iters_log2 = o.iters_log2;
+    lc.persistent = o.launch == BMMC_LAUNCH_PERSISTENT ||
+                    (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0);
+    lc.grid_log2 = o.grid_log2 ? o.grid_log2 : kDefaultGridLog2;
+    lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);
@@ -544,7 +574,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         std::vector<u64> W;
         for (int r = t; r < m.nb; ++r)
             if ((H >> r) & 1u) W.push_back(u64(1) << r);
-        int st = build_tiled(m.A, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[0]);
+        int st = build_tiled(m.A, m.c, m.ulog2, t, W, lc, swz, &p->pass[0]);
         if (st != BMMC_OK) return st;
         info.tile_log2 = t;
         single(BMMC_ROUTE_FUSED);
@@ -564,7 +594,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         std::vector<u64> W;
         for (int r = t; r < m.nb; ++r)
             if ((H >> r) & 1u) W.push_back(u64(1) << r);
-        int st = build_tiled(T1, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[1]);
+        int st = build_tiled(T1, m.c, m.ulog2, t, W, lc, swz, &p->pass[1]);
         if (st != BMMC_OK) return st;
         p->npasses = 2;
         info.passes = 2;
@@ -583,7 +613,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     Basis wb = vb;
     for (int r = t; r < m.nb && (int)W.size() < t; ++r)
         if (wb.add(u64(1) << r)) W.push_back(u64(1) << r);
-    int st = build_tiled(m.A, m.c, m.ulog2, t, W, o.iters_log2, swz, &p->pass[0]);
+    int st = build_tiled(m.A, m.c, m.ulog2, t, W, lc, swz, &p->pass[0]);
     if (st != BMMC_OK) return st;
     info.tile_log2 = t;
     single(BMMC_ROUTE_FUSED);

@@ -36,5 +36,11 @@ int build_plan(int n, const uint64_t *A, uint64_t c, size_t elem_bytes,
 // size of 2^unit_log2 bytes, and the LDS byte budget of one workgroup.
 int max_tile_log2(int unit_log2);
 constexpr uint32_t kMaxLdsBytes = 65536;
+// The persistent launch double-buffers tiles of up to 64 KiB (gfx950 gives a
+// workgroup up to 160 KiB of LDS).
+constexpr uint32_t kMaxPersistentLdsBytes = 131072;
+// Persistent launch: 2^10 workgroups, four per compute unit on a 256-CU
+// MI355X.
+constexpr int kDefaultGridLog2 = 10;
 
 }  // namespace bmmc

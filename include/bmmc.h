@@ -72,8 +72,22 @@ typedef struct bmmc_plan_options {
     int route;      /* BMMC_ROUTE_* */
     int tile_log2;  /* tile side in units (log2); 0 = planner's choice */
     int no_swizzle; /* 1 = plain row-major LDS tile (bank-conflict ablation) */
-    int iters_log2; /* log2 of tiles per workgroup; 0 = one */
+    int iters_log2; /* one-tile launch: log2 of tiles staged together per workgroup */
+    int launch;     /* BMMC_LAUNCH_*: how the tile pass is launched */
+    int grid_log2;  /* persistent launch: log2 of workgroups; 0 = planner's choice */
+    int walk;       /* persistent launch: BMMC_WALK_* order of tiles; 0 = planner's choice */
 } bmmc_plan_options;
+
+/* Tile orders of the persistent launch. */
+#define BMMC_WALK_AUTO 0
+#define BMMC_WALK_RANGES 1      /* workgroup w walks the contiguous block range of w */
+#define BMMC_WALK_INTERLEAVED 2 /* at each step the workgroups take adjacent blocks */
+
+/* Launch styles of the tile pass. */
+#define BMMC_LAUNCH_AUTO 0       /* planner's choice */
+#define BMMC_LAUNCH_ONE_TILE 1   /* one workgroup per tile (or per 2^iters_log2 tiles) */
+#define BMMC_LAUNCH_PERSISTENT 2 /* 2^grid_log2 workgroups, each walking a range of tiles
+                                    with the next tile's loads overlapping this tile's stores */
 
 /* What a plan does, for tests and benchmarks. */
 typedef struct bmmc_plan_info {
@@ -96,8 +110,12 @@ typedef struct bmmc_plan_info {
  * affine, so the address of any element is the XOR of the contributions of
  * its block, row and lane bits).
  *
- * TILED: block b (bit k of the block index, the low iters_log2 bits iterated
- * inside one workgroup) starts at input offset XOR_k in_blk[k]; tile row h
+ * TILED: block b (bit k of the block index; with the one-tile launch the
+ * low iters_log2 bits are iterated inside one workgroup; with the persistent
+ * launch workgroup w walks, for k < 2^r with r = blk_bits - grid_log2 and
+ * gray(k) = k XOR (k >> 1), blocks w * 2^r XOR gray(k) (ranges) or
+ * gray(k) * 2^grid_log2 XOR w (interleaved)) starts at input offset
+ * XOR_k in_blk[k]; tile row h
  * (t bits) adds in_h; a row is 2^t contiguous units.  The tile is staged in
  * LDS at address XOR_k lds_wr_h[k] over the row bits XOR XOR_k lds_wr_lo[k]
  * over the bits of the unit's position in its row.  Output segment g (t bits) of the tile lies at XOR_k out_blk[k]
@@ -117,8 +135,12 @@ typedef struct bmmc_pass_desc {
     int32_t chunk_log2;  /* log2 units per vector chunk */
     int32_t blk_bits;    /* block-index bits (TILED), chunk-index bits (CHUNK),
                             unit-index bits (NAIVE) */
-    int32_t iters_log2;  /* tiles per workgroup, log2 (TILED) */
+    int32_t iters_log2;  /* one-tile launch: tiles staged together, log2 (TILED) */
     int32_t unit_xor;    /* in-chunk unit permutation (CHUNK) */
+    int32_t launch;      /* BMMC_LAUNCH_ONE_TILE or BMMC_LAUNCH_PERSISTENT (TILED) */
+    int32_t grid_log2;   /* persistent launch: 2^grid_log2 workgroups (TILED) */
+    int32_t walk;        /* persistent launch: BMMC_WALK_RANGES or _INTERLEAVED (TILED) */
+    int32_t reserved;
     uint64_t out_c;
     uint32_t lds_c;
     uint32_t lds_bytes;  /* LDS bytes per workgroup (TILED) */

@@ -39,6 +39,36 @@ class ReplayError(AssertionError):
     pass
 
 
+LAUNCH_ONE_TILE, LAUNCH_PERSISTENT = 1, 2
+
+
+def check_persistent_walk(d):
+    """Replays the persistent launch's walk: workgroup w starts at block
+    w << r and moves to the next block by XORing block bit ctz(k + 1) into its
+    running bases.  Every block must be visited exactly once, and the running
+    input base must equal the directly computed one at every step."""
+    r = d.blk_bits - d.grid_log2
+    if r < 0 or d.grid_log2 < 0:
+        raise ReplayError("grid larger than the number of tiles")
+    if d.walk not in (1, 2):
+        raise ReplayError("unknown walk")
+    shift = d.grid_log2 if d.walk == 2 else 0
+    seen = np.zeros(1 << d.blk_bits, dtype=np.int64)
+    for w in range(1 << d.grid_log2):
+        blk = w if d.walk == 2 else w << r
+        base = int(_xor_table(np.uint64(blk), d.in_blk, d.blk_bits))
+        for k in range(1 << r):
+            if base != int(_xor_table(np.uint64(blk), d.in_blk, d.blk_bits)):
+                raise ReplayError("running base diverged")
+            seen[blk] += 1
+            if k + 1 < (1 << r):
+                bit = shift + ((k + 1) & -(k + 1)).bit_length() - 1
+                blk ^= 1 << bit
+                base ^= int(d.in_blk[bit])
+    if np.any(seen != 1):
+        raise ReplayError("persistent walk does not visit every tile once")
+
+
 def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     """Source unit index of each output unit for one TILED pass."""
     ul, t, nb = d.unit_log2, d.t, d.nbits
@@ -49,7 +79,11 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     TILE = U << (2 * t)
     blk_bits = d.blk_bits
     nblk = 1 << blk_bits
-    if d.lds_bytes != TILE << d.iters_log2:
+    if d.launch == LAUNCH_PERSISTENT:
+        if d.lds_bytes != 2 * TILE or d.iters_log2 != 0:
+            raise ReplayError("persistent launch needs two LDS tiles")
+        check_persistent_walk(d)
+    elif d.lds_bytes != TILE << d.iters_log2:
         raise ReplayError("lds_bytes does not match the tile geometry")
     total_units = 1 << nb
 

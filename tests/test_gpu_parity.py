@@ -88,6 +88,13 @@ for it in (1, 2, 3):
     SMALL.append(("bitrev", 18, 4, dict(iters_log2=it)))
     SMALL.append(("bpc", 18, 16, dict(iters_log2=it)))
 SMALL.append(("general", 15, 4, dict(no_swizzle=1)))
+for e in (1, 4, 16):
+    for kind in ("general", "bpc"):
+        SMALL.append((kind, 16, e, dict(launch=bm.LAUNCH_ONE_TILE)))
+        for g in (1, 3, 6):
+            SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=g)))
+            SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=g,
+                                            walk=bm.WALK_INTERLEAVED)))
 SMALL.append(("bitrev", 12, 4, dict(tile_log2=6)))  # n = 2t: a single tile
 SMALL.append(("general", 12, 4, dict(tile_log2=6)))
 

@@ -34,11 +34,28 @@ def test_library_exports_every_header_function():
         assert hasattr(L, name), name
 
 
-def test_struct_sizes_match_header_layout():
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors have the C header's sizes and field offsets."""
     import ctypes
-    # 8 int32 + u64 + 2 u32 + 2*36 u64 + 36 u32 + 2*8 u64 + 2*8 u32 + 16 u32
-    expect = 8 * 4 + 8 + 2 * 4 + 2 * 36 * 8 + 36 * 4 + 2 * 8 * 8 + 2 * 8 * 4 + 16 * 4
-    assert ctypes.sizeof(bm.bmmc_pass_desc) == expect
+    import subprocess
+    structs = {"bmmc_pass_desc": bm.bmmc_pass_desc, "bmmc_plan_info": bm.bmmc_plan_info,
+               "bmmc_plan_options": bm.bmmc_plan_options}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "bmmc.h"',
+             "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (name, name))
+        for field, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (name, field, name, field))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    out = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
+    for name, cls in structs.items():
+        assert int(out[name]) == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert int(out[name + "." + field]) == getattr(cls, field).offset, (name, field)
 
 
 # --------------------------------------------------------------------------
@@ -245,6 +262,11 @@ def _cases():
     for it in (1, 2, 3):
         cases.append(("general", 16, 4, dict(iters_log2=it)))
         cases.append(("bitrev", 16, 4, dict(iters_log2=it)))
+    for e in (1, 4, 16):
+        cases.append(("general", 15, e, dict(launch=bm.LAUNCH_ONE_TILE)))
+        cases.append(("general", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2)))
+        cases.append(("bpc", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2,
+                                         walk=bm.WALK_INTERLEAVED)))
     cases.append(("general", 14, 4, dict(no_swizzle=1)))
     cases.append(("general", 5, 4, dict()))
     cases.append(("general", 2, 4, dict()))
