@@ -150,6 +150,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--kind", default=None, choices=["bitrev", "transpose", "bpc", "bmmc"],
+                    help="custom workload instead of --workload: the matrix kind")
+    ap.add_argument("--n", type=int, default=24, help="custom workload: index bits")
+    ap.add_argument("--elem", type=int, default=4, help="custom workload: element bytes")
+    ap.add_argument("--seed", type=int, default=1, help="custom workload: matrix seed")
     ap.add_argument("--perm", type=int, default=0, help="c5: permutation index 0..31")
     ap.add_argument("--route", default="auto", choices=["auto", "naive", "two_pass", "fused"])
     ap.add_argument("--tile-log2", type=int, default=0)
@@ -177,10 +182,24 @@ def main():
     bm.lib()  # fails loudly when the HIP library is missing
 
     name = args.workload
-    w = wl.WORKLOADS[name]
-    n, elem = w.n, w.elem_bytes
-    A, c = wl.workload_matrix(name, accept=lib_accepts(n), perm_index=args.perm)
-    x = wl.workload_data(name)
+    if args.kind:
+        n, elem = args.n, args.elem
+        if args.kind == "bitrev":
+            A, c = wl.bit_reverse_matrix(n), 0
+        elif args.kind == "transpose":
+            A, c = wl.transpose_matrix(n // 2, n - n // 2), 0
+        elif args.kind == "bpc":
+            A, c = wl.random_bpc(n, args.seed)
+        else:
+            A, c = wl.random_bmmc(n, args.seed, lib_accepts(n))
+        x = wl.fill_random_bytes(n, elem, args.seed)
+        workload_name = "%s_n%d_%dB" % (args.kind, n, elem)
+    else:
+        w = wl.WORKLOADS[name]
+        n, elem = w.n, w.elem_bytes
+        A, c = wl.workload_matrix(name, accept=lib_accepts(n), perm_index=args.perm)
+        x = wl.workload_data(name)
+        workload_name = WORKLOAD_NAMES[name] + ("_perm%d" % args.perm if name == "c5" else "")
     nbytes = elem << n
     route = {"auto": bm.ROUTE_AUTO, "naive": bm.ROUTE_NAIVE, "two_pass": bm.ROUTE_TWO_PASS,
              "fused": bm.ROUTE_FUSED}[args.route]
@@ -193,7 +212,7 @@ def main():
                    grid_log2=args.grid_log2,
                    walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk])
     plan_us = (time.perf_counter() - t0) * 1e6
-    if name == "c4" and route == bm.ROUTE_TWO_PASS:
+    if name == "c4" and not args.kind and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2
 
     pairs = 1 if args.warm else max(1, -(-(1 << 30) // (2 * nbytes)))
@@ -243,7 +262,7 @@ def main():
         if parity.startswith("MISMATCH"):
             print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
 
-    traffic = read_traffic(name)
+    traffic = None if args.kind else read_traffic(name)
     passes = plan.info.passes
     roofline = {
         "bound": "hbm",
@@ -270,7 +289,7 @@ def main():
         "dtype": {1: "u8", 2: "u16", 4: "u32", 8: "u64", 16: "u128"}[plan.info.unit_bytes],
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[name] + ("_perm%d" % args.perm if name == "c5" else ""),
+            "workload": workload_name,
             "n": n, "elem_bytes": elem, "bytes_per_step": int(algo_bytes),
             "residency": ("one buffer pair, repeated (cache-warm)" if args.warm else
                           "%d rotating buffer pairs, %.2f GiB working set (HBM)"

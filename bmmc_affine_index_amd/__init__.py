@@ -38,6 +38,7 @@ WALK_AUTO, WALK_RANGES, WALK_INTERLEAVED = 0, 1, 2
 MAX_N = 32
 MAX_BITS = 36
 MAX_TILE = 8
+MAX_CHUNK_BITS = 16
 MAX_PASSES = 2
 
 EXPORTED = (
@@ -73,10 +74,11 @@ class bmmc_pass_desc(ctypes.Structure):
                 ("lds_bytes", ctypes.c_uint32),
                 ("in_blk", ctypes.c_uint64 * MAX_BITS), ("out_blk", ctypes.c_uint64 * MAX_BITS),
                 ("lds_blk", ctypes.c_uint32 * MAX_BITS),
-                ("in_h", ctypes.c_uint64 * MAX_TILE), ("out_g", ctypes.c_uint64 * MAX_TILE),
-                ("lds_wr_h", ctypes.c_uint32 * MAX_TILE),
-                ("lds_wr_lo", ctypes.c_uint32 * MAX_TILE),
-                ("lds_rd", ctypes.c_uint32 * (2 * MAX_TILE))]
+                ("ld_in", ctypes.c_uint64 * MAX_CHUNK_BITS),
+                ("ld_lds", ctypes.c_uint32 * MAX_CHUNK_BITS),
+                ("st_out", ctypes.c_uint64 * MAX_CHUNK_BITS),
+                ("st_lds", ctypes.c_uint32 * MAX_CHUNK_BITS),
+                ("st_unit", ctypes.c_uint32 * 4)]
 
 
 class BmmcError(RuntimeError):

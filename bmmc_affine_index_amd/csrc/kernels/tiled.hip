@@ -33,14 +33,15 @@ template <int UL, int T, int IT> struct TiledCfg {
     static constexpr int NTL = CHL < 8 ? CHL : 8;           // log2 threads
     static constexpr int NT = 1 << NTL;
     static constexpr int RPPL = NTL - CPSL;                 // log2 rows per pass
-    static constexpr int JL = T - RPPL;                     // log2 passes per tile
+    static constexpr int JL = CHL - NTL;                    // log2 passes per tile
     static constexpr int J = 1 << JL;
     static constexpr int TILE = U << (2 * T);               // bytes per tile
     static constexpr int LDS = TILE << IT;
     static_assert(RPPL >= 0 && JL >= 0, "tile geometry");
 };
 
-// Per-lane address parts, fixed for the whole launch.
+// Per-lane address parts, fixed for the whole launch: the XOR of the table
+// entries of the thread-index bits of a chunk (chunk c = (j << NTL) | tid).
 struct LaneParts {
     uint64_t in_lane, out_lane;
     uint32_t wr_lane, rd_lane;
@@ -48,26 +49,22 @@ struct LaneParts {
 
 template <class C, int T>
 __device__ __forceinline__ LaneParts lane_parts(const bmmc_pass_desc &d, uint32_t tid) {
-    const uint32_t q = tid & ((1u << C::CPSL) - 1);  // chunk within a row / segment
-    const uint32_t hl = tid >> C::CPSL;              // low row (segment) bits
     LaneParts p;
-    p.in_lane = dev::xor_bits_lane<C::RPPL>(d.in_h, hl) ^ (uint64_t)(q * C::CB);
-    p.wr_lane = dev::xor_bits_lane<C::RPPL>(d.lds_wr_h, hl) ^
-                dev::xor_bits_lane<C::CPSL>(d.lds_wr_lo + C::WL, q);
-    p.out_lane = dev::xor_bits_lane<C::RPPL>(d.out_g, hl) ^ (uint64_t)(q * C::CB);
-    p.rd_lane = dev::xor_bits_lane<C::CPSL>(d.lds_rd + C::WL, q) ^
-                dev::xor_bits_lane<C::RPPL>(d.lds_rd + T, hl);
+    p.in_lane = dev::xor_bits_lane<C::NTL>(d.ld_in, tid);
+    p.wr_lane = dev::xor_bits_lane<C::NTL>(d.ld_lds, tid);
+    p.out_lane = dev::xor_bits_lane<C::NTL>(d.st_out, tid);
+    p.rd_lane = dev::xor_bits_lane<C::NTL>(d.st_lds, tid);
     return p;
 }
 
-// Issue the global loads of one tile (rows j * 2^RPPL + lane row bits).
+// Issue the global loads of one tile: pass j covers chunks (j << NTL) | tid.
 template <class C, int T>
 __device__ __forceinline__ void load_tile(dev::Chunk<C::CB> (&v)[C::J], const uint8_t *in,
                                           uint64_t in_base, const bmmc_pass_desc &d,
                                           const LaneParts &p) {
 #pragma unroll
     for (int j = 0; j < C::J; ++j) {
-        const uint64_t in_j = in_base ^ dev::xor_bits_lane<C::JL>(d.in_h + C::RPPL, (uint32_t)j);
+        const uint64_t in_j = in_base ^ dev::xor_bits_lane<C::JL>(d.ld_in + C::NTL, (uint32_t)j);
         v[j] = dev::gload<C::CB>(in + (in_j ^ p.in_lane));
     }
 }
@@ -78,26 +75,27 @@ __device__ __forceinline__ void stage_tile(uint8_t *tile_lds, const dev::Chunk<C
                                            const bmmc_pass_desc &d, const LaneParts &p) {
 #pragma unroll
     for (int j = 0; j < C::J; ++j) {
-        const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.lds_wr_h + C::RPPL, (uint32_t)j);
+        const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.ld_lds + C::NTL, (uint32_t)j);
         dev::lds_store<C::CB>(tile_lds + (wr_j ^ p.wr_lane), v[j]);
     }
 }
 
-// Read the tile back in output order and store whole output segments.
+// Read the tile back in output order and store whole output chunks.
 template <class C, int T>
 __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds, uint64_t obase,
                                            uint32_t rbase, const bmmc_pass_desc &d,
                                            const LaneParts &p) {
 #pragma unroll
     for (int j = 0; j < C::J; ++j) {
-        const uint64_t out_j = obase ^ dev::xor_bits_lane<C::JL>(d.out_g + C::RPPL, (uint32_t)j);
+        const uint64_t out_j =
+            obase ^ dev::xor_bits_lane<C::JL>(d.st_out + C::NTL, (uint32_t)j);
         const uint32_t rd_j =
-            rbase ^ dev::xor_bits_lane<C::JL>(d.lds_rd + T + C::RPPL, (uint32_t)j) ^ p.rd_lane;
+            rbase ^ dev::xor_bits_lane<C::JL>(d.st_lds + C::NTL, (uint32_t)j) ^ p.rd_lane;
         dev::Chunk<C::CB> ch;
         dev::zero(ch);
 #pragma unroll
         for (int e = 0; e < C::W; ++e) {
-            const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.lds_rd, (uint32_t)e);
+            const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.st_unit, (uint32_t)e);
             dev::put_unit<C::CB, C::U>(ch, e, dev::lds_load_unit<C::U>(tile_lds + (rd_j ^ rd_e)));
         }
         dev::gstore<C::CB>(out + (out_j ^ p.out_lane), ch);

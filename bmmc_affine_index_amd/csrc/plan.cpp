@@ -226,8 +226,11 @@ int max_tile_log2(int ulog2) {
 
 namespace {
 
+// Tile side per unit size: rows of at least 256 bytes, and tiles of at least
+// 16 KiB so that the persistent launch keeps enough bytes in flight (8-byte
+// units with 8 KiB tiles measured 0.72 of copy, with 32 KiB tiles 0.89).
 int default_tile_log2(int ulog2) {
-    static const int t[5] = {8, 7, 6, 5, 5};
+    static const int t[5] = {8, 7, 6, 6, 5};
     return t[ulog2];
 }
 
@@ -283,18 +286,26 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     if (!inverse(M, Minv)) return BMMC_ERR_INVALID_ARG;
 
     const TileGeom g = tile_geom(ulog2, t);
-    const int lanes = std::min(64, 1 << g.ntl);
-    const int cps = 1 << g.cpsl;
+    const int cbits = 2 * t - g.wl;  // chunk-index bits of a tile: thread bits, then pass bits
+    const int lane_bits = std::min(6, g.ntl);
+    const int lanes = 1 << lane_bits;
 
-    // Two free choices make the output-order LDS reads conflict-free:
-    //  * the order of the tile's output segments: the lanes of a read take
-    //    the first rppl coordinates of g, so the planner picks which
-    //    coordinates of G those are (`gperm`);
-    //  * the LDS layout: the slot of local (lo, h) is
-    //    (h << t) | (P.lo XOR S.h), with P an invertible map of the chunk
-    //    index inside a row and S (t x t) an XOR swizzle by row; both keep
-    //    the units of a chunk together, so the write of a chunk stays one
-    //    vector access.  Sx holds S's t columns followed by P's t columns.
+    // Chunk coordinates.  Load phase: position p < cpsl is bit p of the
+    // chunk's place in its input row, then the row bits; the threads of a
+    // wave read whole rows.  Drain phase: coordinate k < cpsl is bit k of the
+    // chunk's place in its output segment, then the segment bits; which
+    // coordinate each thread bit takes (`rpos`) is chosen below.
+    auto load_local = [&](int p) -> u64 {  // local input vector of load position p
+        return p < g.cpsl ? (u64(1) << (g.wl + p)) : (u64(1) << (t + p - g.cpsl));
+    };
+    auto drain_local = [&](int k) -> u64 {  // local output vector of drain coordinate k
+        return k < g.cpsl ? (u64(1) << (g.wl + k)) : (u64(1) << (t + k - g.cpsl));
+    };
+
+    // LDS layout: the slot of local (lo, h) is (h << t) | (P.lo XOR S.h),
+    // with P an invertible map of the chunk index inside a row and S an XOR
+    // swizzle by row; both leave the units of a chunk together, so a chunk
+    // is written with one vector access.  Sx = S's t columns, then P's.
     auto slot = [&](u64 u, const std::vector<u64> &Sx) -> u64 {
         u64 lo = u & lo_t, h = u >> t, s = 0;
         for (int k = 0; k < t; ++k) {
@@ -303,58 +314,59 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         }
         return (h << t) | s;
     };
-    // read columns: input-local vector of each output-local coordinate
-    auto read_cols = [&](const std::vector<int> &gperm) {
-        std::vector<u64> rc(2 * t);
-        for (int k = 0; k < t; ++k) rc[k] = Minv.col(k);
-        for (int k = 0; k < t; ++k) rc[t + k] = Minv.col(t + gperm[k]);
-        return rc;
+
+    // Bank model.  Measured on gfx950 with the LDS bank-conflict counter:
+    // 4-byte reads behave as 32 banks serving a half-wave per cycle; 16-byte
+    // accesses are conflict-free when each group of 8 lanes covers 8 distinct
+    // 16-byte bank groups.  The cost weights that model first and a 64-bank
+    // full-wave model second.
+    const int rbytes = 1 << ulog2, wbytes = 1 << (ulog2 + g.wl);
+    auto ideal_cycles = [&](int bytes, int banks) {
+        const int per = std::min(64, bytes >= 4 ? (4 * banks) / bytes : banks);
+        return (lanes + per - 1) / per;
     };
-    auto cost = [&](const std::vector<u64> &rc, const std::vector<u64> &Sx) {
+    const int ideal = 8 * ideal_cycles(rbytes, 32) + 2 * ideal_cycles(rbytes, 64) +
+                      ideal_cycles(wbytes, 32) + ideal_cycles(wbytes, 64);
+    auto cost = [&](const std::vector<u64> &rv, const std::vector<u64> &Sx) {
         uint32_t wa[64], ra[64];
-        for (int l = 0; l < lanes; ++l) {
-            u64 q = (u64)(l & (cps - 1)), hl = (u64)(l >> g.cpsl);
-            // write phase: chunk q of row hl
-            wa[l] = (uint32_t)(slot((hl << t) | (q << g.wl), Sx) << ulog2);
-            // read phase: unit q*w of output segment hl
-            u64 src = 0;
-            for (int b = 0; b < g.cpsl; ++b)
-                if ((q >> b) & 1u) src ^= rc[g.wl + b];
-            for (int b = 0; b < g.rppl; ++b)
-                if ((hl >> b) & 1u) src ^= rc[t + b];
-            ra[l] = (uint32_t)(slot(src, Sx) << ulog2);
+        uint32_t wcol[6], rcol[6];
+        for (int p = 0; p < lane_bits; ++p) {
+            wcol[p] = (uint32_t)(slot(load_local(p), Sx) << ulog2);
+            rcol[p] = (uint32_t)(slot(rv[p], Sx) << ulog2);
         }
-        int cw = bank_cycles(wa, lanes, 1 << (ulog2 + g.wl), 32) +
-                 bank_cycles(wa, lanes, 1 << (ulog2 + g.wl), 64);
-        int cr = 2 * bank_cycles(ra, lanes, 1 << ulog2, 32) +
-                 4 * bank_cycles(ra, lanes, 1 << ulog2, 64);
-        return cr + cw;
+        for (int l = 0; l < lanes; ++l) {
+            uint32_t a = 0, b = 0;
+            for (int p = 0; p < lane_bits; ++p)
+                if ((l >> p) & 1) { a ^= wcol[p]; b ^= rcol[p]; }
+            wa[l] = a;
+            ra[l] = b;
+        }
+        return 8 * bank_cycles(ra, lanes, rbytes, 32) + 2 * bank_cycles(ra, lanes, rbytes, 64) +
+               bank_cycles(wa, lanes, wbytes, 32) + bank_cycles(wa, lanes, wbytes, 64);
     };
-    std::vector<int> gperm(t);
-    for (int k = 0; k < t; ++k) gperm[k] = k;
+
+    // Drain-phase lane layout: the first `pc` thread bits stay on the low
+    // chunk bits of the output segment so that 8 lanes store one contiguous
+    // 128-byte piece; the remaining lane bits of the wave are searched.
+    int cb_log2 = ulog2 + g.wl;
+    const int pc = std::min(g.cpsl, std::max(0, 7 - cb_log2));
+    std::vector<int> rpos(cbits);
+    for (int k = 0; k < cbits; ++k) rpos[k] = k;
     std::vector<u64> S(2 * t, 0);
-    for (int k = 0; k < t; ++k) S[t + k] = u64(1) << k;  // P = identity
+    for (int k = 0; k < t; ++k) S[t + k] = u64(1) << k;  // P = identity, S = 0
+    auto read_vecs = [&](const std::vector<int> &rp) {
+        std::vector<u64> rv(cbits);
+        for (int p = 0; p < cbits; ++p) rv[p] = Minv.apply(drain_local(rp[p]));
+        return rv;
+    };
     if (swizzle && t > g.wl) {
         const u64 colmask = lo_t & ~low_mask(g.wl);
-        // lower bound: one cycle per lane group on each model
-        int ideal = 0;
-        {
-            const int rbytes = 1 << ulog2, wbytes = 1 << (ulog2 + g.wl);
-            for (int banks : {32, 64}) {
-                int rb = rbytes >= 4 ? rbytes : 4, wb = wbytes >= 4 ? wbytes : 4;
-                ideal += (banks == 32 ? 2 : 4) *
-                         std::max(1, (lanes * rb + 4 * banks - 1) / (4 * banks));
-                ideal += std::max(1, (lanes * wb + 4 * banks - 1) / (4 * banks));
-            }
-        }
         u64 seed = 0x5EEDull ^ ((u64)t << 8) ^ (u64)ulog2;
         for (int k = 0; k < 2 * t; ++k) seed = seed * 31 + Minv.r[k];
         int best_cost = 1 << 30;
-        std::vector<int> best_perm = gperm;
+        std::vector<int> best_rpos = rpos;
         std::vector<u64> best_S = S, cand(2 * t);
         auto random_p = [&](std::vector<u64> &Sx) {
-            // random invertible map of the chunk-index bits (wl..t-1); the
-            // unit bits inside a chunk stay fixed
             for (;;) {
                 Mat Pm = Mat::zeros(t, t);
                 for (int k = 0; k < t; ++k)
@@ -365,46 +377,64 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
                 }
             }
         };
-        // candidate lane coordinates of g: every rppl-subset, taken first
-        const int rl = std::min(g.rppl, t);
-        std::vector<int> pick(rl);
-        for (int k = 0; k < rl; ++k) pick[k] = k;
-        int budget = 1200;  // cost evaluations
-        for (bool more = true; more && best_cost > ideal && budget > 0;) {
-            std::vector<int> perm(pick.begin(), pick.end());
-            for (int k = 0; k < t; ++k)
-                if (std::find(pick.begin(), pick.end(), k) == pick.end()) perm.push_back(k);
-            const std::vector<u64> rc = read_cols(perm);
-            auto consider = [&](const std::vector<u64> &Sx) {
-                --budget;
-                int cc = cost(rc, Sx);
-                if (cc < best_cost) { best_cost = cc; best_perm = perm; best_S = Sx; }
-            };
-            for (int k = 0; k < t; ++k) { cand[k] = 0; cand[t + k] = u64(1) << k; }
-            consider(cand);
-            // the diagonal skew: row h shifts by h (restricted to chunk bits)
-            for (int k = 0; k < t; ++k) cand[k] = (u64(1) << k) & colmask;
-            consider(cand);
-            for (int tries = 0; tries < 96 && best_cost > ideal && budget > 0; ++tries) {
-                for (int k = 0; k < t; ++k) cand[k] = splitmix(seed) & colmask;
-                if (tries & 1) random_p(cand);
-                else for (int k = 0; k < t; ++k) cand[t + k] = u64(1) << k;
-                consider(cand);
+        // Bits of a source position that no swizzle can move: the unit bits
+        // inside a chunk that select different dwords.  The lanes of one
+        // conflict group must span them.
+        const u64 fixed = low_mask(g.wl) & ~low_mask(std::max(0, 2 - ulog2));
+        const int grp_per = std::min(64, rbytes >= 4 ? 128 / rbytes : 32);
+        const int grp_bits = std::min(lane_bits, __builtin_ctz((unsigned)grp_per));
+        // ordered choices for the free lane positions pc .. lane_bits-1
+        const int nfree = std::max(0, lane_bits - pc);
+        std::vector<int> pool;
+        for (int k = pc; k < cbits; ++k) pool.push_back(k);
+        std::vector<int> sel(nfree, 0);
+        int budget = 4000;
+        bool more = true;
+        while (more && best_cost > ideal && budget > 0) {
+            // build rpos from sel (indices into pool, all distinct)
+            bool distinct = true;
+            for (int a = 0; a < nfree && distinct; ++a)
+                for (int b = a + 1; b < nfree; ++b)
+                    if (sel[a] == sel[b]) { distinct = false; break; }
+            if (distinct && (int)pool.size() >= nfree) {
+                std::vector<int> rp;
+                for (int k = 0; k < pc; ++k) rp.push_back(k);
+                for (int a = 0; a < nfree; ++a) rp.push_back(pool[sel[a]]);
+                for (int k : pool)
+                    if (std::find(rp.begin(), rp.end(), k) == rp.end()) rp.push_back(k);
+                const std::vector<u64> rv = read_vecs(rp);
+                // pre-filter: the conflict group's lanes must span the fixed bits
+                Basis fb;
+                for (int p = 0; p < grp_bits; ++p) fb.add(rv[p] & fixed);
+                if (fb.size() == __builtin_popcountll(fixed)) {
+                    auto consider = [&](const std::vector<u64> &Sx) {
+                        --budget;
+                        int cc = cost(rv, Sx);
+                        if (cc < best_cost) { best_cost = cc; best_rpos = rp; best_S = Sx; }
+                    };
+                    for (int k = 0; k < t; ++k) { cand[k] = 0; cand[t + k] = u64(1) << k; }
+                    consider(cand);
+                    for (int k = 0; k < t; ++k) cand[k] = (u64(1) << k) & colmask;
+                    consider(cand);
+                    for (int tries = 0; tries < 48 && best_cost > ideal && budget > 0; ++tries) {
+                        for (int k = 0; k < t; ++k) cand[k] = splitmix(seed) & colmask;
+                        if (tries & 1) random_p(cand);
+                        else for (int k = 0; k < t; ++k) cand[t + k] = u64(1) << k;
+                        consider(cand);
+                    }
+                }
             }
-            // next rl-subset of {0..t-1} in lexicographic order
-            int i = rl - 1;
-            while (i >= 0 && pick[i] == t - rl + i) --i;
-            if (i < 0) {
-                more = false;
-            } else {
-                ++pick[i];
-                for (int k = i + 1; k < rl; ++k) pick[k] = pick[k - 1] + 1;
-            }
+            // next tuple (odometer over pool indices)
+            int a = nfree - 1;
+            while (a >= 0 && ++sel[a] == (int)pool.size()) sel[a--] = 0;
+            if (a < 0) more = false;
         }
-        gperm = best_perm;
-        S = best_S;
+        if (best_cost < (1 << 30)) {
+            rpos = best_rpos;
+            S = best_S;
+        }
     }
-    const std::vector<u64> rcols = read_cols(gperm);
+    const std::vector<u64> rvec = read_vecs(rpos);
 
     std::memset(d, 0, sizeof(*d));
     d->kernel = BMMC_KERNEL_TILED;
@@ -418,7 +448,12 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         // persistent: two LDS tiles (double buffer), no staged iterations
         d->launch = BMMC_LAUNCH_PERSISTENT;
         d->iters_log2 = 0;
-        d->grid_log2 = std::max(0, std::min(lc.grid_log2, blk_bits));
+        // One workgroup per compute unit (2^8 on a 256-CU MI355X) walking
+        // long tile ranges measured best for large arrays; below 2^14 tiles
+        // two per compute unit shorten each walk.
+        const int want = lc.grid_log2 ? lc.grid_log2
+                                      : (blk_bits >= 14 ? kDefaultGridLog2 : kDefaultGridLog2 + 1);
+        d->grid_log2 = std::max(0, std::min(want, blk_bits));
         d->walk = lc.walk;
         d->lds_bytes = (uint32_t)(2 * tile_bytes);
     } else {
@@ -433,13 +468,25 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         d->out_blk[k] = (z & ~lo_t) << ulog2;
         d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_t), S) << ulog2);
     }
-    for (int k = 0; k < t; ++k) {
-        d->in_h[k] = W[k] << ulog2;
-        d->out_g[k] = gb.vec[gperm[k]] << ulog2;
-        d->lds_wr_h[k] = (uint32_t)(slot(u64(1) << (t + k), S) << ulog2);
-        d->lds_wr_lo[k] = (uint32_t)(slot(u64(1) << k, S) << ulog2);
+    for (int p = 0; p < cbits; ++p) {
+        const u64 lv = load_local(p);
+        const u64 in_local = (lv & lo_t) | [&] {
+            u64 h = lv >> t, off = 0;
+            for (int k = 0; k < t; ++k)
+                if ((h >> k) & 1u) off ^= W[k];
+            return off;
+        }();
+        d->ld_in[p] = in_local << ulog2;
+        d->ld_lds[p] = (uint32_t)(slot(lv, S) << ulog2);
+        const u64 ov = drain_local(rpos[p]);
+        u64 out_local = ov & lo_t;
+        for (int k = 0; k < t; ++k)
+            if (((ov >> t) >> k) & 1u) out_local ^= gb.vec[k];
+        d->st_out[p] = out_local << ulog2;
+        d->st_lds[p] = (uint32_t)(slot(rvec[p], S) << ulog2);
     }
-    for (int k = 0; k < 2 * t; ++k) d->lds_rd[k] = (uint32_t)(slot(rcols[k], S) << ulog2);
+    for (int b = 0; b < g.wl; ++b)
+        d->st_unit[b] = (uint32_t)(slot(Minv.apply(u64(1) << b), S) << ulog2);
     d->out_c = (c & ~lo_t) << ulog2;
     d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
     return BMMC_OK;
@@ -497,7 +544,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     lc.iters_log2 = o.iters_log2;
     lc.persistent = o.launch == BMMC_LAUNCH_PERSISTENT ||
                     (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0);
-    lc.grid_log2 = o.grid_log2 ? o.grid_log2 : kDefaultGridLog2;
+    lc.grid_log2 = o.grid_log2;  // 0: chosen per pass from the tile count
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;

@@ -39,8 +39,8 @@ constexpr uint32_t kMaxLdsBytes = 65536;
 // The persistent launch double-buffers tiles of up to 64 KiB (gfx950 gives a
 // workgroup up to 160 KiB of LDS).
 constexpr uint32_t kMaxPersistentLdsBytes = 131072;
-// Persistent launch: 2^10 workgroups, four per compute unit on a 256-CU
-// MI355X.
-constexpr int kDefaultGridLog2 = 10;
+// Persistent launch: 2^8 workgroups, one per compute unit on a 256-CU
+// MI355X (measured against 2^9 .. 2^11 on the benchmark workloads).
+constexpr int kDefaultGridLog2 = 8;
 
 }  // namespace bmmc

@@ -108,32 +108,34 @@ typedef struct bmmc_plan_info {
  * is XORed in when the corresponding index bit is 1, which is how the kernels
  * evaluate A.x XOR c without a per-element matrix-vector product (the map is
  * affine, so the address of any element is the XOR of the contributions of
- * its block, row and lane bits).
+ * its block, chunk and unit bits).
  *
- * TILED: block b (bit k of the block index; with the one-tile launch the
- * low iters_log2 bits are iterated inside one workgroup; with the persistent
- * launch workgroup w walks, for k < 2^r with r = blk_bits - grid_log2 and
- * gray(k) = k XOR (k >> 1), blocks w * 2^r XOR gray(k) (ranges) or
- * gray(k) * 2^grid_log2 XOR w (interleaved)) starts at input offset
- * XOR_k in_blk[k]; tile row h
- * (t bits) adds in_h; a row is 2^t contiguous units.  The tile is staged in
- * LDS at address XOR_k lds_wr_h[k] over the row bits XOR XOR_k lds_wr_lo[k]
- * over the bits of the unit's position in its row.  Output segment g (t bits) of the tile lies at XOR_k out_blk[k]
- * XOR out_c XOR out_g(g); its unit at position y (t bits) is read from LDS
- * address lds_rd(y, g) XOR lds_blk(b) XOR lds_c, with lds_rd indexed by y's
- * bits (0..t-1) then g's bits (t..2t-1).
+ * TILED: the array is cut into 2^blk_bits tiles of 2^(2t) units; tile b
+ * starts at input offset XOR_k in_blk[k] over the set bits k of b.  With the
+ * one-tile launch a workgroup moves tiles b = (w << iters_log2) | s; with
+ * the persistent launch workgroup w walks, for k < 2^r with
+ * r = blk_bits - grid_log2 and gray(k) = k XOR (k >> 1), the tiles
+ * w * 2^r XOR gray(k) (ranges) or gray(k) * 2^grid_log2 XOR w (interleaved).
+ * A tile is moved in chunks of 2^chunk_log2 units: chunk c = (j << T) | tid
+ * (T = log2 threads per workgroup, j the pass) is loaded from input offset
+ * tile base XOR_p ld_in[p] and written to LDS address XOR_p ld_lds[p] over
+ * the set bits p of c; in the drain phase chunk c is stored at output offset
+ * XOR_k out_blk[k] XOR out_c XOR_p st_out[p], its unit e read from LDS
+ * address XOR_k lds_blk[k] XOR lds_c XOR_p st_lds[p] XOR_b st_unit[b] over
+ * the set bits b of e.
  * CHUNK: chunk index bit k moves the output by out_blk[k]; out_c is the
  * constant; unit_xor permutes the units inside a chunk (unit e goes to
  * e XOR unit_xor).  The input chunk is read at chunk_index * chunk_bytes.
  * NAIVE: unit index bit k moves the output by out_blk[k]; out_c constant.
  * COPY: nothing but nbits/unit_log2. */
+#define BMMC_MAX_CHUNK_BITS 16
 typedef struct bmmc_pass_desc {
     int32_t kernel;      /* BMMC_KERNEL_* */
     int32_t unit_log2;   /* log2 bytes of one unit */
     int32_t nbits;       /* index bits at unit granularity */
     int32_t t;           /* tile side / segment length, log2 units (TILED) */
     int32_t chunk_log2;  /* log2 units per vector chunk */
-    int32_t blk_bits;    /* block-index bits (TILED), chunk-index bits (CHUNK),
+    int32_t blk_bits;    /* tile-index bits (TILED), chunk-index bits (CHUNK),
                             unit-index bits (NAIVE) */
     int32_t iters_log2;  /* one-tile launch: tiles staged together, log2 (TILED) */
     int32_t unit_xor;    /* in-chunk unit permutation (CHUNK) */
@@ -147,11 +149,11 @@ typedef struct bmmc_pass_desc {
     uint64_t in_blk[BMMC_MAX_BITS];
     uint64_t out_blk[BMMC_MAX_BITS];
     uint32_t lds_blk[BMMC_MAX_BITS];
-    uint64_t in_h[BMMC_MAX_TILE];
-    uint64_t out_g[BMMC_MAX_TILE];
-    uint32_t lds_wr_h[BMMC_MAX_TILE];
-    uint32_t lds_wr_lo[BMMC_MAX_TILE];
-    uint32_t lds_rd[2 * BMMC_MAX_TILE];
+    uint64_t ld_in[BMMC_MAX_CHUNK_BITS];
+    uint32_t ld_lds[BMMC_MAX_CHUNK_BITS];
+    uint64_t st_out[BMMC_MAX_CHUNK_BITS];
+    uint32_t st_lds[BMMC_MAX_CHUNK_BITS];
+    uint32_t st_unit[4];
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; immutable after creation */

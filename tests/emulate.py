@@ -74,8 +74,9 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     ul, t, nb = d.unit_log2, d.t, d.nbits
     U = 1 << ul
     g = tiled_geometry(ul, t)
-    wl, cpsl, ntl, rppl, jl = g["wl"], g["cpsl"], g["ntl"], g["rppl"], g["jl"]
+    wl, cpsl, ntl, jl = g["wl"], g["cpsl"], g["ntl"], g["jl"]
     W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
+    cbits = ntl + jl
     TILE = U << (2 * t)
     blk_bits = d.blk_bits
     nblk = 1 << blk_bits
@@ -87,17 +88,11 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
         raise ReplayError("lds_bytes does not match the tile geometry")
     total_units = 1 << nb
 
-    b = np.arange(nblk, dtype=np.uint64)[:, None, None]
-    tid = np.arange(NT, dtype=np.uint64)[None, :, None]
-    j = np.arange(J, dtype=np.uint64)[None, None, :]
-    q = tid & np.uint64((1 << cpsl) - 1)
-    hl = tid >> np.uint64(cpsl)
-    h = (j << np.uint64(rppl)) | hl  # tile row (input segment) index
+    b = np.arange(nblk, dtype=np.uint64)[:, None]
+    cidx = np.arange(NT * J, dtype=np.uint64)[None, :]  # chunk index (j << ntl) | tid
 
-    in_off = (_xor_table(b, d.in_blk, blk_bits) ^ _xor_table(h, d.in_h, t)
-              ^ (q * np.uint64(CB)))
-    wr = _xor_table(h, d.lds_wr_h, t) ^ _xor_table(q, [d.lds_wr_lo[wl + k] for k in range(cpsl)],
-                                                   cpsl)
+    in_off = _xor_table(b, d.in_blk, blk_bits) ^ _xor_table(cidx, d.ld_in, cbits)
+    wr = _xor_table(cidx, d.ld_lds, cbits)
     in_off, wr = np.broadcast_arrays(in_off, wr)
     if np.any(in_off % np.uint64(CB)) or np.any(wr % np.uint64(CB)):
         raise ReplayError("misaligned chunk")
@@ -108,7 +103,7 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
 
     # LDS of every block, holding source unit indices
     lds = np.full((nblk, TILE // U), -1, dtype=np.int64)
-    bidx = np.broadcast_to(np.arange(nblk)[:, None, None], in_off.shape)
+    bidx = np.broadcast_to(np.arange(nblk)[:, None], in_off.shape)
     for e in range(W):
         slot = (wr // np.uint64(U) + np.uint64(e)).astype(np.int64)
         src = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
@@ -122,12 +117,10 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     if np.any(read_in != 1):
         raise ReplayError("input unit not read exactly once")
 
-    gseg = h  # output segment index within the tile, same lane split
     out_off = (_xor_table(b, d.out_blk, blk_bits) ^ np.uint64(d.out_c)
-               ^ _xor_table(gseg, d.out_g, t) ^ (q * np.uint64(CB)))
+               ^ _xor_table(cidx, d.st_out, cbits))
     rbase = (_xor_table(b, d.lds_blk, blk_bits) ^ np.uint64(d.lds_c)
-             ^ _xor_table(gseg, [d.lds_rd[t + k] for k in range(t)], t)
-             ^ _xor_table(q, [d.lds_rd[wl + k] for k in range(cpsl)], cpsl))
+             ^ _xor_table(cidx, d.st_lds, cbits))
     out_off, rbase = np.broadcast_arrays(out_off, rbase)
     if np.any(out_off % np.uint64(CB)):
         raise ReplayError("misaligned output chunk")
@@ -136,7 +129,7 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     result = np.full(total_units, -1, dtype=np.int64)
     reads = np.zeros((nblk, TILE // U), dtype=np.int64)
     for e in range(W):
-        rd = rbase ^ _xor_table(np.uint64(e), d.lds_rd, wl)
+        rd = rbase ^ _xor_table(np.uint64(e), d.st_unit, wl)
         if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(TILE)):
             raise ReplayError("LDS read misaligned or out of range")
         slot = (rd // np.uint64(U)).astype(np.int64)
@@ -151,17 +144,21 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
         raise ReplayError("output unit never written")
 
     if check_coalescing:
-        seg = np.uint64(U << t)
-        # lanes with the same row bits cover one whole aligned segment
-        for arr in (in_off, out_off):
-            a = arr.reshape(nblk, NT >> cpsl, 1 << cpsl, J)
+        # load: the lanes of a row read it whole; drain: every group of
+        # 2^pc lanes stores one contiguous aligned piece (128 bytes, or the
+        # whole segment when shorter)
+        pc_load = cpsl
+        pc_drain = min(cpsl, max(0, 7 - (ul + wl)))
+        for arr, pcx in ((in_off, pc_load), (out_off, pc_drain)):
+            G = 1 << pcx
+            a = arr.reshape(nblk, (NT * J) // G, G)
             starts = a.min(axis=2)
-            if np.any(starts % seg):
-                raise ReplayError("segment not aligned")
-            rel = np.sort(a - starts[:, :, None, :], axis=2)
-            want = (np.arange(1 << cpsl, dtype=np.uint64) * np.uint64(CB))[None, None, :, None]
+            if np.any(starts % np.uint64(G * CB)):
+                raise ReplayError("lane group not aligned")
+            rel = np.sort(a - starts[:, :, None], axis=2)
+            want = (np.arange(G, dtype=np.uint64) * np.uint64(CB))[None, None, :]
             if not np.array_equal(rel, np.broadcast_to(want, rel.shape)):
-                raise ReplayError("a wave's access is not whole segments")
+                raise ReplayError("a lane group's access is not contiguous")
     return result
 
 
@@ -229,34 +226,25 @@ def bank_cycles(addr, nbytes: int, banks: int) -> int:
 def tiled_read_addresses(d):
     """LDS byte addresses of wave 0's first output-order read (unit 0)."""
     g = tiled_geometry(d.unit_log2, d.t)
-    lanes = min(64, 1 << g["ntl"])
+    lane_bits = min(6, g["ntl"])
     out = []
-    for l in range(lanes):
-        q, hl = l & ((1 << g["cpsl"]) - 1), l >> g["cpsl"]
+    for l in range(1 << lane_bits):
         a = 0
-        for k in range(g["cpsl"]):
-            if (q >> k) & 1:
-                a ^= d.lds_rd[g["wl"] + k]
-        for k in range(g["rppl"]):
-            if (hl >> k) & 1:
-                a ^= d.lds_rd[d.t + k]
+        for p in range(lane_bits):
+            if (l >> p) & 1:
+                a ^= d.st_lds[p]
         out.append(a)
     return out
 
 
 def tiled_write_addresses(d):
     g = tiled_geometry(d.unit_log2, d.t)
-    lanes = min(64, 1 << g["ntl"])
-    CB = 1 << (d.unit_log2 + g["wl"])
+    lane_bits = min(6, g["ntl"])
     out = []
-    for l in range(lanes):
-        q, hl = l & ((1 << g["cpsl"]) - 1), l >> g["cpsl"]
+    for l in range(1 << lane_bits):
         a = 0
-        for k in range(g["cpsl"]):
-            if (q >> k) & 1:
-                a ^= d.lds_wr_lo[g["wl"] + k]
-        for k in range(g["rppl"]):
-            if (hl >> k) & 1:
-                a ^= d.lds_wr_h[k]
+        for p in range(lane_bits):
+            if (l >> p) & 1:
+                a ^= d.ld_lds[p]
         out.append(a)
     return out

@@ -316,12 +316,12 @@ def test_replay_detects_planted_table_errors():
     P = bm.Plan(12, A, c, 4)
     # a read map that is no longer a bijection reads a slot twice
     d = P.passes()[0]
-    d.lds_rd[3] = d.lds_rd[2]
+    d.st_lds[3] = d.st_lds[2]
     with pytest.raises(ReplayError):
         replay_pass(d)
     # a still-bijective but wrong map is caught by the comparison with the oracle
     d = P.passes()[0]
-    d.lds_rd[3] ^= d.lds_rd[2]
+    d.st_lds[3] ^= d.st_lds[2]
     x = np.arange(1 << 12, dtype=np.int32)
     got = x[replay_pass(d)]
     assert not np.array_equal(got, oracle.apply(A, c, x))
@@ -344,14 +344,13 @@ def test_swizzle_makes_reads_conflict_free(kind, n, e):
     wa = tiled_write_addresses(d)
     CB = U << min(4 - d.unit_log2, d.t)
     lanes = len(ra)
+    # conflict-free under the measured model (32 banks, half a wave per
+    # cycle for 4-byte reads; 8 lanes per cycle for 16-byte accesses), and
+    # under a 64-bank full-wave model
     for banks in (32, 64):
         ideal_r = -(-lanes * max(U, 4) // (4 * banks))
         ideal_w = -(-lanes * CB // (4 * banks))
-        # conflict-free for a full-wave 64-bank LDS; at most 2-way when the
-        # LDS serves half-waves over 32 banks (the lanes of one half do not
-        # span both low bank bits for some bit permutations)
-        assert bank_cycles(ra, U, banks) <= ideal_r * (1 if banks == 64 else 2), \
-            (banks, P.describe())
+        assert bank_cycles(ra, U, banks) == ideal_r, (banks, P.describe())
         assert bank_cycles(wa, CB, banks) == ideal_w
     # the plain layout is conflicted for the transpose (the ablation)
     if kind == "transpose":
