@@ -271,6 +271,8 @@ def main():
         "unit": "GB/s",
         "frac": round(algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": traffic,
+        "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-normalised)",
+        "algorithmic_bytes_per_launch": int(algo_bytes),
     }
     if passes > 1:
         roofline["kernel"] = "both passes of the two-pass plan (one step)"
