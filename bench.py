@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--elem", type=int, default=4, help="custom workload: element bytes")
     ap.add_argument("--seed", type=int, default=1, help="custom workload: matrix seed")
     ap.add_argument("--perm", type=int, default=0, help="c5: permutation index 0..31")
+    ap.add_argument("--perms", type=int, default=0,
+                    help="c5: time permutations 0..PERMS-1 and report min/median/max")
     ap.add_argument("--route", default="auto", choices=["auto", "naive", "two_pass", "fused"])
     ap.add_argument("--tile-log2", type=int, default=0)
     ap.add_argument("--iters-log2", type=int, default=0)
@@ -163,6 +165,7 @@ def main():
     ap.add_argument("--launch", default="auto", choices=["auto", "one_tile", "persistent"])
     ap.add_argument("--grid-log2", type=int, default=0)
     ap.add_argument("--walk", default="auto", choices=["auto", "ranges", "interleaved"])
+    ap.add_argument("--block-map", type=int, default=0)
     ap.add_argument("--warm", action="store_true", help="reuse one buffer pair")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,7 +213,8 @@ def main():
     plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
                    no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
                    grid_log2=args.grid_log2,
-                   walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk])
+                   walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
+                   block_map=args.block_map)
     plan_us = (time.perf_counter() - t0) * 1e6
     if name == "c4" and not args.kind and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2
@@ -241,6 +245,33 @@ def main():
     algo_bytes = 2.0 * nbytes
     value = algo_bytes / (ms * 1e-3) / 1e9
     copy_gbs = algo_bytes / (ms_copy * 1e-3) / 1e9
+
+    perm_stats = None
+    if args.perms and name == "c5" and not args.kind:
+        # the workload's protocol: every permutation planned and timed the
+        # same way on the same buffers; min / median / max of the throughput
+        vals = []
+        for k in range(args.perms):
+            Ak, ck = wl.workload_matrix(name, perm_index=k)
+            pk = bm.Plan(n, Ak, ck, elem, route=route, tile_log2=args.tile_log2,
+                         no_swizzle=args.no_swizzle, iters_log2=args.iters_log2,
+                         launch=launch, grid_log2=args.grid_log2,
+                         walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
+                         block_map=args.block_map)
+
+            def stepk(i, o, pk=pk):
+                st = bm.bmmc_execute(pk.handle, i, o, s_handle)
+                if st != bm.OK:
+                    raise bm.BmmcError(st, "bmmc_execute")
+            msk = time_loop(torch, stepk, bufs, args.steps, args.warmup, stream)
+            vals.append(algo_bytes / (msk * 1e-3) / 1e9)
+            print("perm %d: %.1f GB/s" % (k, vals[-1]), file=sys.stderr, flush=True)
+        sv = sorted(vals)
+        perm_stats = {"perms": len(vals), "min_gbs": round(sv[0], 2),
+                      "median_gbs": round(sv[len(sv) // 2], 2), "max_gbs": round(sv[-1], 2),
+                      "min_frac_of_copy": round(sv[0] / copy_gbs, 4),
+                      "median_frac_of_copy": round(sv[len(sv) // 2] / copy_gbs, 4),
+                      "max_frac_of_copy": round(sv[-1] / copy_gbs, 4)}
 
     parity = "skipped"
     if not args.no_check:
@@ -307,6 +338,8 @@ def main():
         "parity": parity,
         "roofline": roofline,
     }
+    if perm_stats:
+        result["permutations"] = perm_stats
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(A, c, x, args.cpu_budget)
     print(json.dumps(result))

@@ -243,7 +243,44 @@ struct LaunchChoice {
     int persistent;  // 1: persistent launch
     int grid_log2;   // persistent: log2 workgroups requested
     int walk;        // persistent: BMMC_WALK_RANGES or BMMC_WALK_INTERLEAVED
+    int block_map;   // 1 identity, 2 reversed, >= 3 random invertible map (seed)
 };
+
+// Re-index the tiles: new block bit k selects the XOR of the old columns in
+// column k of an invertible map L.  The three block tables are linear in the
+// block index, so they are transformed alike and the set of tiles is unchanged.
+void remap_blocks(bmmc_pass_desc *d, int mode) {
+    const int nbk = d->blk_bits;
+    if (mode <= 1 || nbk < 2) return;
+    std::vector<u64> cols(nbk);
+    if (mode == 2) {
+        for (int k = 0; k < nbk; ++k) cols[k] = u64(1) << (nbk - 1 - k);
+    } else {
+        u64 seed = 0xB10C0000ull + (u64)mode;
+        for (;;) {
+            Mat L = Mat::zeros(nbk, nbk);
+            for (int k = 0; k < nbk; ++k) L.set_col(k, splitmix(seed) & low_mask(nbk));
+            if (rank(L) == nbk) {
+                for (int k = 0; k < nbk; ++k) cols[k] = L.col(k);
+                break;
+            }
+        }
+    }
+    uint64_t in2[BMMC_MAX_BITS] = {}, out2[BMMC_MAX_BITS] = {};
+    uint32_t lds2[BMMC_MAX_BITS] = {};
+    for (int k = 0; k < nbk; ++k)
+        for (int j = 0; j < nbk; ++j)
+            if ((cols[k] >> j) & 1u) {
+                in2[k] ^= d->in_blk[j];
+                out2[k] ^= d->out_blk[j];
+                lds2[k] ^= d->lds_blk[j];
+            }
+    for (int k = 0; k < nbk; ++k) {
+        d->in_blk[k] = in2[k];
+        d->out_blk[k] = out2[k];
+        d->lds_blk[k] = lds2[k];
+    }
+}
 
 int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W,
                 const LaunchChoice &lc, bool swizzle, bmmc_pass_desc *d) {
@@ -489,6 +526,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         d->st_unit[b] = (uint32_t)(slot(Minv.apply(u64(1) << b), S) << ulog2);
     d->out_c = (c & ~lo_t) << ulog2;
     d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
+    remap_blocks(d, lc.block_map);
     return BMMC_OK;
 }
 
@@ -546,6 +584,8 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
                     (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0);
     lc.grid_log2 = o.grid_log2;  // 0: chosen per pass from the tile count
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
+    if (o.block_map < 0) return BMMC_ERR_INVALID_ARG;
+    lc.block_map = o.block_map ? o.block_map : 1;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);

@@ -76,6 +76,10 @@ typedef struct bmmc_plan_options {
     int launch;     /* BMMC_LAUNCH_*: how the tile pass is launched */
     int grid_log2;  /* persistent launch: log2 of workgroups; 0 = planner's choice */
     int walk;       /* persistent launch: BMMC_WALK_* order of tiles; 0 = planner's choice */
+    int block_map;  /* re-indexing of the tiles: 0 = planner's choice, 1 = identity,
+                       2 = reversed bit order, >= 3 = a random invertible F2 map seeded
+                       with the value (the set of tiles is the same; only the order in
+                       which workgroups meet them changes) */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */

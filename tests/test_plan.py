@@ -267,6 +267,9 @@ def _cases():
         cases.append(("general", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2)))
         cases.append(("bpc", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2,
                                          walk=bm.WALK_INTERLEAVED)))
+    for bmap in (2, 3, 17):
+        cases.append(("general", 16, 4, dict(block_map=bmap)))
+        cases.append(("bitrev", 16, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
     cases.append(("general", 14, 4, dict(no_swizzle=1)))
     cases.append(("general", 5, 4, dict()))
     cases.append(("general", 2, 4, dict()))
