@@ -150,8 +150,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--kind", default=None, choices=["bitrev", "transpose", "bpc", "bmmc"],
-                    help="custom workload instead of --workload: the matrix kind")
+    ap.add_argument("--kind", default=None,
+                    choices=["bitrev", "transpose", "bpc", "bmmc", "blockperm"],
+                    help="custom workload instead of --workload: the matrix kind "
+                         "(blockperm: identity on the low --seg-log2 bits, random on the rest)")
+    ap.add_argument("--seg-log2", type=int, default=10, help="blockperm: block size, log2 elements")
     ap.add_argument("--n", type=int, default=24, help="custom workload: index bits")
     ap.add_argument("--elem", type=int, default=4, help="custom workload: element bytes")
     ap.add_argument("--seed", type=int, default=1, help="custom workload: matrix seed")
@@ -162,7 +165,8 @@ def main():
     ap.add_argument("--tile-log2", type=int, default=0)
     ap.add_argument("--iters-log2", type=int, default=0)
     ap.add_argument("--no-swizzle", action="store_true")
-    ap.add_argument("--launch", default="auto", choices=["auto", "one_tile", "persistent"])
+    ap.add_argument("--launch", default="auto",
+                    choices=["auto", "one_tile", "persistent", "streamed"])
     ap.add_argument("--grid-log2", type=int, default=0)
     ap.add_argument("--walk", default="auto", choices=["auto", "ranges", "interleaved"])
     ap.add_argument("--block-map", type=int, default=0)
@@ -193,10 +197,16 @@ def main():
             A, c = wl.transpose_matrix(n // 2, n - n // 2), 0
         elif args.kind == "bpc":
             A, c = wl.random_bpc(n, args.seed)
+        elif args.kind == "blockperm":
+            sl = args.seg_log2
+            Q, _ = wl.random_bmmc(n - sl, args.seed, lib_accepts(n - sl))
+            A = np.array([1 << r for r in range(sl)] + [int(q) << sl for q in Q], dtype=np.uint64)
+            c = 0
         else:
             A, c = wl.random_bmmc(n, args.seed, lib_accepts(n))
         x = wl.fill_random_bytes(n, elem, args.seed)
-        workload_name = "%s_n%d_%dB" % (args.kind, n, elem)
+        workload_name = "%s_n%d_%dB" % (args.kind, n, elem) + (
+            "_seg%d" % args.seg_log2 if args.kind == "blockperm" else "")
     else:
         w = wl.WORKLOADS[name]
         n, elem = w.n, w.elem_bytes
@@ -209,7 +219,7 @@ def main():
 
     t0 = time.perf_counter()
     launch = {"auto": bm.LAUNCH_AUTO, "one_tile": bm.LAUNCH_ONE_TILE,
-              "persistent": bm.LAUNCH_PERSISTENT}[args.launch]
+              "persistent": bm.LAUNCH_PERSISTENT, "streamed": bm.LAUNCH_STREAMED}[args.launch]
     plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
                    no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
                    grid_log2=args.grid_log2,

@@ -32,7 +32,7 @@ KIND_NAMES = {0: "identity", 1: "bpc", 2: "tiled", 3: "general"}
 ROUTE_AUTO, ROUTE_NAIVE, ROUTE_TWO_PASS, ROUTE_FUSED = 0, 1, 2, 3
 ROUTE_NAMES = {0: "auto", 1: "naive", 2: "two_pass", 3: "fused"}
 KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE = 0, 1, 2, 3
-LAUNCH_AUTO, LAUNCH_ONE_TILE, LAUNCH_PERSISTENT = 0, 1, 2
+LAUNCH_AUTO, LAUNCH_ONE_TILE, LAUNCH_PERSISTENT, LAUNCH_STREAMED = 0, 1, 2, 3
 WALK_AUTO, WALK_RANGES, WALK_INTERLEAVED = 0, 1, 2
 
 MAX_N = 32
@@ -291,11 +291,12 @@ class Plan:
 
     def describe(self) -> dict:
         i = self.info
-        launch = [{1: "one_tile", 2: "persistent"}.get(d.launch, "-") if d.kernel == KERNEL_TILED
+        launch = [{1: "one_tile", 2: "persistent", 3: "streamed"}.get(d.launch, "-")
+                  if d.kernel == KERNEL_TILED
                   else {0: "copy", 1: "chunk", 3: "naive"}.get(d.kernel, "?") for d in self.passes()]
         grid = [d.grid_log2 for d in self.passes() if d.kernel == KERNEL_TILED]
         walk = [{1: "ranges", 2: "interleaved"}.get(d.walk) for d in self.passes()
-                if d.kernel == KERNEL_TILED and d.launch == LAUNCH_PERSISTENT]
+                if d.kernel == KERNEL_TILED and d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED)]
         return {"n": i.n, "elem_bytes": i.elem_bytes, "kind": KIND_NAMES[i.kind],
                 "route": ROUTE_NAMES[i.route], "passes": i.passes, "unit_bytes": i.unit_bytes,
                 "unit_bits": i.unit_bits, "tile_log2": i.tile_log2, "n_over": i.n_over,

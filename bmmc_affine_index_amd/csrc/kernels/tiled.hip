@@ -174,6 +174,56 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
     }
 }
 
+// Streamed: the persistent walk with the waves split by role.  Waves of the
+// first half only load tiles and stage them in LDS; waves of the second half
+// only drain tiles and store them.  On gfx9-family GPUs loads and stores share
+// one wait counter, so a wave that has stores in flight cannot wait for its
+// loads alone; with one kind of access per wave every wait is exact, loads of
+// tile k+1 stay in flight while tile k drains, and stores are never waited
+// for.  One barrier per tile orders the halves: the loaders write buffer k&1
+// before barrier k, the storers read it after barrier k and have finished
+// before barrier k+1, after which the loaders may write it again (tile k+2).
+template <int UL, int T>
+__global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
+    bmmc_tiled_streamed_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                               const bmmc_pass_desc d) {
+    using C = TiledCfg<UL, T, 0>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE];
+    const bool loader = threadIdx.x < C::NT;  // wave-uniform: NT is a multiple of 64 or all
+    const LaneParts p = lane_parts<C, T>(d, threadIdx.x & (C::NT - 1));
+    const int r = d.blk_bits - d.grid_log2;
+    const bool interleaved = d.walk == BMMC_WALK_INTERLEAVED;
+    const uint64_t first = interleaved ? (uint64_t)blockIdx.x : ((uint64_t)blockIdx.x << r);
+    const int shift = interleaved ? d.grid_log2 : 0;
+    const uint64_t count = uint64_t(1) << r;
+
+    uint64_t in_base = dev::xor_bits_uniform(d.in_blk, first);
+    uint64_t out_base = dev::xor_bits_uniform(d.out_blk, first) ^ d.out_c;
+    uint32_t rd_base = dev::xor_bits_uniform(d.lds_blk, first) ^ d.lds_c;
+
+    dev::Chunk<C::CB> v[C::J];
+    if (loader) load_tile<C, T>(v, in, in_base, d, p);
+    for (uint64_t k = 0; k < count; ++k) {
+        uint8_t *buf = lds + (k & 1) * C::TILE;
+        const bool more = k + 1 < count;
+        const int bit = more ? shift + __builtin_ctzll(k + 1) : 0;
+        if (loader) stage_tile<C, T>(buf, v, d, p);
+        __syncthreads();
+        if (loader) {
+            if (more) {
+                in_base ^= d.in_blk[bit];
+                load_tile<C, T>(v, in, in_base, d, p);
+            }
+        } else {
+            drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
+            if (more) {
+                out_base ^= d.out_blk[bit];
+                rd_base ^= d.lds_blk[bit];
+            }
+        }
+    }
+}
+
 namespace {
 
 constexpr int kMaxT[5] = {8, 7, 7, 6, 6};
@@ -188,10 +238,16 @@ struct TiledArgs {
 
 template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     using C = TiledCfg<UL, T, IT>;
-    if (a.d->launch == BMMC_LAUNCH_PERSISTENT) {
+    if (a.d->launch == BMMC_LAUNCH_PERSISTENT || a.d->launch == BMMC_LAUNCH_STREAMED) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
-            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
-                               dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out, *a.d);
+            if (a.d->launch == BMMC_LAUNCH_STREAMED)
+                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T>),
+                                   dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
+                                   a.out, *a.d);
+            else
+                hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
+                                   dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out,
+                                   *a.d);
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
         } else {
             return BMMC_ERR_UNSUPPORTED;
@@ -230,7 +286,7 @@ int dispatch(int ul, int t, int it, const TiledArgs *a) {
 }  // namespace
 
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
-    if (launch == BMMC_LAUNCH_PERSISTENT &&
+    if ((launch == BMMC_LAUNCH_PERSISTENT || launch == BMMC_LAUNCH_STREAMED) &&
         (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
          (uint64_t(2) << (2 * t + unit_log2)) > 131072))
         return false;
@@ -240,9 +296,10 @@ bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
 int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
     if (d.iters_log2 > d.blk_bits || d.grid_log2 > d.blk_bits || d.grid_log2 < 0)
         return BMMC_ERR_INVALID_ARG;
-    if (d.launch != BMMC_LAUNCH_PERSISTENT && d.launch != BMMC_LAUNCH_ONE_TILE)
+    if (d.launch != BMMC_LAUNCH_PERSISTENT && d.launch != BMMC_LAUNCH_ONE_TILE &&
+        d.launch != BMMC_LAUNCH_STREAMED)
         return BMMC_ERR_INVALID_ARG;
-    if (d.launch == BMMC_LAUNCH_PERSISTENT && d.walk != BMMC_WALK_RANGES &&
+    if (d.launch != BMMC_LAUNCH_ONE_TILE && d.walk != BMMC_WALK_RANGES &&
         d.walk != BMMC_WALK_INTERLEAVED)
         return BMMC_ERR_INVALID_ARG;
     TiledArgs a{&d, static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), s};

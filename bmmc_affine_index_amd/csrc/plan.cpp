@@ -240,7 +240,7 @@ int default_tile_log2(int ulog2) {
 // B's first t columns, the tile's image is 2^t whole output segments.
 struct LaunchChoice {
     int iters_log2;  // one-tile launch: tiles staged together
-    int persistent;  // 1: persistent launch
+    int persistent;  // BMMC_LAUNCH_PERSISTENT or _STREAMED; 0: one-tile launch
     int grid_log2;   // persistent: log2 workgroups requested
     int walk;        // persistent: BMMC_WALK_RANGES or BMMC_WALK_INTERLEAVED
     int block_map;   // 1 identity, 2 reversed, >= 3 random invertible map (seed)
@@ -483,7 +483,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     const u64 tile_bytes = u64(1) << (2 * t + ulog2);
     if (lc.persistent && 2 * tile_bytes <= kMaxPersistentLdsBytes) {
         // persistent: two LDS tiles (double buffer), no staged iterations
-        d->launch = BMMC_LAUNCH_PERSISTENT;
+        d->launch = lc.persistent;
         d->iters_log2 = 0;
         // One workgroup per compute unit (2^8 on a 256-CU MI355X) walking
         // long tile ranges measured best for large arrays; below 2^14 tiles
@@ -573,15 +573,16 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     if (o.route < BMMC_ROUTE_AUTO || o.route > BMMC_ROUTE_FUSED) return BMMC_ERR_INVALID_ARG;
     if (o.tile_log2 < 0 || o.tile_log2 > BMMC_MAX_TILE || o.iters_log2 < 0 || o.iters_log2 > 3)
         return BMMC_ERR_INVALID_ARG;
-    if (o.launch < BMMC_LAUNCH_AUTO || o.launch > BMMC_LAUNCH_PERSISTENT || o.grid_log2 < 0 ||
+    if (o.launch < BMMC_LAUNCH_AUTO || o.launch > BMMC_LAUNCH_STREAMED || o.grid_log2 < 0 ||
         o.grid_log2 > 24)
         return BMMC_ERR_INVALID_ARG;
-    if (o.launch == BMMC_LAUNCH_PERSISTENT && o.iters_log2 > 0) return BMMC_ERR_INVALID_ARG;
+    if (o.launch >= BMMC_LAUNCH_PERSISTENT && o.iters_log2 > 0) return BMMC_ERR_INVALID_ARG;
     if (o.walk < BMMC_WALK_AUTO || o.walk > BMMC_WALK_INTERLEAVED) return BMMC_ERR_INVALID_ARG;
     LaunchChoice lc;
     lc.iters_log2 = o.iters_log2;
-    lc.persistent = o.launch == BMMC_LAUNCH_PERSISTENT ||
-                    (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0);
+    lc.persistent = o.launch >= BMMC_LAUNCH_PERSISTENT ? o.launch
+                    : (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0) ? BMMC_LAUNCH_PERSISTENT
+                                                                          : 0;
     lc.grid_log2 = o.grid_log2;  // 0: chosen per pass from the tile count
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     if (o.block_map < 0) return BMMC_ERR_INVALID_ARG;

@@ -92,6 +92,7 @@ typedef struct bmmc_plan_options {
 #define BMMC_LAUNCH_ONE_TILE 1   /* one workgroup per tile (or per 2^iters_log2 tiles) */
 #define BMMC_LAUNCH_PERSISTENT 2 /* 2^grid_log2 workgroups, each walking a range of tiles
                                     with the next tile's loads overlapping this tile's stores */
+#define BMMC_LAUNCH_STREAMED 3   /* as PERSISTENT, with loader waves and storer waves */
 
 /* What a plan does, for tests and benchmarks. */
 typedef struct bmmc_plan_info {
@@ -143,7 +144,7 @@ typedef struct bmmc_pass_desc {
                             unit-index bits (NAIVE) */
     int32_t iters_log2;  /* one-tile launch: tiles staged together, log2 (TILED) */
     int32_t unit_xor;    /* in-chunk unit permutation (CHUNK) */
-    int32_t launch;      /* BMMC_LAUNCH_ONE_TILE or BMMC_LAUNCH_PERSISTENT (TILED) */
+    int32_t launch;      /* BMMC_LAUNCH_ONE_TILE, _PERSISTENT or _STREAMED (TILED) */
     int32_t grid_log2;   /* persistent launch: 2^grid_log2 workgroups (TILED) */
     int32_t walk;        /* persistent launch: BMMC_WALK_RANGES or _INTERLEAVED (TILED) */
     int32_t reserved;

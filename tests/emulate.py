@@ -39,7 +39,7 @@ class ReplayError(AssertionError):
     pass
 
 
-LAUNCH_ONE_TILE, LAUNCH_PERSISTENT = 1, 2
+LAUNCH_ONE_TILE, LAUNCH_PERSISTENT, LAUNCH_STREAMED = 1, 2, 3
 
 
 def check_persistent_walk(d):
@@ -80,7 +80,7 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     TILE = U << (2 * t)
     blk_bits = d.blk_bits
     nblk = 1 << blk_bits
-    if d.launch == LAUNCH_PERSISTENT:
+    if d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED):
         if d.lds_bytes != 2 * TILE or d.iters_log2 != 0:
             raise ReplayError("persistent launch needs two LDS tiles")
         check_persistent_walk(d)

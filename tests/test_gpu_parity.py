@@ -88,6 +88,12 @@ for it in (1, 2, 3):
     SMALL.append(("bitrev", 18, 4, dict(iters_log2=it)))
     SMALL.append(("bpc", 18, 16, dict(iters_log2=it)))
 SMALL.append(("general", 15, 4, dict(no_swizzle=1)))
+for e in (1, 2, 4, 8, 16):
+    for kind in ("general", "bpc", "bitrev"):
+        SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_STREAMED)))
+        SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=2)))
+        SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=3,
+                                        walk=bm.WALK_INTERLEAVED)))
 for bmap in (2, 3, 99):
     SMALL.append(("general", 17, 4, dict(block_map=bmap)))
     SMALL.append(("bpc", 17, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))

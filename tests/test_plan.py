@@ -267,6 +267,9 @@ def _cases():
         cases.append(("general", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2)))
         cases.append(("bpc", 15, e, dict(launch=bm.LAUNCH_PERSISTENT, grid_log2=2,
                                          walk=bm.WALK_INTERLEAVED)))
+    for e in (1, 4, 16):
+        cases.append(("general", 15, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=2)))
+        cases.append(("bpc", 16, e, dict(launch=bm.LAUNCH_STREAMED, walk=bm.WALK_INTERLEAVED)))
     for bmap in (2, 3, 17):
         cases.append(("general", 16, 4, dict(block_map=bmap)))
         cases.append(("bitrev", 16, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
