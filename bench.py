@@ -144,6 +144,80 @@ def cpu_baseline(A, c, x, budget_s: float):
                                                              threads)}
 
 
+ABLATION_VARIANTS = [
+    # name, plan options; the paper's Figure 9 columns, then this library's default
+    ("naive", dict(route=bm.ROUTE_NAIVE)),
+    ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True)),
+    ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE)),
+    ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
+    ("persistent (default)", dict()),
+]
+
+
+def run_ablation(args, torch):
+    """The paper's Figure 9 (speedup of each optimisation over the naive kernel
+    for random BPC, bit-reversal and random BMMC) and Figure 11 (the same
+    against the array size), on 32-bit elements.  Random BMMCs are run both
+    as the pages' two tiled passes and as the fused single pass."""
+    import oracle
+    stream = torch.cuda.current_stream()
+    s_handle = int(stream.cuda_stream)
+    for n in [int(v) for v in args.sizes.split(",")]:
+        elem = 4
+        nbytes = elem << n
+        x = wl.fill_random_bytes(n, elem, 1000 + n)
+        raw = torch.from_numpy(x.reshape(-1)).to("cuda:0")
+        pairs = max(1, -(-(1 << 30) // (2 * nbytes)))
+        ins = [raw] + [raw.clone() for _ in range(pairs - 1)]
+        outs = [torch.empty_like(raw) for _ in range(pairs)]
+        bufs = list(zip(ins, outs))
+        steps = max(10, min(args.steps, int(2e9 // (2 * nbytes)) or 10))
+
+        def copy(i, o):
+            bm.bmmc_copy(i, o, nbytes, s_handle)
+        ms_copy = time_loop(torch, copy, bufs, steps, 3, stream)
+        copy_gbs = 2.0 * nbytes / (ms_copy * 1e-3) / 1e9
+        kinds = [("random_bpc", wl.random_bpc(n, 7)), ("bit_reverse", (wl.bit_reverse_matrix(n), 0)),
+                 ("random_bmmc", wl.random_bmmc(n, 7, lib_accepts(n)))]
+        for kind, (A, c) in kinds:
+            variants = list(ABLATION_VARIANTS)
+            if kind == "random_bmmc":
+                variants = [variants[0]] + [
+                    (nm + " two-pass", dict(kw, route=bm.ROUTE_TWO_PASS)) for nm, kw in variants[1:4]
+                ] + [("persistent two-pass", dict(route=bm.ROUTE_TWO_PASS)), variants[4]]
+            base = None
+            for vname, kw in variants:
+                plan = bm.Plan(n, A, c, elem, **kw)
+
+                def step(i, o, plan=plan):
+                    st = bm.bmmc_execute(plan.handle, i, o, s_handle)
+                    if st != bm.OK:
+                        raise bm.BmmcError(st, "bmmc_execute")
+                ms = time_loop(torch, step, bufs, steps, 3, stream)
+                gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
+                base = base or gbs
+                step(*bufs[0])
+                torch.cuda.synchronize()
+                got = outs[0].cpu().numpy().reshape(x.shape)
+                if n <= 24:
+                    ok = np.array_equal(got, oracle.apply(A, c, x, threads=16))
+                else:
+                    idx = np.random.Generator(np.random.PCG64(n)).integers(
+                        0, 1 << n, size=1 << 18, dtype=np.uint64)
+                    ok = oracle.check_sampled(A, c, x, got, idx)[0] == 0
+                print(json.dumps({"ablation": True, "kind": kind, "n": n, "elem_bytes": elem,
+                                  "variant": vname, "gbs": round(gbs, 1),
+                                  "frac_of_copy": round(gbs / copy_gbs, 4),
+                                  "speedup_vs_naive": round(gbs / base, 3),
+                                  "ms": round(ms, 5), "copy_gbs": round(copy_gbs, 1),
+                                  "passes": plan.info.passes,
+                                  "parity": "bit-exact" if ok else "MISMATCH"}), flush=True)
+                if not ok:
+                    sys.exit(3)
+        del ins, outs, bufs, raw
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +248,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="the paper's Figure 9/11 variants over kinds and sizes, "
+                         "one JSON line each (not the headline line)")
+    ap.add_argument("--sizes", default="20,24,28", help="ablation: comma-separated n")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -187,6 +265,10 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     bm.lib()  # fails loudly when the HIP library is missing
+
+    if args.ablation:
+        run_ablation(args, torch)
+        return
 
     name = args.workload
     if args.kind:
