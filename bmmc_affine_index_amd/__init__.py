@@ -44,7 +44,8 @@ MAX_PASSES = 2
 EXPORTED = (
     "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
-    "bmmc_plan_get_factor", "bmmc_plan_get_pass",
+    "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_parm_matrix",
+    "bmmc_matrix_inverse", "bmmc_tensor_permute_matrix",
 )
 
 
@@ -129,6 +130,14 @@ def lib():
     L.bmmc_plan_get_pass.argtypes = [ctypes.c_void_p, ctypes.c_int,
                                      ctypes.POINTER(bmmc_pass_desc)]
     L.bmmc_plan_get_pass.restype = ctypes.c_int
+    L.bmmc_parm_matrix.argtypes = [ctypes.c_int, ctypes.c_uint64, u64p]
+    L.bmmc_parm_matrix.restype = ctypes.c_int
+    L.bmmc_matrix_inverse.argtypes = [ctypes.c_int, u64p, u64p]
+    L.bmmc_matrix_inverse.restype = ctypes.c_int
+    intp = ctypes.POINTER(ctypes.c_int)
+    L.bmmc_tensor_permute_matrix.argtypes = [ctypes.c_int, intp, intp, ctypes.c_uint64, u64p,
+                                             u64p, intp]
+    L.bmmc_tensor_permute_matrix.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -236,6 +245,41 @@ def bmmc_plan_get_pass(plan: int, pass_index: int) -> bmmc_pass_desc:
     return d
 
 
+def bmmc_parm_matrix(n: int, mask: int):
+    """Row masks of the BMMC that parm conjugates with (see include/bmmc.h)."""
+    A = (ctypes.c_uint64 * max(n, 1))()
+    st = lib().bmmc_parm_matrix(int(n), int(mask), A)
+    if st != OK:
+        raise BmmcError(st, "bmmc_parm_matrix")
+    return [int(a) for a in A[:n]]
+
+
+def bmmc_matrix_inverse(A: Sequence[int]):
+    """Row masks of A^{-1} over F2."""
+    n, arr = _rows(A)
+    out = (ctypes.c_uint64 * max(n, 1))()
+    st = lib().bmmc_matrix_inverse(n, arr, out)
+    if st != OK:
+        raise BmmcError(st, "bmmc_matrix_inverse")
+    return [int(a) for a in out[:n]]
+
+
+def bmmc_tensor_permute_matrix(dim_log2: Sequence[int], perm: Sequence[int],
+                               flip_mask: int = 0):
+    """(A, c, n) of the BPC that permutes and flips tensor dimensions."""
+    k = len(dim_log2)
+    dl = (ctypes.c_int * k)(*[int(v) for v in dim_log2])
+    pm = (ctypes.c_int * k)(*[int(v) for v in perm])
+    A = (ctypes.c_uint64 * MAX_N)()
+    c = ctypes.c_uint64()
+    n = ctypes.c_int()
+    st = lib().bmmc_tensor_permute_matrix(k, dl, pm, int(flip_mask), A, ctypes.byref(c),
+                                          ctypes.byref(n))
+    if st != OK:
+        raise BmmcError(st, "bmmc_tensor_permute_matrix")
+    return [int(a) for a in A[:n.value]], int(c.value), n.value
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrapper
 # ---------------------------------------------------------------------------
@@ -324,3 +368,57 @@ def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw)
         out = torch.empty_like(inp)
     Plan(n, A, c, elem, **plan_kw)(inp, out, stream)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Users of the permutation: parm and tensor dimensions
+# ---------------------------------------------------------------------------
+
+def parm(x, mask: int, f, stream=None):
+    """parm mask f x: split the 2^n rows of x by the F2 dot product i.mask,
+    apply f to the part with i.mask = 0 and to the other part (each in
+    increasing index order, as a tensor of 2^(n-1) rows), and stitch the
+    results back in place of the parts.  f takes and returns a device tensor
+    of the same shape.  The two permutations run in this library's kernels."""
+    import torch
+    rows = x.shape[0]
+    n = rows.bit_length() - 1
+    if rows != (1 << n) or n < 1:
+        raise ValueError("the first axis must have 2^n entries, n >= 1")
+    A = bmmc_parm_matrix(n, mask)
+    y = permute(x, A, 0, stream=stream)
+    half = rows // 2
+    z = torch.empty_like(y)
+    z[:half] = f(y[:half])
+    z[half:] = f(y[half:])
+    return permute(z, bmmc_matrix_inverse(A), 0, stream=stream)
+
+
+def permute_dims(t, perm: Sequence[int], flip: Sequence[int] = (), stream=None):
+    """t.flip(flip).permute(perm).contiguous() for a contiguous device tensor
+    whose dimensions are powers of two, as one BPC permutation."""
+    shape = list(t.shape)
+    dl = []
+    for s in shape:
+        if s < 1 or s & (s - 1):
+            raise ValueError("every dimension must be a power of two")
+        dl.append(s.bit_length() - 1)
+    fm = 0
+    for d in flip:
+        fm |= 1 << (d % len(shape))
+    A, c, n = bmmc_tensor_permute_matrix(dl, [p % len(shape) for p in perm], fm)
+    out_shape = [shape[p % len(shape)] for p in perm]
+    if n == 0:
+        return t.clone().reshape(out_shape)
+    flat = t.reshape(1 << n, -1) if t.numel() else t
+    return permute(flat, A, c, stream=stream).reshape(out_shape)
+
+
+def flip(t, dims: Sequence[int], stream=None):
+    """t.flip(dims) for power-of-two dimensions, as one BPC permutation."""
+    return permute_dims(t, list(range(t.dim())), flip=dims, stream=stream)
+
+
+def transpose2d(t, stream=None):
+    """The transpose of a 2^a x 2^b matrix (a rotation of the index bits)."""
+    return permute_dims(t, [1, 0], stream=stream)

@@ -215,6 +215,31 @@ int bmmc_plan_get_factor(const bmmc_plan *plan, int pass, uint64_t *A_out, uint6
  * check addressing, coalescing and LDS banks without a GPU.  Host-only. */
 int bmmc_plan_get_pass(const bmmc_plan *plan, int pass, bmmc_pass_desc *desc);
 
+/* ---- users of the permutation (host-only matrix builders) -------------- */
+
+/* The BMMC of parm ("Efficient GPU Implementation of Affine Index
+ * Permutations on Arrays", introduction: parm mask f xs splits xs by the F2
+ * dot product i.mask, applies f to both parts and stitches them back; parm
+ * with mask m is a BMMC, parm on the two halves, and the inverse BMMC).
+ * Writes n row masks to A_out: output bit n-1 = i.mask, the other output
+ * bits are the input bits except the mask's lowest set bit, in order, so the
+ * first half holds the elements with i.mask = 0 and both halves keep
+ * increasing index order.  mask must be nonzero with no bits at >= n. */
+int bmmc_parm_matrix(int n, uint64_t mask, uint64_t *A_out);
+
+/* Inverse over F2 of n row masks (for the inverse permutation: (A, c) is
+ * undone by (A^{-1}, A^{-1}.c)).  BMMC_ERR_SINGULAR if A is singular. */
+int bmmc_matrix_inverse(int n, const uint64_t *A, uint64_t *A_inv);
+
+/* The BPC that permutes (and flips) the dimensions of a row-major tensor of
+ * shape (2^dim_log2[0], ..., 2^dim_log2[ndims-1]): output dimension j is
+ * input dimension perm[j]; input dimension d is reversed when bit d of
+ * flip_mask is set.  Writes n = sum(dim_log2) row masks to A_out (room for
+ * BMMC_MAX_N), the complement to *c_out and n to *n_out.  Host-only. */
+int bmmc_tensor_permute_matrix(int ndims, const int *dim_log2, const int *perm,
+                               uint64_t flip_mask, uint64_t *A_out, uint64_t *c_out,
+                               int *n_out);
+
 #ifdef __cplusplus
 }
 #endif

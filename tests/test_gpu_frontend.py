@@ -1,0 +1,71 @@
+"""GPU tests of the permutation's users: tensor-dimension permutes and flips
+against PyTorch's CPU reference, and parm against its definition."""
+import numpy as np
+import pytest
+
+import bmmc_affine_index_amd as bm
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+DTYPES = ["uint8", "float16", "float32", "int64", "complex128"]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("seed", range(4))
+def test_permute_dims_matches_torch(dtype, seed):
+    torch = _torch()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = int(rng.integers(2, 6))
+    shape = [1 << int(v) for v in rng.integers(0, 6, size=k)]
+    perm = [int(v) for v in rng.permutation(k)]
+    flips = [d for d in range(k) if rng.random() < 0.4]
+    dt = getattr(torch, dtype)
+    x = torch.from_numpy(rng.integers(0, 100, size=shape).astype(np.float64)).to(dt)
+    want = (x.flip(flips) if flips else x).permute(perm).contiguous()
+    got = bm.permute_dims(x.to("cuda:0"), perm, flip=flips)
+    torch.cuda.synchronize()
+    assert got.shape == want.shape
+    assert torch.equal(got.cpu(), want)
+
+
+def test_flip_and_transpose():
+    torch = _torch()
+    x = torch.arange(1 << 20, dtype=torch.int32).reshape(256, 64, 64)
+    d = x.to("cuda:0")
+    assert torch.equal(bm.flip(d, [0, 2]).cpu(), x.flip([0, 2]))
+    m = torch.arange(1 << 18, dtype=torch.float32).reshape(512, 512)
+    assert torch.equal(bm.transpose2d(m.to("cuda:0")).cpu(), m.T.contiguous())
+    r = torch.arange(1 << 16, dtype=torch.float32).reshape(64, 1024)
+    assert torch.equal(bm.transpose2d(r.to("cuda:0")).cpu(), r.T.contiguous())
+
+
+def _parm_reference(x, mask, f):
+    n = x.shape[0].bit_length() - 1
+    cls = np.array([bin(i & mask).count("1") & 1 for i in range(1 << n)])
+    out = np.empty_like(x)
+    for b in (0, 1):
+        idx = np.nonzero(cls == b)[0]
+        out[idx] = f(x[idx])
+    return out
+
+
+@pytest.mark.parametrize("n,mask", [(4, 0b0011), (10, 0b1000000001), (16, 0xF0F1), (18, 0x20000)])
+def test_parm_matches_definition(n, mask):
+    torch = _torch()
+    rng = np.random.Generator(np.random.PCG64(n))
+    x = rng.integers(0, 1000, size=1 << n).astype(np.int64)
+    got = bm.parm(torch.from_numpy(x).to("cuda:0"), mask, lambda t: torch.cumsum(t, 0))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), _parm_reference(x, mask, np.cumsum))
+    # a 2-D payload: rows move whole
+    y = rng.random((1 << n, 4)).astype(np.float32)
+    got = bm.parm(torch.from_numpy(y).to("cuda:0"), mask, lambda t: t.flip(0))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), _parm_reference(y, mask, lambda a: a[::-1]))
