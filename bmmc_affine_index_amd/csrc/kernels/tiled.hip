@@ -183,13 +183,18 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
 // for.  One barrier per tile orders the halves: the loaders write buffer k&1
 // before barrier k, the storers read it after barrier k and have finished
 // before barrier k+1, after which the loaders may write it again (tile k+2).
-template <int UL, int T>
+template <int UL, int T, int DEPTH>
 __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     bmmc_tiled_streamed_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                const bmmc_pass_desc d) {
     using C = TiledCfg<UL, T, 0>;
+    static_assert(DEPTH == 1 || DEPTH == 2, "tiles of loads in flight per loader wave");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE];
-    const bool loader = threadIdx.x < C::NT;  // wave-uniform: NT is a multiple of 64 or all
+    static_assert(C::NT >= 64, "each role must be whole waves");
+    // The role is the same for every lane of a wave (NT is a multiple of 64);
+    // reading it from the first lane tells the compiler so, which keeps the
+    // loaders' running tile index in scalar registers.
+    const bool loader = __builtin_amdgcn_readfirstlane((int)threadIdx.x) < C::NT;
     const LaneParts p = lane_parts<C, T>(d, threadIdx.x & (C::NT - 1));
     const int r = d.blk_bits - d.grid_log2;
     const bool interleaved = d.walk == BMMC_WALK_INTERLEAVED;
@@ -197,28 +202,44 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     const int shift = interleaved ? d.grid_log2 : 0;
     const uint64_t count = uint64_t(1) << r;
 
+    // loaders: running input base of the last tile loaded (tiles are loaded
+    // in walk order, DEPTH ahead of the one being staged)
     uint64_t in_base = dev::xor_bits_uniform(d.in_blk, first);
+    uint64_t loaded = 0;  // tiles loaded so far
+    // storers: running bases of the next tile to drain
     uint64_t out_base = dev::xor_bits_uniform(d.out_blk, first) ^ d.out_c;
     uint32_t rd_base = dev::xor_bits_uniform(d.lds_blk, first) ^ d.lds_c;
 
-    dev::Chunk<C::CB> v[C::J];
-    if (loader) load_tile<C, T>(v, in, in_base, d, p);
-    for (uint64_t k = 0; k < count; ++k) {
-        uint8_t *buf = lds + (k & 1) * C::TILE;
-        const bool more = k + 1 < count;
-        const int bit = more ? shift + __builtin_ctzll(k + 1) : 0;
-        if (loader) stage_tile<C, T>(buf, v, d, p);
-        __syncthreads();
-        if (loader) {
-            if (more) {
-                in_base ^= d.in_blk[bit];
-                load_tile<C, T>(v, in, in_base, d, p);
-            }
-        } else {
-            drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
-            if (more) {
-                out_base ^= d.out_blk[bit];
-                rd_base ^= d.lds_blk[bit];
+    dev::Chunk<C::CB> v[DEPTH][C::J];
+    auto load_next = [&](dev::Chunk<C::CB>(&dst)[C::J]) {
+        if (loaded > 0) in_base ^= d.in_blk[shift + __builtin_ctzll(loaded)];
+        load_tile<C, T>(dst, in, in_base, d, p);
+        ++loaded;
+    };
+    auto drain_next = [&](uint64_t k, uint8_t *buf) {
+        drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
+        if (k + 1 < count) {
+            const int bit = shift + __builtin_ctzll(k + 1);
+            out_base ^= d.out_blk[bit];
+            rd_base ^= d.lds_blk[bit];
+        }
+    };
+    if (loader) {
+        load_next(v[0]);
+        if (DEPTH == 2 && count > 1) load_next(v[1]);
+    }
+    for (uint64_t k = 0; k < count; k += DEPTH) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            if (k + s < count) {  // uniform
+                uint8_t *buf = lds + ((k + s) & 1) * C::TILE;
+                if (loader) stage_tile<C, T>(buf, v[s], d, p);
+                __syncthreads();
+                if (loader) {
+                    if (loaded < count) load_next(v[s]);
+                } else {
+                    drain_next(k + s, buf);
+                }
             }
         }
     }
@@ -238,16 +259,26 @@ struct TiledArgs {
 
 template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     using C = TiledCfg<UL, T, IT>;
-    if (a.d->launch == BMMC_LAUNCH_PERSISTENT || a.d->launch == BMMC_LAUNCH_STREAMED) {
-        if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
-            if (a.d->launch == BMMC_LAUNCH_STREAMED)
-                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T>),
+    if (a.d->launch == BMMC_LAUNCH_STREAMED) {
+        if constexpr (IT == 0 && 2 * C::TILE <= 131072 && C::NT >= 64) {
+            if (a.d->depth == 2)
+                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2>),
                                    dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
                                    a.out, *a.d);
             else
-                hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
-                                   dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out,
-                                   *a.d);
+                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1>),
+                                   dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
+                                   a.out, *a.d);
+            return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+        } else {
+            return BMMC_ERR_UNSUPPORTED;
+        }
+    }
+    if (a.d->launch == BMMC_LAUNCH_PERSISTENT) {
+        if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
+            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
+                               dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out,
+                               *a.d);
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
         } else {
             return BMMC_ERR_UNSUPPORTED;
@@ -290,6 +321,11 @@ bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
         (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
          (uint64_t(2) << (2 * t + unit_log2)) > 131072))
         return false;
+    if (launch == BMMC_LAUNCH_STREAMED) {
+        // each role must be whole waves: 2t - (units per chunk, log2) >= 6
+        const int wl = (4 - unit_log2) < t ? (4 - unit_log2) : t;
+        if (2 * t - wl < 6) return false;
+    }
     return dispatch<0, 1, 0>(unit_log2, t, iters_log2, nullptr) == BMMC_OK;
 }
 

@@ -244,6 +244,8 @@ struct LaunchChoice {
     int grid_log2;   // persistent: log2 workgroups requested
     int walk;        // persistent: BMMC_WALK_RANGES or BMMC_WALK_INTERLEAVED
     int block_map;   // 1 identity, 2 reversed, >= 3 random invertible map (seed)
+    int depth;       // streamed: tiles of loads in flight per loader wave
+    bool auto_launch;  // launch style left to the planner
 };
 
 // Re-index the tiles: new block bit k selects the XOR of the old columns in
@@ -481,9 +483,18 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     d->chunk_log2 = g.wl;
     d->blk_bits = blk_bits;
     const u64 tile_bytes = u64(1) << (2 * t + ulog2);
-    if (lc.persistent && 2 * tile_bytes <= kMaxPersistentLdsBytes) {
+    int launch = lc.persistent;
+    // Planner's choice, measured on the benchmark workloads: below 2^14 tiles
+    // the streamed launch with loads two tiles ahead (the 64 MiB transpose:
+    // 0.914 of copy against 0.887 persistent); above, the persistent launch
+    // (bit-reversal n = 28: 0.865 against 0.78 streamed).
+    if (lc.auto_launch && launch) launch = blk_bits < 14 ? BMMC_LAUNCH_STREAMED
+                                                         : BMMC_LAUNCH_PERSISTENT;
+    // the streamed launch splits waves by role, so each role needs whole waves
+    if (launch == BMMC_LAUNCH_STREAMED && g.ntl < 6) launch = BMMC_LAUNCH_PERSISTENT;
+    if (launch && 2 * tile_bytes <= kMaxPersistentLdsBytes) {
         // persistent: two LDS tiles (double buffer), no staged iterations
-        d->launch = lc.persistent;
+        d->launch = launch;
         d->iters_log2 = 0;
         // One workgroup per compute unit (2^8 on a 256-CU MI355X) walking
         // long tile ranges measured best for large arrays; below 2^14 tiles
@@ -492,6 +503,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
                                       : (blk_bits >= 14 ? kDefaultGridLog2 : kDefaultGridLog2 + 1);
         d->grid_log2 = std::max(0, std::min(want, blk_bits));
         d->walk = lc.walk;
+        d->depth = launch == BMMC_LAUNCH_STREAMED ? lc.depth : 1;
         d->lds_bytes = (uint32_t)(2 * tile_bytes);
     } else {
         d->launch = BMMC_LAUNCH_ONE_TILE;
@@ -580,12 +592,15 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     if (o.walk < BMMC_WALK_AUTO || o.walk > BMMC_WALK_INTERLEAVED) return BMMC_ERR_INVALID_ARG;
     LaunchChoice lc;
     lc.iters_log2 = o.iters_log2;
+    lc.auto_launch = o.launch == BMMC_LAUNCH_AUTO;
     lc.persistent = o.launch >= BMMC_LAUNCH_PERSISTENT ? o.launch
                     : (o.launch == BMMC_LAUNCH_AUTO && o.iters_log2 == 0) ? BMMC_LAUNCH_PERSISTENT
                                                                           : 0;
     lc.grid_log2 = o.grid_log2;  // 0: chosen per pass from the tile count
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     if (o.block_map < 0) return BMMC_ERR_INVALID_ARG;
+    if (o.depth < 0 || o.depth > 2) return BMMC_ERR_INVALID_ARG;
+    lc.depth = o.depth ? o.depth : 2;
     lc.block_map = o.block_map ? o.block_map : 1;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;

@@ -94,6 +94,10 @@ for e in (1, 2, 4, 8, 16):
         SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=2)))
         SMALL.append((kind, 17, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=3,
                                         walk=bm.WALK_INTERLEAVED)))
+        for dp in (1, 2):
+            for g in (0, 5, 6):  # g = 5, 6: walks of 2 and 1 tiles (odd/short counts)
+                SMALL.append((kind, 16, e, dict(launch=bm.LAUNCH_STREAMED, depth=dp,
+                                                grid_log2=g)))
 for bmap in (2, 3, 99):
     SMALL.append(("general", 17, 4, dict(block_map=bmap)))
     SMALL.append(("bpc", 17, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
