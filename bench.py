@@ -245,6 +245,7 @@ def main():
     ap.add_argument("--walk", default="auto", choices=["auto", "ranges", "interleaved"])
     ap.add_argument("--block-map", type=int, default=0)
     ap.add_argument("--depth", type=int, default=0)
+    ap.add_argument("--cache-hint", type=int, default=0)
     ap.add_argument("--warm", action="store_true", help="reuse one buffer pair")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -307,7 +308,7 @@ def main():
                    no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
                    grid_log2=args.grid_log2,
                    walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
-                   block_map=args.block_map, depth=args.depth)
+                   block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
     plan_us = (time.perf_counter() - t0) * 1e6
     if name == "c4" and not args.kind and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2
@@ -350,7 +351,7 @@ def main():
                          no_swizzle=args.no_swizzle, iters_log2=args.iters_log2,
                          launch=launch, grid_log2=args.grid_log2,
                          walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
-                         block_map=args.block_map, depth=args.depth)
+                         block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
 
             def stepk(i, o, pk=pk):
                 st = bm.bmmc_execute(pk.handle, i, o, s_handle)

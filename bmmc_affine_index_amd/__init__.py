@@ -53,7 +53,8 @@ class bmmc_plan_options(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int), ("tile_log2", ctypes.c_int),
                 ("no_swizzle", ctypes.c_int), ("iters_log2", ctypes.c_int),
                 ("launch", ctypes.c_int), ("grid_log2", ctypes.c_int),
-                ("walk", ctypes.c_int), ("depth", ctypes.c_int), ("block_map", ctypes.c_int)]
+                ("walk", ctypes.c_int), ("depth", ctypes.c_int), ("cache_hint", ctypes.c_int),
+                ("block_map", ctypes.c_int)]
 
 
 class bmmc_plan_info(ctypes.Structure):
@@ -71,6 +72,7 @@ class bmmc_pass_desc(ctypes.Structure):
                 ("iters_log2", ctypes.c_int32), ("unit_xor", ctypes.c_int32),
                 ("launch", ctypes.c_int32), ("grid_log2", ctypes.c_int32),
                 ("walk", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("cache_hint", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("out_c", ctypes.c_uint64), ("lds_c", ctypes.c_uint32),
                 ("lds_bytes", ctypes.c_uint32),
                 ("in_blk", ctypes.c_uint64 * MAX_BITS), ("out_blk", ctypes.c_uint64 * MAX_BITS),
@@ -192,10 +194,10 @@ def bmmc_plan_create_ex(n: int, A: Sequence[int], c: int, elem_bytes: int,
                         route: int = ROUTE_AUTO, tile_log2: int = 0, no_swizzle: int = 0,
                         iters_log2: int = 0, launch: int = LAUNCH_AUTO,
                         grid_log2: int = 0, walk: int = WALK_AUTO, block_map: int = 0,
-                        depth: int = 0) -> int:
+                        depth: int = 0, cache_hint: int = 0) -> int:
     _, arr = _rows(A)
     opt = bmmc_plan_options(route, tile_log2, no_swizzle, iters_log2, launch, grid_log2, walk,
-                            depth, block_map)
+                            depth, cache_hint, block_map)
     return lib().bmmc_plan_create_ex(int(n), arr, int(c), int(elem_bytes),
                                      ctypes.byref(opt)) or 0
 
@@ -291,12 +293,13 @@ class Plan:
     def __init__(self, n: int, A: Sequence[int], c: int, elem_bytes: int,
                  route: int = ROUTE_AUTO, tile_log2: int = 0, no_swizzle: bool = False,
                  iters_log2: int = 0, launch: int = LAUNCH_AUTO, grid_log2: int = 0,
-                 walk: int = WALK_AUTO, block_map: int = 0, depth: int = 0):
+                 walk: int = WALK_AUTO, block_map: int = 0, depth: int = 0,
+                 cache_hint: int = 0):
         self.n, self.elem_bytes = int(n), int(elem_bytes)
         self.A, self.c = [int(a) for a in A], int(c)
         self.handle = bmmc_plan_create_ex(n, A, c, elem_bytes, route, tile_log2,
                                           int(bool(no_swizzle)), iters_log2, launch, grid_log2,
-                                          walk, block_map, depth)
+                                          walk, block_map, depth, cache_hint)
         if not self.handle:
             raise BmmcError(bmmc_last_error(), "bmmc_plan_create")
         self.info = bmmc_plan_get_info(self.handle)

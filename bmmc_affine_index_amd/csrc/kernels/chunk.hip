@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const uint64_t x = first + ((uint64_t)k << kChunkNTL) + tid;
-        if (x < nchunks) v[k] = dev::gload<CB>(in + x * CB);
+        if (x < nchunks) v[k] = dev::gload_hint<CB>(in + x * CB, d.cache_hint & 1);
     }
     const uint32_t ux = (uint32_t)d.unit_xor;
 #pragma unroll
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
             }
         }
         const uint64_t off = dev::xor_bits_uniform(d.out_blk, xu) ^ lane_off ^ d.out_c;
-        dev::gstore<CB>(out + off, c);
+        dev::gstore_hint<CB>(out + off, c, d.cache_hint & 2);
     }
 }
 

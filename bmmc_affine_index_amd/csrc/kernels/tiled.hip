@@ -65,7 +65,7 @@ __device__ __forceinline__ void load_tile(dev::Chunk<C::CB> (&v)[C::J], const ui
 #pragma unroll
     for (int j = 0; j < C::J; ++j) {
         const uint64_t in_j = in_base ^ dev::xor_bits_lane<C::JL>(d.ld_in + C::NTL, (uint32_t)j);
-        v[j] = dev::gload<C::CB>(in + (in_j ^ p.in_lane));
+        v[j] = dev::gload_hint<C::CB>(in + (in_j ^ p.in_lane), d.cache_hint & 1);
     }
 }
 
@@ -98,7 +98,7 @@ __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds
             const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.st_unit, (uint32_t)e);
             dev::put_unit<C::CB, C::U>(ch, e, dev::lds_load_unit<C::U>(tile_lds + (rd_j ^ rd_e)));
         }
-        dev::gstore<C::CB>(out + (out_j ^ p.out_lane), ch);
+        dev::gstore_hint<C::CB>(out + (out_j ^ p.out_lane), ch, d.cache_hint & 2);
     }
 }
 

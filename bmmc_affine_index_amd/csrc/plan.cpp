@@ -246,6 +246,7 @@ struct LaunchChoice {
     int block_map;   // 1 identity, 2 reversed, >= 3 random invertible map (seed)
     int depth;       // streamed: tiles of loads in flight per loader wave
     bool auto_launch;  // launch style left to the planner
+    int cache_hint;    // descriptor bits: 1 non-temporal loads, 2 non-temporal stores
 };
 
 // Re-index the tiles: new block bit k selects the XOR of the old columns in
@@ -538,6 +539,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         d->st_unit[b] = (uint32_t)(slot(Minv.apply(u64(1) << b), S) << ulog2);
     d->out_c = (c & ~lo_t) << ulog2;
     d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
+    d->cache_hint = lc.cache_hint;
     remap_blocks(d, lc.block_map);
     return BMMC_OK;
 }
@@ -556,6 +558,9 @@ void build_chunk(const Mat &A, u64 c, int ulog2, int wl, int kernel, bmmc_pass_d
     for (int k = 0; k < nb - wl; ++k) d->out_blk[k] = A.apply(u64(1) << (k + wl)) << ulog2;
     d->out_c = (c & ~low_mask(wl)) << ulog2;
     d->unit_xor = (int32_t)(c & low_mask(wl));
+    // whole chunks stream through with non-temporal hints; the naive pass's
+    // scattered one-unit stores measured far slower with them
+    d->cache_hint = kernel == BMMC_KERNEL_CHUNK ? 3 : 0;
 }
 
 void build_copy(int nb, int ulog2, bmmc_pass_desc *d) {
@@ -600,6 +605,10 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     if (o.block_map < 0) return BMMC_ERR_INVALID_ARG;
     if (o.depth < 0 || o.depth > 2) return BMMC_ERR_INVALID_ARG;
+    if (o.cache_hint < 0 || o.cache_hint > 4) return BMMC_ERR_INVALID_ARG;
+    // Planner's choice: non-temporal loads and stores (measured on the four
+    // large workloads: +1% to +5% over no hint; loads alone lose).
+    lc.cache_hint = o.cache_hint == 1 ? 0 : o.cache_hint == 2 ? 1 : o.cache_hint == 3 ? 2 : 3;
     lc.depth = o.depth ? o.depth : 2;
     lc.block_map = o.block_map ? o.block_map : 1;
     const int e = __builtin_ctzll((u64)elem_bytes);

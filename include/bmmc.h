@@ -78,6 +78,8 @@ typedef struct bmmc_plan_options {
     int walk;       /* persistent launch: BMMC_WALK_* order of tiles; 0 = planner's choice */
     int depth;      /* streamed launch: tiles of loads in flight per loader wave (1 or 2);
                        0 = planner's choice */
+    int cache_hint; /* tile pass: 0 = planner's choice, 1 = none, 2 = non-temporal loads,
+                       3 = non-temporal stores, 4 = both */
     int block_map;  /* re-indexing of the tiles: 0 = planner's choice, 1 = identity,
                        2 = reversed bit order, >= 3 = a random invertible F2 map seeded
                        with the value (the set of tiles is the same; only the order in
@@ -150,6 +152,8 @@ typedef struct bmmc_pass_desc {
     int32_t grid_log2;   /* persistent launch: 2^grid_log2 workgroups (TILED) */
     int32_t walk;        /* persistent launch: BMMC_WALK_RANGES or _INTERLEAVED (TILED) */
     int32_t depth;       /* streamed launch: tiles of loads in flight per loader wave, 1 or 2 */
+    int32_t cache_hint;  /* bit 0 non-temporal loads, bit 1 non-temporal stores */
+    int32_t reserved;
     uint64_t out_c;
     uint32_t lds_c;
     uint32_t lds_bytes;  /* LDS bytes per workgroup (TILED) */

@@ -98,6 +98,9 @@ for e in (1, 2, 4, 8, 16):
             for g in (0, 5, 6):  # g = 5, 6: walks of 2 and 1 tiles (odd/short counts)
                 SMALL.append((kind, 16, e, dict(launch=bm.LAUNCH_STREAMED, depth=dp,
                                                 grid_log2=g)))
+for hint in (2, 3, 4):
+    for e in (1, 4, 8, 16):
+        SMALL.append(("general", 17, e, dict(cache_hint=hint)))
 for bmap in (2, 3, 99):
     SMALL.append(("general", 17, 4, dict(block_map=bmap)))
     SMALL.append(("bpc", 17, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
@@ -139,14 +142,17 @@ def test_random_general_sweep(seed):
 
 def test_copy_ceiling_kernel():
     torch = _torch()
-    for nbytes in (0, 1, 15, 16, 4096 + 7, (1 << 20) + 48, 3 << 20):
-        src = torch.randint(0, 256, (max(nbytes, 1),), dtype=torch.uint8, device="cuda:0")
+    # both launch shapes (one-shot up to 4 MiB and above 64 MiB, grid-stride
+    # between), their edges, and ragged byte tails; each buffer has 64 spare
+    # bytes that must keep the sentinel
+    for nbytes in (0, 1, 15, 16, 4096 + 7, (1 << 20) + 48, 3 << 20, 4 << 20, (4 << 20) + 16,
+                   (17 << 20) + 5, 64 << 20, (64 << 20) + 16, (200 << 20) + 9):
+        src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda:0")
         dst = torch.full_like(src, SENTINEL)
         bm.copy(src, dst, nbytes)
         torch.cuda.synchronize()
-        assert torch.equal(src[:nbytes], dst[:nbytes])
-        if nbytes < src.numel():
-            assert int(dst[nbytes:].eq(SENTINEL).all()) == 1
+        assert torch.equal(src[:nbytes], dst[:nbytes]), nbytes
+        assert int(dst[nbytes:].eq(SENTINEL).all()) == 1, nbytes
 
 
 def test_two_pass_plan_reused_and_streams():
