@@ -42,7 +42,7 @@ MAX_CHUNK_BITS = 16
 MAX_PASSES = 2
 
 EXPORTED = (
-    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_copy",
+    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_plan_tune", "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
     "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_parm_matrix",
     "bmmc_matrix_inverse", "bmmc_tensor_permute_matrix",
@@ -72,7 +72,7 @@ class bmmc_pass_desc(ctypes.Structure):
                 ("iters_log2", ctypes.c_int32), ("unit_xor", ctypes.c_int32),
                 ("launch", ctypes.c_int32), ("grid_log2", ctypes.c_int32),
                 ("walk", ctypes.c_int32), ("depth", ctypes.c_int32),
-                ("cache_hint", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cache_hint", ctypes.c_int32), ("block_map", ctypes.c_int32),
                 ("out_c", ctypes.c_uint64), ("lds_c", ctypes.c_uint32),
                 ("lds_bytes", ctypes.c_uint32),
                 ("in_blk", ctypes.c_uint64 * MAX_BITS), ("out_blk", ctypes.c_uint64 * MAX_BITS),
@@ -117,6 +117,9 @@ def lib():
     L.bmmc_execute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p]
     L.bmmc_execute.restype = ctypes.c_int
+    L.bmmc_plan_tune.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int]
+    L.bmmc_plan_tune.restype = ctypes.c_int
     L.bmmc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.bmmc_copy.restype = ctypes.c_int
     L.bmmc_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -204,6 +207,10 @@ def bmmc_plan_create_ex(n: int, A: Sequence[int], c: int, elem_bytes: int,
 
 def bmmc_execute(plan: int, inp, out, stream=None) -> int:
     return lib().bmmc_execute(plan, _ptr(inp), _ptr(out), _stream(stream))
+
+
+def bmmc_plan_tune(plan: int, inp, out, stream=None, reps: int = 0) -> int:
+    return lib().bmmc_plan_tune(plan, _ptr(inp), _ptr(out), _stream(stream), int(reps))
 
 
 def bmmc_copy(inp, out, nbytes: int, stream=None) -> int:
@@ -315,6 +322,12 @@ class Plan:
         return [bmmc_plan_get_factor(self.handle, k, self.n) for k in range(self.info.passes)]
 
     def __call__(self, inp, out, stream=None) -> None:
+        self._check(inp, out)
+        st = bmmc_execute(self.handle, inp, out, stream)
+        if st != OK:
+            raise BmmcError(st, "bmmc_execute")
+
+    def _check(self, inp, out) -> None:
         for t in (inp, out):
             if hasattr(t, "is_cuda"):
                 if not t.is_cuda or not t.is_contiguous():
@@ -322,9 +335,15 @@ class Plan:
                 if t.numel() * t.element_size() != self.nbytes:
                     raise ValueError("tensor holds %d bytes, the plan moves %d"
                                      % (t.numel() * t.element_size(), self.nbytes))
-        st = bmmc_execute(self.handle, inp, out, stream)
+
+    def tune(self, inp, out, stream=None, reps: int = 0) -> None:
+        """Time the candidate tile orders on these buffers and keep the
+        fastest (bmmc_plan_tune); ``out`` then holds the permutation."""
+        self._check(inp, out)
+        st = bmmc_plan_tune(self.handle, inp, out, stream, reps)
         if st != OK:
-            raise BmmcError(st, "bmmc_execute")
+            raise BmmcError(st, "bmmc_plan_tune")
+        self.info = bmmc_plan_get_info(self.handle)
 
     def close(self) -> None:
         if getattr(self, "handle", 0):
@@ -347,12 +366,14 @@ class Plan:
                 if d.kernel == KERNEL_TILED and d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED)]
         depth = [d.depth for d in self.passes()
                  if d.kernel == KERNEL_TILED and d.launch == LAUNCH_STREAMED]
+        bmap = [d.block_map for d in self.passes() if d.kernel == KERNEL_TILED]
         return {"n": i.n, "elem_bytes": i.elem_bytes, "kind": KIND_NAMES[i.kind],
                 "route": ROUTE_NAMES[i.route], "passes": i.passes, "unit_bytes": i.unit_bytes,
                 "unit_bits": i.unit_bits, "tile_log2": i.tile_log2, "n_over": i.n_over,
                 "scratch_bytes": i.scratch_bytes, "kernels": launch,
                 "grid_log2": grid[0] if grid else None, "walk": walk[0] if walk else None,
-                "depth": depth[0] if depth else None}
+                "depth": depth[0] if depth else None,
+                "block_map": bmap[0] if bmap else None}
 
 
 def copy(inp, out, nbytes: Optional[int] = None, stream=None) -> None:

@@ -2,7 +2,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <memory>
 #include <new>
+#include <vector>
 
 #include "../../include/bmmc.h"
 #include "launch.h"
@@ -31,6 +33,59 @@ bool overlaps(const void *a, const void *b, size_t bytes) {
     return x < y + bytes && y < x + bytes;
 }
 
+size_t bytes_of(const bmmc_plan *p) { return (size_t)p->elem_bytes << p->n; }
+
+// Arguments of bmmc_execute and bmmc_plan_tune.
+int check_buffers(const bmmc_plan *p, const void *in, const void *out) {
+    if (!p || !in || !out) return BMMC_ERR_INVALID_ARG;
+    const size_t bytes = bytes_of(p);
+    const size_t align = bytes < 16 ? bytes : 16;
+    if (((uintptr_t)in % align) || ((uintptr_t)out % align)) return BMMC_ERR_INVALID_ARG;
+    if (overlaps(in, out, bytes)) return BMMC_ERR_ALIAS;
+    return BMMC_OK;
+}
+
+bool supported(const bmmc_plan &p) {
+    for (int k = 0; k < p.npasses; ++k) {
+        const bmmc_pass_desc &d = p.pass[k];
+        if (d.kernel == BMMC_KERNEL_TILED &&
+            !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2, d.launch))
+            return false;
+    }
+    return true;
+}
+
+// The scratch array of a two-pass plan: one array's bytes on the current
+// device, allocated on first use and kept until the plan is destroyed.
+int plan_scratch(const bmmc_plan *p, void **out) {
+    std::lock_guard<std::mutex> lock(p->scratch_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BMMC_ERR_HIP;
+    if (p->scratch && p->scratch_device != dev) {
+        (void)hipFree(p->scratch);
+        p->scratch = nullptr;
+    }
+    if (!p->scratch) {
+        if (hipMalloc(&p->scratch, bytes_of(p)) != hipSuccess) {
+            (void)hipGetLastError();
+            p->scratch = nullptr;
+            return BMMC_ERR_OUT_OF_MEMORY;
+        }
+        p->scratch_device = dev;
+    }
+    *out = p->scratch;
+    return BMMC_OK;
+}
+
+// One pass straight from `in` to `out`; two through `scratch`.
+int run_passes(const bmmc_pass_desc *pass, int npasses, const void *in, void *out,
+               void *scratch, hipStream_t s) {
+    if (npasses == 1) return run_pass(pass[0], in, out, s);
+    int st = run_pass(pass[0], in, scratch, s);
+    if (st != BMMC_OK) return st;
+    return run_pass(pass[1], scratch, out, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -43,14 +98,8 @@ bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem
         return nullptr;
     }
     int st = bmmc::build_plan(n, A, c, elem_bytes, opt, p);
-    if (st == BMMC_OK) {
-        for (int k = 0; k < p->npasses; ++k) {
-            const bmmc_pass_desc &d = p->pass[k];
-            if (d.kernel == BMMC_KERNEL_TILED &&
-                !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2, d.launch))
-                st = BMMC_ERR_UNSUPPORTED;
-        }
-    }
+    if (st == BMMC_OK && !supported(*p)) st = BMMC_ERR_UNSUPPORTED;
+    if (opt) p->opt = *opt;
     if (st != BMMC_OK) {
         delete p;
         g_last_error = st;
@@ -65,37 +114,107 @@ bmmc_plan *bmmc_plan_create(int n, const uint64_t *A, uint64_t c, size_t elem_by
 }
 
 int bmmc_execute(const bmmc_plan *p, const void *in, void *out, void *stream) {
-    if (!p || !in || !out) return BMMC_ERR_INVALID_ARG;
-    const size_t bytes = (size_t)p->elem_bytes << p->n;
-    const size_t align = bytes < 16 ? bytes : 16;
-    if (((uintptr_t)in % align) || ((uintptr_t)out % align)) return BMMC_ERR_INVALID_ARG;
-    if (overlaps(in, out, bytes)) return BMMC_ERR_ALIAS;
+    int st = check_buffers(p, in, out);
+    if (st != BMMC_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p->npasses == 1) return run_pass(p->pass[0], in, out, s);
-
     void *scratch = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(p->scratch_mu);
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return BMMC_ERR_HIP;
-        if (p->scratch && p->scratch_device != dev) {
-            (void)hipFree(p->scratch);
-            p->scratch = nullptr;
-        }
-        if (!p->scratch) {
-            if (hipMalloc(&p->scratch, bytes) != hipSuccess) {
-                (void)hipGetLastError();
-                p->scratch = nullptr;
-                return BMMC_ERR_OUT_OF_MEMORY;
-            }
-            p->scratch_device = dev;
-        }
-        scratch = p->scratch;
-    }
-    if (overlaps(in, scratch, bytes) || overlaps(out, scratch, bytes)) return BMMC_ERR_ALIAS;
-    int st = run_pass(p->pass[0], in, scratch, s);
+    st = plan_scratch(p, &scratch);
     if (st != BMMC_OK) return st;
-    return run_pass(p->pass[1], scratch, out, s);
+    if (overlaps(in, scratch, bytes_of(p)) || overlaps(out, scratch, bytes_of(p)))
+        return BMMC_ERR_ALIAS;
+    return run_passes(p->pass, p->npasses, in, out, scratch, s);
+}
+
+int bmmc_plan_tune(bmmc_plan *p, const void *in, void *out, void *stream, int reps) {
+    int st = check_buffers(p, in, out);
+    if (st != BMMC_OK) return st;
+    if (reps < 0 || reps > 1000) return BMMC_ERR_INVALID_ARG;
+    if (reps == 0) reps = 3;
+    bool tiled = false;
+    for (int k = 0; k < p->npasses; ++k) tiled |= p->pass[k].kernel == BMMC_KERNEL_TILED;
+    if (!tiled) {  // nothing to choose: run it once, so that `out` holds the result
+        st = bmmc_execute(p, in, out, stream);
+        if (st == BMMC_OK && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+            st = BMMC_ERR_HIP;
+        return st;
+    }
+
+    // candidates: (launch style, block order), keeping what the caller fixed
+    std::vector<int> launches, maps;
+    if (p->opt.launch) launches = {p->opt.launch};
+    else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
+    if (p->opt.block_map) maps = {p->opt.block_map};
+    else maps = {1, 3, 5, 6};
+    std::vector<std::unique_ptr<bmmc_plan>> cand;
+    for (int l : launches)
+        for (int m : maps) {
+            bmmc_plan_options o = p->opt;
+            o.launch = l;
+            o.block_map = m;
+            std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
+            if (!q) return BMMC_ERR_OUT_OF_MEMORY;
+            if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) !=
+                    BMMC_OK ||
+                !supported(*q))
+                continue;
+            bool dup = false;  // same tables as an earlier candidate
+            for (const auto &r : cand)
+                dup |= r->npasses == q->npasses &&
+                       std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
+            if (!dup) cand.push_back(std::move(q));
+        }
+    if (cand.empty()) return BMMC_ERR_UNSUPPORTED;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *scratch = nullptr;
+    bool two = false;
+    for (const auto &q : cand) two |= q->npasses > 1;
+    if (two) {
+        st = plan_scratch(p, &scratch);
+        if (st != BMMC_OK) return st;
+        if (overlaps(in, scratch, bytes_of(p)) || overlaps(out, scratch, bytes_of(p)))
+            return BMMC_ERR_ALIAS;
+    }
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        (void)hipGetLastError();
+        return BMMC_ERR_HIP;
+    }
+    std::vector<float> best(cand.size(), 1e30f);
+    st = BMMC_OK;
+    for (int round = 0; round < 2 && st == BMMC_OK; ++round)
+        for (size_t i = 0; i < cand.size() && st == BMMC_OK; ++i) {
+            const bmmc_plan &q = *cand[i];
+            st = run_passes(q.pass, q.npasses, in, out, scratch, s);  // warm-up
+            if (st == BMMC_OK && hipEventRecord(e0, s) != hipSuccess) st = BMMC_ERR_HIP;
+            for (int r = 0; r < reps && st == BMMC_OK; ++r)
+                st = run_passes(q.pass, q.npasses, in, out, scratch, s);
+            float ms = 0.f;
+            if (st == BMMC_OK &&
+                (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                st = BMMC_ERR_HIP;
+            if (st == BMMC_OK && ms < best[i]) best[i] = ms;
+        }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != BMMC_OK) {
+        (void)hipGetLastError();
+        return st;
+    }
+    size_t w = 0;
+    for (size_t i = 1; i < cand.size(); ++i)
+        if (best[i] < best[w]) w = i;
+    const bmmc_plan &q = *cand[w];
+    p->info = q.info;
+    p->npasses = q.npasses;
+    std::memcpy(p->pass, q.pass, sizeof(p->pass));
+    std::memcpy(p->factor_A, q.factor_A, sizeof(p->factor_A));
+    std::memcpy(p->factor_c, q.factor_c, sizeof(p->factor_c));
+    // `out` holds the last candidate's result, which is the same permutation
+    return BMMC_OK;
 }
 
 int bmmc_copy(const void *in, void *out, size_t nbytes, void *stream) {

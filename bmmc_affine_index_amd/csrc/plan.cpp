@@ -243,18 +243,23 @@ struct LaunchChoice {
     int persistent;  // BMMC_LAUNCH_PERSISTENT or _STREAMED; 0: one-tile launch
     int grid_log2;   // persistent: log2 workgroups requested
     int walk;        // persistent: BMMC_WALK_RANGES or BMMC_WALK_INTERLEAVED
-    int block_map;   // 1 identity, 2 reversed, >= 3 random invertible map (seed)
+    int block_map;   // 1 identity, 2 reversed, 3-5 locality orders, >= 8 random (seed)
     int depth;       // streamed: tiles of loads in flight per loader wave
     bool auto_launch;  // launch style left to the planner
     int cache_hint;    // descriptor bits: 1 non-temporal loads, 2 non-temporal stores
 };
 
+// Highest set bit of a byte offset (-1 for 0).
+int top_bit(u64 v) { return v ? 63 - __builtin_clzll(v) : -1; }
+
 // Re-index the tiles: new block bit k selects the XOR of the old columns in
 // column k of an invertible map L.  The three block tables are linear in the
 // block index, so they are transformed alike and the set of tiles is unchanged.
+// Modes 2 (reversed bit order) and >= 8 (a seeded random L); the locality
+// orders 3-7 are built into the block basis itself (block_basis).
 void remap_blocks(bmmc_pass_desc *d, int mode) {
     const int nbk = d->blk_bits;
-    if (mode <= 1 || nbk < 2) return;
+    if ((mode != 2 && mode < 8) || nbk < 2) return;
     std::vector<u64> cols(nbk);
     if (mode == 2) {
         for (int k = 0; k < nbk; ++k) cols[k] = u64(1) << (nbk - 1 - k);
@@ -283,6 +288,65 @@ void remap_blocks(bmmc_pass_desc *d, int mode) {
         d->out_blk[k] = out2[k];
         d->lds_blk[k] = lds2[k];
     }
+}
+
+// Block basis of a tile pass: input vectors x_0 .. x_{m-1}, independent
+// modulo the tile space V, such that block index b names the tile
+// (XOR of x_k over the set bits k of b) + V.  Any such basis tiles the array;
+// the choice only decides which tiles are in flight together.
+//
+// Mode 1 takes the input coordinates that are no pivot of V (the identity
+// order).  Modes 3-7 draw from two candidate lists, each sorted nearest first
+// by the top bit of the candidate's representative reduced modulo the tile's
+// own span on that side: input-aligned vectors e_r (near on the input side)
+// and output-aligned vectors B e_r (A x = e_r, near on the output side).  For
+// a bit-permute-complement matrix the two lists hold the same vectors.  The
+// tiles in flight together differ in the `conc` concurrent block bits (the
+// top grid_log2 bits of a range walk, whose workgroups start far apart and
+// move in step) or in the low bits (one-tile launches and the interleaved
+// walk, conc = 0); picks go to the concurrent bits first, then to the other
+// bits from bit 0 up:
+//   3: alternately input- and output-nearest, 4: input-nearest,
+//   5: output-nearest, 6: output-nearest for the concurrent bits and then
+//   input-nearest, 7: the reverse of 6.
+std::vector<u64> block_basis(const Mat &A, const Mat &B, int t, const Basis &vb,
+                             const Basis &avb, const std::vector<int> &R, int mode, int conc) {
+    const int nb = A.rows, m = (int)R.size();
+    std::vector<u64> X(m);
+    if (mode < 3 || mode > 7) {
+        for (int k = 0; k < m; ++k) X[k] = u64(1) << R[k];
+        return X;
+    }
+    struct Cand { int key; u64 x; };
+    std::vector<Cand> near[2];
+    for (int r = t; r < nb; ++r) {
+        near[0].push_back({top_bit(vb.reduce(u64(1) << r)), u64(1) << r});
+        near[1].push_back({top_bit(avb.reduce(u64(1) << r)), B.apply(u64(1) << r)});
+    }
+    for (auto &v : near)
+        std::stable_sort(v.begin(), v.end(), [](const Cand &a, const Cand &b) { return a.key < b.key; });
+    Basis acc = vb;
+    size_t pos[2] = {0, 0};
+    for (int i = 0; i < m; ++i) {
+        int side;
+        switch (mode) {
+        case 3: side = i & 1; break;
+        case 4: side = 0; break;
+        case 5: side = 1; break;
+        case 6: side = i < conc ? 1 : 0; break;
+        default: side = i < conc ? 0 : 1; break;
+        }
+        // next independent candidate of that side; the other side if it has none
+        u64 x = 0;
+        for (int tries = 0; tries < 2 && !x; ++tries, side ^= 1)
+            for (; pos[side] < near[side].size() && !x; ++pos[side])
+                if (acc.add(near[side][pos[side]].x)) x = near[side][pos[side]].x;
+        // stored reduced modulo V: only non-pivot coordinates >= t remain, so
+        // the tile's input rows start on row boundaries
+        const int k = i < conc ? m - conc + i : i - conc;
+        X[k] = vb.reduce(x);
+    }
+    return X;
 }
 
 int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W,
@@ -511,9 +575,23 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         d->iters_log2 = iters_log2;
         d->lds_bytes = (uint32_t)(tile_bytes << iters_log2);
     }
+    Basis vb, avb;  // the tile's span on the input side and on the output side
+    for (int j = 0; j < t; ++j) {
+        vb.add(u64(1) << j);
+        avb.add(u64(1) << j);
+    }
+    for (int k = 0; k < t; ++k) {
+        vb.add(W[k]);
+        avb.add(gb.vec[k]);
+    }
+    Mat Binv;
+    if (!inverse(A, Binv)) return BMMC_ERR_SINGULAR;
+    const bool range_walk = d->launch != BMMC_LAUNCH_ONE_TILE && d->walk == BMMC_WALK_RANGES;
+    const std::vector<u64> X =
+        block_basis(A, Binv, t, vb, avb, R, lc.block_map, range_walk ? d->grid_log2 : 0);
     for (int k = 0; k < blk_bits; ++k) {
-        u64 x = u64(1) << R[k];
-        u64 z = A.apply(x);
+        const u64 x = X[k];
+        const u64 z = A.apply(x);
         d->in_blk[k] = x << ulog2;
         d->out_blk[k] = (z & ~lo_t) << ulog2;
         d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_t), S) << ulog2);
@@ -540,6 +618,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     d->out_c = (c & ~lo_t) << ulog2;
     d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
     d->cache_hint = lc.cache_hint;
+    d->block_map = lc.block_map;
     remap_blocks(d, lc.block_map);
     return BMMC_OK;
 }

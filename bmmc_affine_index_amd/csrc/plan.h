@@ -13,6 +13,7 @@ struct bmmc_plan {
     int elem_bytes = 0;
     uint64_t A[BMMC_MAX_N] = {};
     uint64_t c = 0;
+    bmmc_plan_options opt = {};  // as the caller gave them (0 = planner's choice)
     bmmc_plan_info info = {};
     int npasses = 0;
     bmmc_pass_desc pass[BMMC_MAX_PASSES] = {};

@@ -81,9 +81,14 @@ typedef struct bmmc_plan_options {
     int cache_hint; /* tile pass: 0 = planner's choice, 1 = none, 2 = non-temporal loads,
                        3 = non-temporal stores, 4 = both */
     int block_map;  /* re-indexing of the tiles: 0 = planner's choice, 1 = identity,
-                       2 = reversed bit order, >= 3 = a random invertible F2 map seeded
-                       with the value (the set of tiles is the same; only the order in
-                       which workgroups meet them changes) */
+                       2 = reversed bit order, 3 = tiles in flight together form a
+                       patch dense on both the input and the output side, 4 = dense on
+                       the input side, 5 = dense on the output side, 6 = (range walk)
+                       workgroups in step are dense on the output side and each
+                       workgroup's successive tiles on the input side, 7 = the reverse
+                       of 6, >= 8 = a random invertible F2 map seeded with the value
+                       (the set of tiles is the same; only the order in which
+                       workgroups meet them changes) */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */
@@ -153,7 +158,7 @@ typedef struct bmmc_pass_desc {
     int32_t walk;        /* persistent launch: BMMC_WALK_RANGES or _INTERLEAVED (TILED) */
     int32_t depth;       /* streamed launch: tiles of loads in flight per loader wave, 1 or 2 */
     int32_t cache_hint;  /* bit 0 non-temporal loads, bit 1 non-temporal stores */
-    int32_t reserved;
+    int32_t block_map;   /* tile order the tables were built with (TILED; 0 otherwise) */
     uint64_t out_c;
     uint32_t lds_c;
     uint32_t lds_bytes;  /* LDS bytes per workgroup (TILED) */
@@ -167,7 +172,7 @@ typedef struct bmmc_pass_desc {
     uint32_t st_unit[4];
 } bmmc_pass_desc;
 
-typedef struct bmmc_plan bmmc_plan; /* opaque; immutable after creation */
+typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */
 
 /* Plan the permutation out[A.i XOR c] = in[i] of 2^n elements of elem_bytes
  * bytes.  Host-only: validates (1 <= n <= 32, elem_bytes in {1,2,4,8,16},
@@ -194,6 +199,23 @@ bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem
  * Launch failures return BMMC_ERR_HIP; faults inside a kernel surface at the
  * caller's next synchronisation, as HIP reports them. */
 int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream);
+
+/* Measure and keep the fastest tile order for this plan on this device.
+ * Which tiles run together decides how well the DRAM pages of HBM are reused,
+ * and the best order depends on the matrix ("Efficient GPU Implementation of
+ * Affine Index Permutations on Arrays", limitations: on the AMD card the
+ * running time varied with the permutation).  Every candidate computes the
+ * same permutation; they differ in the launch style (the planner's persistent
+ * or streamed walk, or one workgroup per tile) and the block order
+ * (bmmc_plan_options.block_map 1, 3, 5 and 6).  An option the caller fixed at
+ * plan creation is kept.  Each candidate runs `reps` times (0 = 3) on
+ * `stream` with `in` and `out` (the same requirements as bmmc_execute), twice
+ * over, timed with HIP events; the fastest replaces the plan's kernel tables.
+ * On return `out` holds the permutation of `in`.  Blocks the host until the
+ * stream has drained; the plan must not be executed concurrently.  A plan
+ * with no tile pass has nothing to choose and is run once.  Errors as
+ * bmmc_execute; on any error the plan is unchanged. */
+int bmmc_plan_tune(bmmc_plan *plan, const void *in, void *out, void *stream, int reps);
 
 /* The ceiling: copy nbytes from `in` to `out` (device pointers, no overlap)
  * with the same vector width and launch style as the permutation kernels,

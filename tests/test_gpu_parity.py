@@ -101,9 +101,13 @@ for e in (1, 2, 4, 8, 16):
 for hint in (2, 3, 4):
     for e in (1, 4, 8, 16):
         SMALL.append(("general", 17, e, dict(cache_hint=hint)))
-for bmap in (2, 3, 99):
+for bmap in (2, 3, 4, 5, 99):
     SMALL.append(("general", 17, 4, dict(block_map=bmap)))
     SMALL.append(("bpc", 17, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
+for bmap in (3, 5, 6, 7):
+    SMALL.append(("bitrev", 18, 4, dict(block_map=bmap, launch=bm.LAUNCH_PERSISTENT, grid_log2=3)))
+    SMALL.append(("general", 18, 8, dict(block_map=bmap, launch=bm.LAUNCH_STREAMED,
+                                         walk=bm.WALK_INTERLEAVED, grid_log2=2)))
 for e in (1, 4, 16):
     for kind in ("general", "bpc"):
         SMALL.append((kind, 16, e, dict(launch=bm.LAUNCH_ONE_TILE)))
@@ -180,17 +184,68 @@ def test_execute_rejects_alias_on_device():
     assert bm.bmmc_execute(P.handle, buf, buf[100:], None) == bm.ERR_ALIAS
 
 
+TUNE_CASES = [("general", 17, 4, {}), ("bpc", 18, 16, {}), ("bitrev", 16, 1, {}),
+              ("transpose", 18, 8, {}), ("general", 15, 2, dict(route=bm.ROUTE_TWO_PASS)),
+              ("general", 17, 4, dict(launch=bm.LAUNCH_ONE_TILE)),
+              ("bpc", 17, 4, dict(block_map=7)), ("general", 12, 4, dict(iters_log2=1)),
+              ("complement", 14, 4, {}), ("identity", 14, 4, {})]
+
+
+@pytest.mark.parametrize("case", TUNE_CASES, ids=lambda c: "%s-n%d-e%d-%s" % (
+    c[0], c[1], c[2], "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
+def test_tune_keeps_results_and_fixed_options(case):
+    torch = _torch()
+    kind, n, e, kw = case
+    A, c = _matrix(kind, n, 9100 + n + e)
+    x = wl.fill_random_bytes(n, e, seed=17 * n + e)
+    want = oracle.apply(A, c, x)
+    P = bm.Plan(n, A, c, e, **kw)
+    before = [(d.kernel, d.launch, d.block_map) for d in P.passes()]
+    raw = np.ascontiguousarray(x).view(np.uint8).reshape(-1)
+    d_in = torch.from_numpy(raw.copy()).to("cuda:0")
+    d_out = torch.full_like(d_in, SENTINEL)
+    P.tune(d_in, d_out, reps=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_out.cpu().numpy().view(x.dtype).reshape(x.shape), want)
+    for rep in range(2):
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        torch.cuda.synchronize()
+        got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
+        assert np.array_equal(got, want), (rep, P.describe())
+    after = P.passes()
+    assert [d.kernel for d in after] == [b[0] for b in before]
+    for d in after:
+        if d.kernel == bm.KERNEL_TILED:
+            if "launch" in kw:
+                assert d.launch == kw["launch"]
+            if "block_map" in kw:
+                assert d.block_map == kw["block_map"]
+            else:
+                assert d.block_map in (1, 3, 5, 6)
+        else:
+            assert (d.kernel, d.launch, d.block_map) in before
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------
 
-def _device_run(name, A, c, x, **plan_kw):
+def _device_run(name, A, c, x, tune=False, **plan_kw):
+    """Run a workload's plan; with tune=True the plan is first tuned on the
+    same buffers (as the benchmark does), then run again into a fresh
+    sentinel-filled output."""
     torch = _torch()
     n = wl.WORKLOADS[name].n
     raw = x.reshape(-1).view(np.uint8)
     P = bm.Plan(n, A, c, raw.size >> n, **plan_kw)
     d_in = torch.from_numpy(raw).to("cuda:0")
     d_out = torch.full_like(d_in, SENTINEL)
+    if tune:
+        P.tune(d_in, d_out)
+        torch.cuda.synchronize()
+        _note("%s tuned: %s" % (name, P.describe()))
+        d_out.fill_(SENTINEL)
     P(d_in, d_out)
     torch.cuda.synchronize()
     got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
@@ -225,7 +280,7 @@ def test_workload_full_check(name):
         assert np.array_equal(A, wl.workload_matrix(name, accept=_lib_accepts(n))[0])
     x = wl.workload_data(name)
     want = oracle.apply(A, c, x, threads=HOST_THREADS)
-    routes = [{}] + ([dict(route=bm.ROUTE_TWO_PASS)] if name == "c1a" else [])
+    routes = [{}, dict(tune=True)] + ([dict(route=bm.ROUTE_TWO_PASS)] if name == "c1a" else [])
     for kw in routes:
         _note("%s %s" % (name, kw))
         got, P = _device_run(name, A, c, x, **kw)
@@ -242,10 +297,12 @@ def test_workload_c3_bitrev28_full():
     x = wl.workload_data(name)
     _note("c3: oracle")
     want = oracle.apply(A, c, x, threads=HOST_THREADS)
-    _note("c3: gpu")
-    got, P = _device_run(name, A, c, x)
-    assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
-    assert np.array_equal(got, want), P.describe()
+    for tune in (False, True):
+        _note("c3: gpu tune=%s" % tune)
+        got, P = _device_run(name, A, c, x, tune=tune)
+        assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
+        assert np.array_equal(got, want), P.describe()
+        del got
 
 
 def test_workload_c4_general30():
@@ -255,7 +312,7 @@ def test_workload_c4_general30():
     x = wl.workload_data(name)
     _note("c4: oracle")
     want = oracle.apply(A, c, x, threads=HOST_THREADS)
-    for kw in ({}, dict(route=bm.ROUTE_TWO_PASS)):
+    for kw in ({}, dict(tune=True), dict(route=bm.ROUTE_TWO_PASS)):
         _note("c4 %s" % kw)
         got, P = _device_run(name, A, c, x, **kw)
         assert P.info.kind == bm.KIND_GENERAL
@@ -263,6 +320,30 @@ def test_workload_c4_general30():
         assert bad == 0, (first, P.describe())
         assert np.array_equal(got, want), P.describe()
         del got
+
+
+def test_workload_c4_every_tuning_candidate():
+    """Each (launch, block order) pair that bmmc_plan_tune chooses among, at
+    the full n = 30 size, on sampled indices."""
+    torch = _torch()
+    name = "c4"
+    n = 30
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == n)
+    x = wl.workload_data(name)
+    d_in = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    d_out = torch.empty_like(d_in)
+    idx = _sample_idx(n, 1 << 18, 31)
+    for launch in (bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE):
+        for bmap in (1, 3, 5, 6):
+            _note("c4 launch=%d block_map=%d" % (launch, bmap))
+            P = bm.Plan(n, A, c, 4, launch=launch, block_map=bmap)
+            d_out.fill_(SENTINEL)
+            P(d_in, d_out)
+            torch.cuda.synchronize()
+            got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
+            bad, first = oracle.check_sampled(A, c, x, got, idx)
+            assert bad == 0, (launch, bmap, first, P.describe())
+            del got
 
 
 def test_workload_c5_random_bpc_records():
@@ -277,6 +358,7 @@ def test_workload_c5_random_bpc_records():
         _note("c5 perm %d" % k)
         P = bm.Plan(n, A, c, 16)
         assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
+        P.tune(d_in, d_out)  # the benchmark tunes each permutation's plan
         d_out.fill_(SENTINEL)
         P(d_in, d_out)
         torch.cuda.synchronize()

@@ -108,6 +108,26 @@ def test_execute_argument_errors_without_gpu():
             bm.bmmc_plan_get_pass(p.handle, k)
 
 
+def test_tune_argument_errors_without_gpu():
+    """bmmc_plan_tune validates before any HIP call: the same buffer rules as
+    bmmc_execute and reps in [0, 1000] (these fake addresses are never
+    touched)."""
+    p = bm.Plan(10, wl.bit_reverse_matrix(10), 0, 4)
+    assert bm.bmmc_plan_tune(0, 4096, 8192) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune(p.handle, 0, 4096) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune(p.handle, 1 << 20 | 4, 1 << 24) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune(p.handle, 1 << 20, (1 << 20) + 2048) == bm.ERR_ALIAS
+    assert bm.bmmc_plan_tune(p.handle, 1 << 20, 1 << 24, None, -1) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune(p.handle, 1 << 20, 1 << 24, None, 1001) == bm.ERR_INVALID_ARG
+
+
+def test_pass_records_block_order():
+    A, c = wl.random_bmmc(16, 5, lambda r: oracle.rank(r) == 16)
+    for bmap in (0, 1, 3, 5, 6, 7, 2, 9):
+        d = bm.Plan(16, A, c, 4, block_map=bmap).passes()[0]
+        assert d.kernel == bm.KERNEL_TILED and d.block_map == (bmap or 1)
+
+
 def test_destroy_null_is_safe():
     bm.bmmc_plan_destroy(0)
 
@@ -270,9 +290,14 @@ def _cases():
     for e in (1, 4, 16):
         cases.append(("general", 15, e, dict(launch=bm.LAUNCH_STREAMED, grid_log2=2)))
         cases.append(("bpc", 16, e, dict(launch=bm.LAUNCH_STREAMED, walk=bm.WALK_INTERLEAVED)))
-    for bmap in (2, 3, 17):
+    for bmap in (2, 3, 4, 5, 17):
         cases.append(("general", 16, 4, dict(block_map=bmap)))
         cases.append(("bitrev", 16, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
+    for bmap in (3, 4, 5, 6, 7):
+        cases.append(("bitrev", 17, 4, dict(block_map=bmap, launch=bm.LAUNCH_PERSISTENT,
+                                            grid_log2=3)))
+        cases.append(("general", 17, 8, dict(block_map=bmap, launch=bm.LAUNCH_STREAMED,
+                                             walk=bm.WALK_INTERLEAVED, grid_log2=2)))
     cases.append(("general", 14, 4, dict(no_swizzle=1)))
     cases.append(("general", 5, 4, dict()))
     cases.append(("general", 2, 4, dict()))
@@ -363,3 +388,70 @@ def test_swizzle_makes_reads_conflict_free(kind, n, e):
         P0 = bm.Plan(n, A, c, e, no_swizzle=1)
         r0 = tiled_read_addresses(P0.passes()[0])
         assert bank_cycles(r0, U, 64) > bank_cycles(ra, U, 64)
+
+
+def _top_bits(tab, k):
+    return [int(v).bit_length() - 1 for v in tab[:k]]
+
+
+def _reduced_out_top_bits(d, unit_log2):
+    """Top bits of the output block offsets reduced modulo the tile's output
+    span (the in-segment bits and the segment vectors in st_out): what a block
+    bit moves the tile's set of output segments by."""
+    basis = []  # (pivot, vector), fully reduced
+    def reduce(v):
+        for p, b in basis:
+            if (v >> p) & 1:
+                v ^= b
+        return v
+    def add(v):
+        v = reduce(v)
+        if v:
+            p = v.bit_length() - 1
+            for i, (q, b) in enumerate(basis):
+                if (b >> p) & 1:
+                    basis[i] = (q, b ^ v)
+            basis.append((p, v))
+    for b in range(unit_log2 + d.t):
+        add(1 << b)
+    for v in d.st_out:
+        add(int(v))
+    return [reduce(int(v)).bit_length() - 1 for v in d.out_blk[:d.blk_bits]]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_locality_block_orders(seed):
+    """Block orders 3-7 draw block vectors nearest first on the input side
+    (input-aligned) or the output side (output-aligned); the tiles stay a
+    partition of the array, which the replay tests check."""
+    n, e = 22, 4
+    A, c = wl.random_bmmc(n, seed, lambda r: oracle.rank(r) == n)
+
+    def desc(mode, launch):
+        P = bm.Plan(n, A, c, e, launch=launch, block_map=mode)
+        return bm.bmmc_plan_get_pass(P.handle, 0)
+
+    d4 = desc(4, bm.LAUNCH_ONE_TILE)
+    d5 = desc(5, bm.LAUNCH_ONE_TILE)
+    m = d4.blk_bits
+    ins = _top_bits(d4.in_blk, m)
+    outs = _reduced_out_top_bits(d5, 2)
+    assert ins == sorted(ins) and len(set(ins)) == m
+    assert outs == sorted(outs) and len(set(outs)) == m
+    # output-aligned vectors move the output by single bits above the segment
+    assert outs[0] >= 2 + d5.t and outs[-1] <= 2 + n - 1
+    d3 = desc(3, bm.LAUNCH_ONE_TILE)
+    # alternating picks; a candidate already spanned by earlier picks is skipped
+    even = _top_bits(d3.in_blk, m)[0::2]
+    odd = _reduced_out_top_bits(d3, 2)[1::2]
+    assert even[0] == ins[0] and even == sorted(even) and set(even) <= set(ins)
+    assert odd[0] == outs[0] and odd == sorted(odd) and set(odd) <= set(outs)
+    # range walk: the concurrent (top grid_log2) bits take the output side
+    d6 = desc(6, bm.LAUNCH_PERSISTENT)
+    g = d6.grid_log2
+    assert 0 < g < m
+    assert _reduced_out_top_bits(d6, 2)[m - g:] == outs[:g]
+    # the other bits take input-aligned vectors, nearest first, skipping any
+    # that the concurrent picks already span
+    low = _top_bits(d6.in_blk, m)[:m - g]
+    assert low == sorted(low) and set(low) <= set(ins)
