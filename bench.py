@@ -150,7 +150,8 @@ ABLATION_VARIANTS = [
     ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True)),
     ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE)),
     ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
-    ("persistent (default)", dict()),
+    ("planner, untuned", dict()),
+    ("tuned (default)", dict(tune=True)),
 ]
 
 
@@ -184,10 +185,14 @@ def run_ablation(args, torch):
             if kind == "random_bmmc":
                 variants = [variants[0]] + [
                     (nm + " two-pass", dict(kw, route=bm.ROUTE_TWO_PASS)) for nm, kw in variants[1:4]
-                ] + [("persistent two-pass", dict(route=bm.ROUTE_TWO_PASS)), variants[4]]
+                ] + [("persistent two-pass", dict(route=bm.ROUTE_TWO_PASS))] + variants[4:]
             base = None
             for vname, kw in variants:
+                kw = dict(kw)
+                tune = kw.pop("tune", False)
                 plan = bm.Plan(n, A, c, elem, **kw)
+                if tune:
+                    plan.tune(pairs=bufs, stream=s_handle)
 
                 def step(i, o, plan=plan):
                     st = bm.bmmc_execute(plan.handle, i, o, s_handle)
@@ -323,12 +328,13 @@ def main():
     stream = torch.cuda.current_stream()
     s_handle = int(stream.cuda_stream)
 
-    # bmmc_plan_tune: time the candidate tile orders on one buffer pair and
-    # keep the fastest (outside the timed region, like plan creation)
+    # bmmc_plan_tune_pairs: time the candidate tile orders over the same
+    # rotating buffer pairs and keep the fastest (outside the timed region,
+    # like plan creation)
     tune_ms = None
     if not args.no_tune:
         t0 = time.perf_counter()
-        plan.tune(*bufs[-1], stream=s_handle)
+        plan.tune(pairs=bufs, stream=s_handle)
         tune_ms = (time.perf_counter() - t0) * 1e3
 
     def step(i, o):
@@ -363,7 +369,7 @@ def main():
                          walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
                          block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
             if not args.no_tune:
-                pk.tune(*bufs[-1], stream=s_handle)
+                pk.tune(pairs=bufs, stream=s_handle)
 
             def stepk(i, o, pk=pk):
                 st = bm.bmmc_execute(pk.handle, i, o, s_handle)

@@ -42,7 +42,8 @@ MAX_CHUNK_BITS = 16
 MAX_PASSES = 2
 
 EXPORTED = (
-    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_plan_tune", "bmmc_copy",
+    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_plan_tune", "bmmc_plan_tune_pairs",
+    "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
     "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_parm_matrix",
     "bmmc_matrix_inverse", "bmmc_tensor_permute_matrix",
@@ -120,6 +121,10 @@ def lib():
     L.bmmc_plan_tune.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int]
     L.bmmc_plan_tune.restype = ctypes.c_int
+    L.bmmc_plan_tune_pairs.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int]
+    L.bmmc_plan_tune_pairs.restype = ctypes.c_int
     L.bmmc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.bmmc_copy.restype = ctypes.c_int
     L.bmmc_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -211,6 +216,16 @@ def bmmc_execute(plan: int, inp, out, stream=None) -> int:
 
 def bmmc_plan_tune(plan: int, inp, out, stream=None, reps: int = 0) -> int:
     return lib().bmmc_plan_tune(plan, _ptr(inp), _ptr(out), _stream(stream), int(reps))
+
+
+def bmmc_plan_tune_pairs(plan: int, pairs, stream=None, reps: int = 0) -> int:
+    """pairs: a sequence of (input, output) device buffers (tensors or
+    addresses)."""
+    k = len(pairs)
+    ins = (ctypes.c_void_p * max(k, 1))(*[_ptr(i) for i, _ in pairs])
+    outs = (ctypes.c_void_p * max(k, 1))(*[_ptr(o) for _, o in pairs])
+    return lib().bmmc_plan_tune_pairs(plan, ins if k else None, outs if k else None, k,
+                                      _stream(stream), int(reps))
 
 
 def bmmc_copy(inp, out, nbytes: int, stream=None) -> int:
@@ -336,13 +351,17 @@ class Plan:
                     raise ValueError("tensor holds %d bytes, the plan moves %d"
                                      % (t.numel() * t.element_size(), self.nbytes))
 
-    def tune(self, inp, out, stream=None, reps: int = 0) -> None:
-        """Time the candidate tile orders on these buffers and keep the
-        fastest (bmmc_plan_tune); ``out`` then holds the permutation."""
-        self._check(inp, out)
-        st = bmmc_plan_tune(self.handle, inp, out, stream, reps)
+    def tune(self, inp=None, out=None, stream=None, reps: int = 0, pairs=None) -> None:
+        """Time the candidate tile orders and keep the fastest
+        (bmmc_plan_tune_pairs), rotating over ``pairs`` [(in, out), ...] or
+        the one pair (inp, out); the first output then holds the permutation
+        of the first input."""
+        pairs = list(pairs) if pairs is not None else [(inp, out)]
+        for i, o in pairs:
+            self._check(i, o)
+        st = bmmc_plan_tune_pairs(self.handle, pairs, stream, reps)
         if st != OK:
-            raise BmmcError(st, "bmmc_plan_tune")
+            raise BmmcError(st, "bmmc_plan_tune_pairs")
         self.info = bmmc_plan_get_info(self.handle)
 
     def close(self) -> None:

@@ -208,13 +208,26 @@ int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream)
  * same permutation; they differ in the launch style (the planner's persistent
  * or streamed walk, or one workgroup per tile) and the block order
  * (bmmc_plan_options.block_map 1, 3, 5 and 6).  An option the caller fixed at
- * plan creation is kept.  Each candidate runs `reps` times (0 = 3) on
- * `stream` with `in` and `out` (the same requirements as bmmc_execute), twice
- * over, timed with HIP events; the fastest replaces the plan's kernel tables.
- * On return `out` holds the permutation of `in`.  Blocks the host until the
- * stream has drained; the plan must not be executed concurrently.  A plan
- * with no tile pass has nothing to choose and is run once.  Errors as
- * bmmc_execute; on any error the plan is unchanged. */
+ * plan creation is kept.  Each candidate runs `reps` times (0 = enough runs
+ * for about 2 ms of work, 3 to 200) on `stream`, twice over, timed with HIP
+ * events; the fastest replaces the plan's kernel tables if it beats the
+ * planner's own choice by more than 2%, and the chosen tables are then run
+ * once on ins[0] -> outs[0].
+ *
+ * Runs rotate over the npairs (1 .. BMMC_MAX_TUNE_PAIRS) device buffer pairs
+ * ins[k] -> outs[k], each with bmmc_execute's requirements; pass the working
+ * set the plan will meet (for arrays that fit the 256 MB Infinity Cache, one
+ * pair times cache-resident runs).  On return outs[0] holds the permutation
+ * of ins[0]; every other outs[k] holds the permutation of ins[k] or is
+ * untouched.  Blocks the host until the stream has drained; the plan must not
+ * be executed concurrently.  A plan with no tile pass has nothing to choose
+ * and is run once.  Errors as bmmc_execute; on any error the plan is
+ * unchanged.  Pointer arrays are the caller's and are not kept. */
+#define BMMC_MAX_TUNE_PAIRS 4096
+int bmmc_plan_tune_pairs(bmmc_plan *plan, const void *const *ins, void *const *outs, int npairs,
+                         void *stream, int reps);
+
+/* bmmc_plan_tune_pairs with the one pair in -> out. */
 int bmmc_plan_tune(bmmc_plan *plan, const void *in, void *out, void *stream, int reps);
 
 /* The ceiling: copy nbytes from `in` to `out` (device pointers, no overlap)

@@ -227,6 +227,32 @@ def test_tune_keeps_results_and_fixed_options(case):
             assert (d.kernel, d.launch, d.block_map) in before
 
 
+@pytest.mark.parametrize("route", [bm.ROUTE_AUTO, bm.ROUTE_TWO_PASS])
+def test_tune_over_rotating_pairs(route):
+    """bmmc_plan_tune_pairs: outs[0] holds the permutation of ins[0]; every
+    other output holds its own input's permutation or is untouched."""
+    torch = _torch()
+    n, e = 16, 4
+    A, c = _inv(n, 5150)
+    xs = [wl.fill_random_bytes(n, e, seed=300 + k) for k in range(5)]
+    d_ins = [torch.from_numpy(np.ascontiguousarray(x).view(np.uint8).reshape(-1).copy())
+             .to("cuda:0") for x in xs]
+    d_outs = [torch.full_like(d, SENTINEL) for d in d_ins]
+    P = bm.Plan(n, A, c, e, route=route)
+    P.tune(pairs=list(zip(d_ins, d_outs)), reps=2)
+    torch.cuda.synchronize()
+    for k, (x, d) in enumerate(zip(xs, d_outs)):
+        got = d.cpu().numpy()
+        want = oracle.apply(A, c, x).view(np.uint8).reshape(-1)
+        untouched = bool(np.all(got == SENTINEL))
+        assert np.array_equal(got, want) or (k > 0 and untouched), k
+    for x, d_in, d_out in zip(xs, d_ins, d_outs):
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(d_out.cpu().numpy(), oracle.apply(A, c, x).view(np.uint8).reshape(-1))
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------

@@ -121,6 +121,20 @@ def test_tune_argument_errors_without_gpu():
     assert bm.bmmc_plan_tune(p.handle, 1 << 20, 1 << 24, None, 1001) == bm.ERR_INVALID_ARG
 
 
+def test_tune_pairs_argument_errors_without_gpu():
+    p = bm.Plan(10, wl.bit_reverse_matrix(10), 0, 4)
+    assert bm.bmmc_plan_tune_pairs(p.handle, []) == bm.ERR_INVALID_ARG
+    pairs = [(1 << 20, 1 << 24), (2 << 20, 2 << 24)]
+    assert bm.bmmc_plan_tune_pairs(0, pairs) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune_pairs(p.handle, pairs + [(0, 1 << 26)]) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_plan_tune_pairs(p.handle, pairs + [(3 << 20, (3 << 20) + 64)]) == bm.ERR_ALIAS
+    assert bm.bmmc_plan_tune_pairs(p.handle, pairs, None, -1) == bm.ERR_INVALID_ARG
+    many = [((k + 1) << 20, (k + 1) << 32) for k in range(4097)]  # one above the limit
+    assert bm.bmmc_plan_tune_pairs(p.handle, many) == bm.ERR_INVALID_ARG
+    with pytest.raises(bm.BmmcError):
+        p.tune(pairs=[])
+
+
 def test_pass_records_block_order():
     A, c = wl.random_bmmc(16, 5, lambda r: oracle.rank(r) == 16)
     for bmap in (0, 1, 3, 5, 6, 7, 2, 9):
