@@ -151,30 +151,40 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
         return st;
     }
 
-    // candidates: (launch style, block order), keeping what the caller fixed
-    std::vector<int> launches, maps;
+    // candidates: (tile side, launch style, block order), keeping what the
+    // caller fixed; the first is the planner's own choice
+    std::vector<int> launches, maps, tiles;
     if (p->opt.launch) launches = {p->opt.launch};
     else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
     if (p->opt.block_map) maps = {p->opt.block_map};
     else maps = {1, 3, 5, 6};
+    tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
     std::vector<std::unique_ptr<bmmc_plan>> cand;
-    for (int l : launches)
-        for (int m : maps) {
-            bmmc_plan_options o = p->opt;
-            o.launch = l;
-            o.block_map = m;
-            std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
-            if (!q) return BMMC_ERR_OUT_OF_MEMORY;
-            if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) !=
-                    BMMC_OK ||
-                !supported(*q))
-                continue;
-            bool dup = false;  // same tables as an earlier candidate
-            for (const auto &r : cand)
-                dup |= r->npasses == q->npasses &&
-                       std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
-            if (!dup) cand.push_back(std::move(q));
-        }
+    for (size_t ti = 0; ti < tiles.size(); ++ti)
+        for (int l : launches)
+            for (int m : maps) {
+                bmmc_plan_options o = p->opt;
+                o.tile_log2 = tiles[ti];
+                o.launch = l;
+                o.block_map = m;
+                std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
+                if (!q) return BMMC_ERR_OUT_OF_MEMORY;
+                if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) !=
+                        BMMC_OK ||
+                    !supported(*q))
+                    continue;
+                // the next larger side (rows twice as long), once the
+                // planner's side is known; the planner clamps it to what
+                // the LDS and the index bits allow (duplicates drop out)
+                if (!p->opt.tile_log2 && tiles.size() == 1 && q->info.tile_log2 > 0 &&
+                    q->info.tile_log2 < BMMC_MAX_TILE)
+                    tiles.push_back(q->info.tile_log2 + 1);
+                bool dup = false;  // same tables as an earlier candidate
+                for (const auto &r : cand)
+                    dup |= r->npasses == q->npasses &&
+                           std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
+                if (!dup) cand.push_back(std::move(q));
+            }
     if (cand.empty()) return BMMC_ERR_UNSUPPORTED;
 
     void *scratch = nullptr;

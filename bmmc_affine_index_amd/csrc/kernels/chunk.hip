@@ -24,7 +24,7 @@ namespace bmmc {
 constexpr int kChunkNTL = 8;   // 256 threads
 constexpr int kChunkCPTL = 2;  // 4 chunks per thread
 
-template <int UL, int WL>
+template <int UL, int WL, bool NT>
 __global__ void __launch_bounds__(1 << kChunkNTL)
     bmmc_chunk_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                       const bmmc_pass_desc d, uint64_t blk0) {
@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const uint64_t x = first + ((uint64_t)k << kChunkNTL) + tid;
-        if (x < nchunks) v[k] = dev::gload_hint<CB>(in + x * CB, d.cache_hint & 1);
+        if (x < nchunks) v[k] = dev::gload_nt<CB, NT>(in + x * CB);
     }
     const uint32_t ux = (uint32_t)d.unit_xor;
 #pragma unroll
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
             }
         }
         const uint64_t off = dev::xor_bits_uniform(d.out_blk, xu) ^ lane_off ^ d.out_c;
-        dev::gstore_hint<CB>(out + off, c, d.cache_hint & 2);
+        dev::gstore_nt<CB, NT>(out + off, c);
     }
 }
 
@@ -79,8 +79,12 @@ int launch_chunk_t(const bmmc_pass_desc &d, const uint8_t *in, uint8_t *out, hip
     const uint64_t blocks = (nchunks + per - 1) / per;
     for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
         const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL>), dim3((uint32_t)nb), dim3(1 << kChunkNTL),
-                           0, s, in, out, d, b0);
+        if (d.cache_hint)
+            hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL, true>), dim3((uint32_t)nb),
+                               dim3(1 << kChunkNTL), 0, s, in, out, d, b0);
+        else
+            hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL, false>), dim3((uint32_t)nb),
+                               dim3(1 << kChunkNTL), 0, s, in, out, d, b0);
     }
     return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
 }
@@ -101,6 +105,7 @@ int dispatch_chunk(int ul, int wl, const bmmc_pass_desc &d, const uint8_t *in, u
 }  // namespace
 
 int launch_chunk(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
+    if (d.cache_hint != 0 && d.cache_hint != 3) return BMMC_ERR_UNSUPPORTED;
     return dispatch_chunk<0, 0>(d.unit_log2, d.chunk_log2, d, static_cast<const uint8_t *>(in),
                                 static_cast<uint8_t *>(out), s);
 }

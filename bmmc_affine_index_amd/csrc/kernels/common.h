@@ -69,46 +69,37 @@ template <> __device__ __forceinline__ void gstore<1>(uint8_t *p, const Chunk<1>
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
 
-template <int BYTES>
-__device__ __forceinline__ Chunk<BYTES> gload_hint(const uint8_t *p, int nontemporal) {
-    if constexpr (BYTES == 16) {
-        if (nontemporal) {
-            nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
-            return Chunk<16>{{v.x, v.y, v.z, v.w}};
-        }
-    } else if constexpr (BYTES == 8) {
-        if (nontemporal) {
-            nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2 *>(p));
-            return Chunk<8>{{v.x, v.y}};
-        }
-    } else if constexpr (BYTES == 4) {
-        if (nontemporal)
-            return Chunk<4>{{__builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p))}};
+// NT is a template parameter: the cache policy is an immediate of the
+// instruction, and a run-time choice would put every access under a branch,
+// which forces the compiler's memory-counter waits down to zero at the joins.
+template <int BYTES, bool NT>
+__device__ __forceinline__ Chunk<BYTES> gload_nt(const uint8_t *p) {
+    if constexpr (NT && BYTES == 16) {
+        nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
+        return Chunk<16>{{v.x, v.y, v.z, v.w}};
+    } else if constexpr (NT && BYTES == 8) {
+        nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2 *>(p));
+        return Chunk<8>{{v.x, v.y}};
+    } else if constexpr (NT && BYTES == 4) {
+        return Chunk<4>{{__builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p))}};
+    } else {
+        return gload<BYTES>(p);
     }
-    return gload<BYTES>(p);
 }
 
-template <int BYTES>
-__device__ __forceinline__ void gstore_hint(uint8_t *p, const Chunk<BYTES> &c, int nontemporal) {
-    if constexpr (BYTES == 16) {
-        if (nontemporal) {
-            nt_u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
-            __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4 *>(p));
-            return;
-        }
-    } else if constexpr (BYTES == 8) {
-        if (nontemporal) {
-            nt_u32x2 v = {c.w[0], c.w[1]};
-            __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x2 *>(p));
-            return;
-        }
-    } else if constexpr (BYTES == 4) {
-        if (nontemporal) {
-            __builtin_nontemporal_store(c.w[0], reinterpret_cast<uint32_t *>(p));
-            return;
-        }
+template <int BYTES, bool NT>
+__device__ __forceinline__ void gstore_nt(uint8_t *p, const Chunk<BYTES> &c) {
+    if constexpr (NT && BYTES == 16) {
+        nt_u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4 *>(p));
+    } else if constexpr (NT && BYTES == 8) {
+        nt_u32x2 v = {c.w[0], c.w[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x2 *>(p));
+    } else if constexpr (NT && BYTES == 4) {
+        __builtin_nontemporal_store(c.w[0], reinterpret_cast<uint32_t *>(p));
+    } else {
+        gstore<BYTES>(p, c);
     }
-    gstore<BYTES>(p, c);
 }
 
 // ---- LDS ----------------------------------------------------------------

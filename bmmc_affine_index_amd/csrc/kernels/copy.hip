@@ -27,12 +27,12 @@ __global__ void __launch_bounds__(1 << kCopyNTL)
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const uint64_t x = first + ((uint64_t)k << kCopyNTL);
-        if (x < n16) v[k] = dev::gload_hint<16>(in + x * 16, 1);
+        if (x < n16) v[k] = dev::gload_nt<16, true>(in + x * 16);
     }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const uint64_t x = first + ((uint64_t)k << kCopyNTL);
-        if (x < n16) dev::gstore_hint<16>(out + x * 16, v[k], 1);
+        if (x < n16) dev::gstore_nt<16, true>(out + x * 16, v[k]);
     }
 }
 
@@ -48,12 +48,12 @@ __global__ void __launch_bounds__(1 << kCopyNTL)
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const uint64_t x = base + ((uint64_t)k << kCopyNTL);
-            if (x < n16) v[k] = dev::gload_hint<16>(in + x * 16, 1);
+            if (x < n16) v[k] = dev::gload_nt<16, true>(in + x * 16);
         }
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const uint64_t x = base + ((uint64_t)k << kCopyNTL);
-            if (x < n16) dev::gstore_hint<16>(out + x * 16, v[k], 1);
+            if (x < n16) dev::gstore_nt<16, true>(out + x * 16, v[k]);
         }
     }
 }

@@ -58,14 +58,14 @@ __device__ __forceinline__ LaneParts lane_parts(const bmmc_pass_desc &d, uint32_
 }
 
 // Issue the global loads of one tile: pass j covers chunks (j << NTL) | tid.
-template <class C, int T>
+template <class C, int T, bool NT>
 __device__ __forceinline__ void load_tile(dev::Chunk<C::CB> (&v)[C::J], const uint8_t *in,
                                           uint64_t in_base, const bmmc_pass_desc &d,
                                           const LaneParts &p) {
 #pragma unroll
     for (int j = 0; j < C::J; ++j) {
         const uint64_t in_j = in_base ^ dev::xor_bits_lane<C::JL>(d.ld_in + C::NTL, (uint32_t)j);
-        v[j] = dev::gload_hint<C::CB>(in + (in_j ^ p.in_lane), d.cache_hint & 1);
+        v[j] = dev::gload_nt<C::CB, NT>(in + (in_j ^ p.in_lane));
     }
 }
 
@@ -81,7 +81,7 @@ __device__ __forceinline__ void stage_tile(uint8_t *tile_lds, const dev::Chunk<C
 }
 
 // Read the tile back in output order and store whole output chunks.
-template <class C, int T>
+template <class C, int T, bool NT>
 __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds, uint64_t obase,
                                            uint32_t rbase, const bmmc_pass_desc &d,
                                            const LaneParts &p) {
@@ -98,13 +98,13 @@ __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds
             const uint32_t rd_e = dev::xor_bits_lane<C::WL>(d.st_unit, (uint32_t)e);
             dev::put_unit<C::CB, C::U>(ch, e, dev::lds_load_unit<C::U>(tile_lds + (rd_j ^ rd_e)));
         }
-        dev::gstore_hint<C::CB>(out + (out_j ^ p.out_lane), ch, d.cache_hint & 2);
+        dev::gstore_nt<C::CB, NT>(out + (out_j ^ p.out_lane), ch);
     }
 }
 
 // One workgroup per tile, or per 2^IT tiles whose loads are all issued
 // before the barrier (the pages' iterated variant).
-template <int UL, int T, int IT>
+template <int UL, int T, int IT, bool NT>
 __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
     bmmc_tiled_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                       const bmmc_pass_desc d, uint64_t blk0) {
@@ -116,14 +116,14 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
     dev::Chunk<C::CB> v[1 << IT][C::J];
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s)
-        load_tile<C, T>(v[s], in, dev::xor_bits_uniform(d.in_blk, tile0 | (uint64_t)s), d, p);
+        load_tile<C, T, NT>(v[s], in, dev::xor_bits_uniform(d.in_blk, tile0 | (uint64_t)s), d, p);
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s) stage_tile<C, T>(lds + s * C::TILE, v[s], d, p);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s) {
         const uint64_t blk = tile0 | (uint64_t)s;
-        drain_tile<C, T>(out, lds + s * C::TILE, dev::xor_bits_uniform(d.out_blk, blk) ^ d.out_c,
+        drain_tile<C, T, NT>(out, lds + s * C::TILE, dev::xor_bits_uniform(d.out_blk, blk) ^ d.out_c,
                          dev::xor_bits_uniform(d.lds_blk, blk) ^ d.lds_c, d, p);
     }
 }
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
 // already in flight.  One barrier per tile suffices: a buffer is rewritten
 // two tiles later, after every thread has passed the barrier that follows
 // its reads.
-template <int UL, int T>
+template <int UL, int T, bool NT>
 __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
     bmmc_tiled_persistent_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                  const bmmc_pass_desc d) {
@@ -155,23 +155,35 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
     uint32_t rd_base = dev::xor_bits_uniform(d.lds_blk, first) ^ d.lds_c;
 
     dev::Chunk<C::CB> v[C::J];
-    load_tile<C, T>(v, in, in_base, d, p);
-    for (uint64_t k = 0; k < count; ++k) {
+    load_tile<C, T, NT>(v, in, in_base, d, p);
+    // Every tile but the last refills the registers with the next tile's
+    // loads before draining.  Loads and stores share one counter, which
+    // completes in issue order; the staging wait can leave the previous
+    // tile's stores in flight only if every path into it has the same
+    // accesses outstanding, so the refill is unconditional and the first
+    // tile is peeled (the loop is then always entered with one tile of loads
+    // followed by one tile of stores).
+    auto step = [&](uint64_t k) {
         uint8_t *buf = lds + (k & 1) * C::TILE;
         stage_tile<C, T>(buf, v, d, p);
         __syncthreads();
-        const bool more = k + 1 < count;
-        const int bit = more ? shift + __builtin_ctzll(k + 1) : 0;
-        if (more) {
-            in_base ^= d.in_blk[bit];
-            load_tile<C, T>(v, in, in_base, d, p);
-        }
-        drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
-        if (more) {
-            out_base ^= d.out_blk[bit];
-            rd_base ^= d.lds_blk[bit];
-        }
+        const int bit = shift + __builtin_ctzll(k + 1);
+        in_base ^= d.in_blk[bit];
+        load_tile<C, T, NT>(v, in, in_base, d, p);
+        __builtin_amdgcn_sched_barrier(0);
+        drain_tile<C, T, NT>(out, buf, out_base, rd_base, d, p);
+        out_base ^= d.out_blk[bit];
+        rd_base ^= d.lds_blk[bit];
+    };
+    uint64_t k = 0;
+    if (count > 1) {
+        step(0);
+        for (k = 1; k + 1 < count; ++k) step(k);
     }
+    uint8_t *buf = lds + (k & 1) * C::TILE;
+    stage_tile<C, T>(buf, v, d, p);
+    __syncthreads();
+    drain_tile<C, T, NT>(out, buf, out_base, rd_base, d, p);
 }
 
 // Streamed: the persistent walk with the waves split by role.  Waves of the
@@ -183,7 +195,7 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
 // for.  One barrier per tile orders the halves: the loaders write buffer k&1
 // before barrier k, the storers read it after barrier k and have finished
 // before barrier k+1, after which the loaders may write it again (tile k+2).
-template <int UL, int T, int DEPTH>
+template <int UL, int T, int DEPTH, bool NT>
 __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     bmmc_tiled_streamed_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                const bmmc_pass_desc d) {
@@ -210,36 +222,63 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     uint64_t out_base = dev::xor_bits_uniform(d.out_blk, first) ^ d.out_c;
     uint32_t rd_base = dev::xor_bits_uniform(d.lds_blk, first) ^ d.lds_c;
 
-    dev::Chunk<C::CB> v[DEPTH][C::J];
-    auto load_next = [&](dev::Chunk<C::CB>(&dst)[C::J]) {
-        if (loaded > 0) in_base ^= d.in_blk[shift + __builtin_ctzll(loaded)];
-        load_tile<C, T>(dst, in, in_base, d, p);
-        ++loaded;
-    };
-    auto drain_next = [&](uint64_t k, uint8_t *buf) {
-        drain_tile<C, T>(out, buf, out_base, rd_base, d, p);
-        if (k + 1 < count) {
-            const int bit = shift + __builtin_ctzll(k + 1);
-            out_base ^= d.out_blk[bit];
-            rd_base ^= d.lds_blk[bit];
-        }
-    };
+    // Each role runs its own loop with exactly `count` barriers, so every
+    // wave meets the same barriers; keeping the roles' code apart leaves each
+    // loop straight-line, which lets the compiler wait for the oldest tile's
+    // loads only (a shared loop body merges both roles' paths and its waits
+    // fall back to "everything outstanding").
     if (loader) {
-        load_next(v[0]);
-        if (DEPTH == 2 && count > 1) load_next(v[1]);
-    }
-    for (uint64_t k = 0; k < count; k += DEPTH) {
+        dev::Chunk<C::CB> v[DEPTH][C::J];
+        // next tile in walk order: one table entry per step (Gray code)
+        auto advance = [&]() {
+            in_base ^= d.in_blk[shift + __builtin_ctzll(loaded)];
+            ++loaded;
+        };
+        load_tile<C, T, NT>(v[0], in, in_base, d, p);
+        loaded = 1;
+        if (count == 1) {
+            stage_tile<C, T>(lds, v[0], d, p);
+            __syncthreads();
+            return;
+        }
+        if constexpr (DEPTH == 2) {
+            // tile 1's loads after tile 0's: waits count loads in issue order
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
+            load_tile<C, T, NT>(v[1], in, in_base, d, p);
+        }
+        // Steady state: every staged buffer is refilled DEPTH tiles ahead.
+        // count is a power of two >= 2, so while k + DEPTH < count the DEPTH
+        // tiles after k + DEPTH - 1 all exist and the refills need no
+        // condition (a conditional refill would leave the compiler unsure how
+        // many loads are outstanding, and it would then wait for all of them).
+        uint64_t k = 0;
+        for (; k + DEPTH < count; k += DEPTH) {
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) {
+                stage_tile<C, T>(lds + ((k + s) & 1) * C::TILE, v[s], d, p);
+                __syncthreads();
+                advance();
+                load_tile<C, T, NT>(v[s], in, in_base, d, p);
+                // keep the refill ahead of the next staging: staging waits
+                // for the older tile only while the refill is in flight
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // the last DEPTH tiles: nothing left to load
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            if (k + s < count) {  // uniform
-                uint8_t *buf = lds + ((k + s) & 1) * C::TILE;
-                if (loader) stage_tile<C, T>(buf, v[s], d, p);
-                __syncthreads();
-                if (loader) {
-                    if (loaded < count) load_next(v[s]);
-                } else {
-                    drain_next(k + s, buf);
-                }
+            stage_tile<C, T>(lds + ((k + s) & 1) * C::TILE, v[s], d, p);
+            __syncthreads();
+        }
+    } else {
+        for (uint64_t k = 0; k < count; ++k) {
+            __syncthreads();
+            drain_tile<C, T, NT>(out, lds + (k & 1) * C::TILE, out_base, rd_base, d, p);
+            if (k + 1 < count) {
+                const int bit = shift + __builtin_ctzll(k + 1);
+                out_base ^= d.out_blk[bit];
+                rd_base ^= d.lds_blk[bit];
             }
         }
     }
@@ -257,16 +296,16 @@ struct TiledArgs {
     hipStream_t s;
 };
 
-template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
+template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
     using C = TiledCfg<UL, T, IT>;
     if (a.d->launch == BMMC_LAUNCH_STREAMED) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072 && C::NT >= 64) {
             if (a.d->depth == 2)
-                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2>),
+                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT>),
                                    dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
                                    a.out, *a.d);
             else
-                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1>),
+                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT>),
                                    dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
                                    a.out, *a.d);
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
@@ -276,7 +315,7 @@ template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     }
     if (a.d->launch == BMMC_LAUNCH_PERSISTENT) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
-            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T>),
+            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T, NT>),
                                dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out,
                                *a.d);
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
@@ -287,10 +326,15 @@ template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     const uint64_t blocks = uint64_t(1) << (a.d->blk_bits - IT);
     for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
         const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT>), dim3((uint32_t)nb), dim3(C::NT), 0,
-                           a.s, a.in, a.out, *a.d, b0);
+        hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT, NT>), dim3((uint32_t)nb), dim3(C::NT),
+                           0, a.s, a.in, a.out, *a.d, b0);
     }
     return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+}
+
+// cache_hint 3: non-temporal loads and stores; 0: plain.
+template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
+    return a.d->cache_hint ? launch_nt<UL, T, IT, true>(a) : launch_nt<UL, T, IT, false>(a);
 }
 
 template <int UL, int T, int IT> constexpr bool valid_cfg() {
@@ -338,6 +382,7 @@ int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t
     if (d.launch != BMMC_LAUNCH_ONE_TILE && d.walk != BMMC_WALK_RANGES &&
         d.walk != BMMC_WALK_INTERLEAVED)
         return BMMC_ERR_INVALID_ARG;
+    if (d.cache_hint != 0 && d.cache_hint != 3) return BMMC_ERR_UNSUPPORTED;
     TiledArgs a{&d, static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), s};
     return dispatch<0, 1, 0>(d.unit_log2, d.t, d.iters_log2, &a);
 }

@@ -246,7 +246,7 @@ struct LaunchChoice {
     int block_map;   // 1 identity, 2 reversed, 3-5 locality orders, >= 8 random (seed)
     int depth;       // streamed: tiles of loads in flight per loader wave
     bool auto_launch;  // launch style left to the planner
-    int cache_hint;    // descriptor bits: 1 non-temporal loads, 2 non-temporal stores
+    int cache_hint;    // descriptor value: 3 non-temporal loads and stores, 0 plain
 };
 
 // Highest set bit of a byte offset (-1 for 0).
@@ -684,10 +684,10 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     lc.walk = o.walk ? o.walk : BMMC_WALK_RANGES;
     if (o.block_map < 0) return BMMC_ERR_INVALID_ARG;
     if (o.depth < 0 || o.depth > 2) return BMMC_ERR_INVALID_ARG;
-    if (o.cache_hint < 0 || o.cache_hint > 4) return BMMC_ERR_INVALID_ARG;
+    if (o.cache_hint < 0 || o.cache_hint > 2) return BMMC_ERR_INVALID_ARG;
     // Planner's choice: non-temporal loads and stores (measured on the four
     // large workloads: +1% to +5% over no hint; loads alone lose).
-    lc.cache_hint = o.cache_hint == 1 ? 0 : o.cache_hint == 2 ? 1 : o.cache_hint == 3 ? 2 : 3;
+    lc.cache_hint = o.cache_hint == 1 ? 0 : 3;
     lc.depth = o.depth ? o.depth : 2;
     lc.block_map = o.block_map ? o.block_map : 1;
     const int e = __builtin_ctzll((u64)elem_bytes);

@@ -78,8 +78,8 @@ typedef struct bmmc_plan_options {
     int walk;       /* persistent launch: BMMC_WALK_* order of tiles; 0 = planner's choice */
     int depth;      /* streamed launch: tiles of loads in flight per loader wave (1 or 2);
                        0 = planner's choice */
-    int cache_hint; /* tile pass: 0 = planner's choice, 1 = none, 2 = non-temporal loads,
-                       3 = non-temporal stores, 4 = both */
+    int cache_hint; /* tile pass: 0 = planner's choice (non-temporal loads and stores),
+                       1 = none, 2 = non-temporal loads and stores */
     int block_map;  /* re-indexing of the tiles: 0 = planner's choice, 1 = identity,
                        2 = reversed bit order, 3 = tiles in flight together form a
                        patch dense on both the input and the output side, 4 = dense on
@@ -157,7 +157,7 @@ typedef struct bmmc_pass_desc {
     int32_t grid_log2;   /* persistent launch: 2^grid_log2 workgroups (TILED) */
     int32_t walk;        /* persistent launch: BMMC_WALK_RANGES or _INTERLEAVED (TILED) */
     int32_t depth;       /* streamed launch: tiles of loads in flight per loader wave, 1 or 2 */
-    int32_t cache_hint;  /* bit 0 non-temporal loads, bit 1 non-temporal stores */
+    int32_t cache_hint;  /* 3 = non-temporal loads and stores, 0 = plain (others unsupported) */
     int32_t block_map;   /* tile order the tables were built with (TILED; 0 otherwise) */
     uint64_t out_c;
     uint32_t lds_c;
@@ -205,10 +205,11 @@ int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream)
  * and the best order depends on the matrix ("Efficient GPU Implementation of
  * Affine Index Permutations on Arrays", limitations: on the AMD card the
  * running time varied with the permutation).  Every candidate computes the
- * same permutation; they differ in the launch style (the planner's persistent
- * or streamed walk, or one workgroup per tile) and the block order
- * (bmmc_plan_options.block_map 1, 3, 5 and 6).  An option the caller fixed at
- * plan creation is kept.  Each candidate runs `reps` times (0 = enough runs
+ * same permutation; they differ in the tile side (the planner's and the next
+ * larger), the launch style (the planner's persistent or streamed walk, or
+ * one workgroup per tile) and the block order (bmmc_plan_options.block_map 1,
+ * 3, 5 and 6): up to 16 candidates.  An option the caller fixed at plan
+ * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, twice over, timed with HIP
  * events; the fastest replaces the plan's kernel tables if it beats the
  * planner's own choice by more than 2%, and the chosen tables are then run

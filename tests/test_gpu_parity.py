@@ -98,9 +98,11 @@ for e in (1, 2, 4, 8, 16):
             for g in (0, 5, 6):  # g = 5, 6: walks of 2 and 1 tiles (odd/short counts)
                 SMALL.append((kind, 16, e, dict(launch=bm.LAUNCH_STREAMED, depth=dp,
                                                 grid_log2=g)))
-for hint in (2, 3, 4):
+for hint in (1, 2):
     for e in (1, 4, 8, 16):
         SMALL.append(("general", 17, e, dict(cache_hint=hint)))
+        SMALL.append(("bitrev", 16, e, dict(cache_hint=hint, launch=bm.LAUNCH_ONE_TILE)))
+        SMALL.append(("transpose", 18, e, dict(cache_hint=hint, launch=bm.LAUNCH_STREAMED)))
 for bmap in (2, 3, 4, 5, 99):
     SMALL.append(("general", 17, 4, dict(block_map=bmap)))
     SMALL.append(("bpc", 17, 16, dict(block_map=bmap, launch=bm.LAUNCH_ONE_TILE)))
@@ -188,7 +190,8 @@ TUNE_CASES = [("general", 17, 4, {}), ("bpc", 18, 16, {}), ("bitrev", 16, 1, {})
               ("transpose", 18, 8, {}), ("general", 15, 2, dict(route=bm.ROUTE_TWO_PASS)),
               ("general", 17, 4, dict(launch=bm.LAUNCH_ONE_TILE)),
               ("bpc", 17, 4, dict(block_map=7)), ("general", 12, 4, dict(iters_log2=1)),
-              ("complement", 14, 4, {}), ("identity", 14, 4, {})]
+              ("complement", 14, 4, {}), ("identity", 14, 4, {}),
+              ("transpose", 16, 4, dict(tile_log2=5)), ("bitrev", 18, 2, {})]
 
 
 @pytest.mark.parametrize("case", TUNE_CASES, ids=lambda c: "%s-n%d-e%d-%s" % (
@@ -215,6 +218,8 @@ def test_tune_keeps_results_and_fixed_options(case):
         assert np.array_equal(got, want), (rep, P.describe())
     after = P.passes()
     assert [d.kernel for d in after] == [b[0] for b in before]
+    if "tile_log2" in kw:
+        assert P.info.tile_log2 == kw["tile_log2"]
     for d in after:
         if d.kernel == bm.KERNEL_TILED:
             if "launch" in kw:
