@@ -215,7 +215,7 @@ def run_ablation(args, torch):
                                   "frac_of_copy": round(gbs / copy_gbs, 4),
                                   "speedup_vs_naive": round(gbs / base, 3),
                                   "ms": round(ms, 5), "copy_gbs": round(copy_gbs, 1),
-                                  "passes": plan.info.passes,
+                                  "passes": plan.info.passes, "plan": plan.describe(),
                                   "parity": "bit-exact" if ok else "MISMATCH"}), flush=True)
                 if not ok:
                     sys.exit(3)
