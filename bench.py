@@ -137,11 +137,33 @@ def cpu_baseline(A, c, x, budget_s: float):
         if el >= budget_s or done >= 100000:
             break
     moved = 2.0 * done * span * elem
+    # the same calls on one thread, for about a fifth of the budget
+    one, t1 = 0, time.perf_counter()
+    while True:
+        lo = (one * span) % N
+        oracle.apply_range(A, c, x, out, lo, lo + span, threads=1)
+        one += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= budget_s / 5 or one >= 100000:
+            break
     return {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d oracle calls of 2^%d consecutive input indices each (%.1f s, "
                       "%d threads), same matrix and data" % (done, span.bit_length() - 1, el,
-                                                             threads)}
+                                                             threads),
+            "single_thread_value": round(2.0 * one * span * elem / el1 / 1e9, 4),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 ABLATION_VARIANTS = [
@@ -226,7 +248,9 @@ def run_ablation(args, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; 1000 for the 4 MiB workloads, whose "
+                         "single steps take microseconds)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--kind", default=None,
@@ -262,6 +286,8 @@ def main():
                          "one JSON line each (not the headline line)")
     ap.add_argument("--sizes", default="20,24,28", help="ablation: comma-separated n")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1000 if (args.workload in ("c1a", "c1b") and not args.kind) else 200
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); "
@@ -453,6 +479,9 @@ def main():
     }
     if perm_stats:
         result["permutations"] = perm_stats
+    if passes > 1:
+        # bytes the passes move in total (each reads and writes the array)
+        result["transfer_gbs"] = round(passes * value, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(A, c, x, args.cpu_budget)
     print(json.dumps(result))
