@@ -89,92 +89,52 @@ def lib_accepts(n: int):
     return accept
 
 
-def time_loop(torch, fn, bufs, steps, warmup, stream):
-    """Warm up, then time exactly `steps` calls with events on `stream`."""
+def time_loop(torch, fn, bufs, steps, warmup, stream, graph=True):
+    """Warm up, then time exactly `steps` calls fn(in, out, stream_handle)
+    with events on `stream`.  graph=True captures the `steps` calls once into
+    a HIP graph and the timed region replays it, so the host's per-call cost
+    (ctypes, argument checks, the launch itself) stays out of the measurement
+    of arrays whose steps take microseconds."""
+    h = int(stream.cuda_stream)
     for k in range(warmup):
-        fn(*bufs[k % len(bufs)])
+        fn(*bufs[k % len(bufs)], h)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for k in range(steps):
-        fn(*bufs[k % len(bufs)])
-    stop.record(stream)
-    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap):
+            hc = int(torch.cuda.current_stream().cuda_stream)
+            for k in range(steps):
+                fn(*bufs[k % len(bufs)], hc)
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        del g
+    else:
+        start.record(stream)
+        for k in range(steps):
+            fn(*bufs[k % len(bufs)], h)
+        stop.record(stream)
+        torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
 
 
 def per_launch_ms(torch, fn, bufs, reps, stream):
     """Median/min/max of individually event-timed launches."""
+    h = int(stream.cuda_stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for k, (a, b) in enumerate(ev):
         a.record(stream)
-        fn(*bufs[k % len(bufs)])
+        fn(*bufs[k % len(bufs)], h)
         b.record(stream)
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     return ms[len(ms) // 2], ms[0], ms[-1]
-
-
-def cpu_baseline(A, c, x, budget_s: float):
-    """The oracle, as it stands, on the host cores: repeated full-array
-    scatters (or index ranges for big arrays) for about budget_s seconds."""
-    import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
-    n = len(A)
-    N = 1 << n
-    elem = x.nbytes >> n
-    out = np.empty_like(x)
-    # one slice of at most 2^24 indices per call keeps each call short
-    span = min(N, 1 << 24)
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        lo = (done * span) % N
-        oracle.apply_range(A, c, x, out, lo, lo + span, threads=threads)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or done >= 100000:
-            break
-    moved = 2.0 * done * span * elem
-    # the same calls on one thread, for about a fifth of the budget
-    one, t1 = 0, time.perf_counter()
-    while True:
-        lo = (one * span) % N
-        oracle.apply_range(A, c, x, out, lo, lo + span, threads=1)
-        one += 1
-        el1 = time.perf_counter() - t1
-        if el1 >= budget_s / 5 or one >= 100000:
-            break
-    return {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d oracle calls of 2^%d consecutive input indices each (%.1f s, "
-                      "%d threads), same matrix and data" % (done, span.bit_length() - 1, el,
-                                                             threads),
-            "single_thread_value": round(2.0 * one * span * elem / el1 / 1e9, 4),
-            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
-
-
-def cpu_model() -> str:
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
-
-
-ABLATION_VARIANTS = [
-    # name, plan options; the paper's Figure 9 columns, then this library's default
-    ("naive", dict(route=bm.ROUTE_NAIVE)),
-    ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True)),
-    ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE)),
-    ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
-    ("planner, untuned", dict()),
-    ("tuned (default)", dict(tune=True)),
-]
 
 
 def run_ablation(args, torch):
@@ -196,9 +156,11 @@ def run_ablation(args, torch):
         bufs = list(zip(ins, outs))
         steps = max(10, min(args.steps, int(2e9 // (2 * nbytes)) or 10))
 
-        def copy(i, o):
-            bm.bmmc_copy(i, o, nbytes, s_handle)
-        ms_copy = time_loop(torch, copy, bufs, steps, 3, stream)
+        def copy(i, o, h):
+            st = bm.bmmc_copy(i, o, nbytes, h)
+            if st != bm.OK:
+                raise bm.BmmcError(st, "bmmc_copy")
+        ms_copy = time_loop(torch, copy, bufs, steps, 3, stream, graph=not args.no_graph)
         copy_gbs = 2.0 * nbytes / (ms_copy * 1e-3) / 1e9
         kinds = [("random_bpc", wl.random_bpc(n, 7)), ("bit_reverse", (wl.bit_reverse_matrix(n), 0)),
                  ("random_bmmc", wl.random_bmmc(n, 7, lib_accepts(n)))]
@@ -216,14 +178,14 @@ def run_ablation(args, torch):
                 if tune:
                     plan.tune(pairs=bufs, stream=s_handle)
 
-                def step(i, o, plan=plan):
-                    st = bm.bmmc_execute(plan.handle, i, o, s_handle)
+                def step(i, o, h, plan=plan):
+                    st = bm.bmmc_execute(plan.handle, i, o, h)
                     if st != bm.OK:
                         raise bm.BmmcError(st, "bmmc_execute")
-                ms = time_loop(torch, step, bufs, steps, 3, stream)
+                ms = time_loop(torch, step, bufs, steps, 3, stream, graph=not args.no_graph)
                 gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
                 base = base or gbs
-                step(*bufs[0])
+                step(*bufs[0], s_handle)
                 torch.cuda.synchronize()
                 got = outs[0].cpu().numpy().reshape(x.shape)
                 if n <= 24:
@@ -279,6 +241,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager calls from Python instead of replaying a HIP graph of them")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip bmmc_plan_tune (the planner's untimed choice of tile order)")
     ap.add_argument("--ablation", action="store_true",
@@ -363,18 +327,19 @@ def main():
         plan.tune(pairs=bufs, stream=s_handle)
         tune_ms = (time.perf_counter() - t0) * 1e3
 
-    def step(i, o):
-        st = bm.bmmc_execute(plan.handle, i, o, s_handle)
+    def step(i, o, h):
+        st = bm.bmmc_execute(plan.handle, i, o, h)
         if st != bm.OK:
             raise bm.BmmcError(st, "bmmc_execute")
 
-    def copy(i, o):
-        st = bm.bmmc_copy(i, o, nbytes, s_handle)
+    def copy(i, o, h):
+        st = bm.bmmc_copy(i, o, nbytes, h)
         if st != bm.OK:
             raise bm.BmmcError(st, "bmmc_copy")
 
-    ms = time_loop(torch, step, bufs, args.steps, args.warmup, stream)
-    ms_copy = time_loop(torch, copy, bufs, args.steps, args.warmup, stream)
+    graph = not args.no_graph
+    ms = time_loop(torch, step, bufs, args.steps, args.warmup, stream, graph=graph)
+    ms_copy = time_loop(torch, copy, bufs, args.steps, args.warmup, stream, graph=graph)
     med, mn, mx = per_launch_ms(torch, step, bufs, 20, stream)
     cmed, _, _ = per_launch_ms(torch, copy, bufs, 20, stream)
 
@@ -397,11 +362,11 @@ def main():
             if not args.no_tune:
                 pk.tune(pairs=bufs, stream=s_handle)
 
-            def stepk(i, o, pk=pk):
-                st = bm.bmmc_execute(pk.handle, i, o, s_handle)
+            def stepk(i, o, h, pk=pk):
+                st = bm.bmmc_execute(pk.handle, i, o, h)
                 if st != bm.OK:
                     raise bm.BmmcError(st, "bmmc_execute")
-            msk = time_loop(torch, stepk, bufs, args.steps, args.warmup, stream)
+            msk = time_loop(torch, stepk, bufs, args.steps, args.warmup, stream, graph=graph)
             vals.append(algo_bytes / (msk * 1e-3) / 1e9)
             print("perm %d: %.1f GB/s" % (k, vals[-1]), file=sys.stderr, flush=True)
         sv = sorted(vals)
@@ -413,7 +378,7 @@ def main():
 
     parity = "skipped"
     if not args.no_check:
-        step(*bufs[0])
+        step(*bufs[0], s_handle)
         torch.cuda.synchronize()
         got = outs[0].cpu().numpy().view(x.dtype).reshape(x.shape)
         import oracle
@@ -466,6 +431,8 @@ def main():
                           "%d rotating buffer pairs, %.2f GiB working set (HBM)"
                           % (pairs, 2 * pairs * nbytes / 2**30)),
             "plan": plan.describe(),
+            "timing": ("eager calls from Python" if args.no_graph else
+                       "one HIP graph of the %d steps, replayed" % args.steps),
         },
         "frac_of_copy": round(value / copy_gbs, 4),
         "copy_ceiling_gbs": round(copy_gbs, 2),

@@ -179,6 +179,43 @@ def test_two_pass_plan_reused_and_streams():
         assert np.array_equal(d_out.cpu().numpy().view(np.uint32), oracle.apply(A, c, x))
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(launch=bm.LAUNCH_ONE_TILE),
+                                dict(launch=bm.LAUNCH_PERSISTENT), dict(launch=bm.LAUNCH_STREAMED),
+                                dict(route=bm.ROUTE_TWO_PASS), dict(route=bm.ROUTE_NAIVE)],
+                         ids=["auto", "one_tile", "persistent", "streamed", "two_pass", "naive"])
+def test_graph_capture_replays(kw):
+    """Executes captured in a HIP graph (as the benchmark times them) give the
+    oracle's result on every replay, with eager work and synchronisation
+    between the replays: the outputs are refilled eagerly before each one."""
+    torch = _torch()
+    n, e = 18, 4
+    A, c = _inv(n, 6060)
+    xs = [wl.fill_random_bytes(n, e, seed=700 + k) for k in range(3)]
+    wants = [oracle.apply(A, c, x).view(np.uint8).reshape(-1) for x in xs]
+    d_ins = [torch.from_numpy(np.ascontiguousarray(x).view(np.uint8).reshape(-1).copy())
+             .to("cuda:0") for x in xs]
+    d_outs = [torch.empty_like(d) for d in d_ins]
+    P = bm.Plan(n, A, c, e, **kw)
+    P(d_ins[0], d_outs[0])  # first call allocates a two-pass plan's scratch
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        h = int(torch.cuda.current_stream().cuda_stream)
+        for d_in, d_out in zip(d_ins, d_outs):
+            assert bm.bmmc_execute(P.handle, d_in, d_out, h) == bm.OK
+        assert bm.bmmc_copy(d_ins[0], d_outs[2], 4096, h) == bm.OK  # the copy kernel too
+    wants[2] = wants[2].copy()
+    wants[2][:4096] = np.ascontiguousarray(xs[0]).view(np.uint8).reshape(-1)[:4096]
+    for rep in range(3):
+        for d_out in d_outs:
+            d_out.fill_(SENTINEL)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (d_out, want) in enumerate(zip(d_outs, wants)):
+            assert np.array_equal(d_out.cpu().numpy(), want), (rep, k, P.describe())
+
+
 def test_execute_rejects_alias_on_device():
     torch = _torch()
     P = bm.Plan(12, wl.bit_reverse_matrix(12), 0, 4)
