@@ -137,6 +137,67 @@ def per_launch_ms(torch, fn, bufs, reps, stream):
     return ms[len(ms) // 2], ms[0], ms[-1]
 
 
+def cpu_baseline(A, c, x, budget_s: float):
+    """The oracle, as it stands, on the host cores: repeated full-array
+    scatters (or index ranges for big arrays) for about budget_s seconds."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n = len(A)
+    N = 1 << n
+    elem = x.nbytes >> n
+    out = np.empty_like(x)
+    # one slice of at most 2^24 indices per call keeps each call short
+    span = min(N, 1 << 24)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        lo = (done * span) % N
+        oracle.apply_range(A, c, x, out, lo, lo + span, threads=threads)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 100000:
+            break
+    moved = 2.0 * done * span * elem
+    # the same calls on one thread, for about a fifth of the budget
+    one, t1 = 0, time.perf_counter()
+    while True:
+        lo = (one * span) % N
+        oracle.apply_range(A, c, x, out, lo, lo + span, threads=1)
+        one += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= budget_s / 5 or one >= 100000:
+            break
+    return {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d oracle calls of 2^%d consecutive input indices each (%.1f s, "
+                      "%d threads), same matrix and data" % (done, span.bit_length() - 1, el,
+                                                             threads),
+            "single_thread_value": round(2.0 * one * span * elem / el1 / 1e9, 4),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+ABLATION_VARIANTS = [
+    # name, plan options; the paper's Figure 9 columns, then this library's default
+    ("naive", dict(route=bm.ROUTE_NAIVE)),
+    ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True)),
+    ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE)),
+    ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
+    ("planner, untuned", dict()),
+    ("tuned (default)", dict(tune=True)),
+]
+
+
 def run_ablation(args, torch):
     """The paper's Figure 9 (speedup of each optimisation over the naive kernel
     for random BPC, bit-reversal and random BMMC) and Figure 11 (the same

@@ -1,0 +1,64 @@
+"""CPU tests of bench.py's host-side parts: the oracle CPU baseline, the
+ablation variants (planned on the host), the HBM-traffic reader and the
+refusal of more than one GPU.  No GPU call is made."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import bmmc_affine_index_amd as bm
+from bmmc_affine_index_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_cpu_baseline_fields():
+    oracle.build()
+    A, c = wl.workload_matrix("c1b")
+    x = wl.workload_data("c1b")
+    r = bench.cpu_baseline(A, c, x, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["value"] > 0 and r["single_thread_value"] > 0 and r["cores"] >= 1
+    assert isinstance(r["cpu_model"], str) and r["host_cpus"] >= 1
+    json.dumps(r)
+
+
+def test_ablation_variants_plan_on_host():
+    for n in (20, 24):
+        kinds = [wl.random_bpc(n, 7), (wl.bit_reverse_matrix(n), 0),
+                 wl.random_bmmc(n, 7, bench.lib_accepts(n))]
+        for A, c in kinds:
+            for name, kw in bench.ABLATION_VARIANTS:
+                kw = {k: v for k, v in kw.items() if k != "tune"}
+                P = bm.Plan(n, A, c, 4, **kw)
+                assert P.info.passes in (1, 2), name
+                P = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS,
+                            **{k: v for k, v in kw.items() if k != "route"})
+                assert P.info.passes in (1, 2)
+
+
+def test_traffic_reader_and_digest():
+    d = bench.kernel_source_digest()
+    assert isinstance(d, str) and len(d) == 16
+    for w in ("c2", "c4"):
+        t = bench.read_traffic(w)
+        assert t is None or t > 0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_help_lists_protocol_options():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0
+    for opt in ("--steps", "--warmup", "--no-graph", "--no-tune", "--ablation", "--perms"):
+        assert opt in r.stdout
