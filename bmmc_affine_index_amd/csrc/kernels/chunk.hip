@@ -75,10 +75,11 @@ namespace {
 template <int UL, int WL>
 int launch_chunk_t(const bmmc_pass_desc &d, const uint8_t *in, uint8_t *out, hipStream_t s) {
     const uint64_t nchunks = uint64_t(1) << d.blk_bits;
-    const uint64_t per = uint64_t(1) << (kChunkNTL + kChunkCPTL);
-    const uint64_t blocks = (nchunks + per - 1) / per;
-    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    const uint64_t per_block = uint64_t(1) << (kChunkNTL + kChunkCPTL);
+    const uint64_t blocks = (nchunks + per_block - 1) / per_block;
+    const uint64_t per = max_blocks_per_launch(1u << kChunkNTL);
+    for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
+        const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
         if (d.cache_hint)
             hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL, true>), dim3((uint32_t)nb),
                                dim3(1 << kChunkNTL), 0, s, in, out, d, b0);

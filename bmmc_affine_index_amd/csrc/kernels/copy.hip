@@ -87,9 +87,9 @@ int launch_copy(const void *in_v, void *out_v, size_t nbytes, hipStream_t s) {
                                dim3(1 << kCopyNTL), 0, s, in, out, n16);
         } else {
             const uint64_t blocks = (n16 + (1u << kCopyNTL) - 1) >> kCopyNTL;
-            for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-                const uint64_t nb =
-                    blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+            const uint64_t per = max_blocks_per_launch(1u << kCopyNTL);
+            for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
+                const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
                 hipLaunchKernelGGL(bmmc_copy_kernel<0>, dim3((uint32_t)nb), dim3(1 << kCopyNTL),
                                    0, s, in, out, n16, b0);
             }
@@ -99,9 +99,9 @@ int launch_copy(const void *in_v, void *out_v, size_t nbytes, hipStream_t s) {
     const uint64_t rest = nbytes - done;
     if (rest) {
         const uint64_t blocks = (rest + 255) / 256;
-        for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-            const uint64_t nb =
-                blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        const uint64_t per = max_blocks_per_launch(256);
+        for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
+            const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
             hipLaunchKernelGGL(bmmc_copy_bytes_kernel, dim3((uint32_t)nb), dim3(256), 0, s,
                                in + done, out + done, rest, b0);
         }

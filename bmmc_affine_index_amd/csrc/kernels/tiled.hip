@@ -324,8 +324,9 @@ template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
         }
     }
     const uint64_t blocks = uint64_t(1) << (a.d->blk_bits - IT);
-    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const uint64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    const uint64_t per = max_blocks_per_launch(C::NT);
+    for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
+        const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
         hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT, NT>), dim3((uint32_t)nb), dim3(C::NT),
                            0, a.s, a.in, a.out, *a.d, b0);
     }

@@ -20,7 +20,12 @@ int launch_copy(const void *in, void *out, size_t nbytes, hipStream_t s);
 // count and launch style.
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch);
 
-// Largest grid (in workgroups) of one launch; bigger passes are split.
-constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 30;
+// The dispatch packet gives the grid size in work-items as a 32-bit count,
+// so one launch covers at most 2^31 work-items here; bigger passes are split
+// into several launches (the kernels take the first workgroup's index).
+constexpr uint64_t kMaxWorkItemsPerLaunch = uint64_t(1) << 31;
+constexpr uint64_t max_blocks_per_launch(uint32_t threads) {
+    return kMaxWorkItemsPerLaunch / threads;
+}
 
 }  // namespace bmmc

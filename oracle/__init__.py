@@ -53,6 +53,9 @@ def _load():
     lib.oracle_gf2_inverse.restype = ctypes.c_int
     lib.oracle_map_index.argtypes = [ctypes.c_int, u64p, ctypes.c_uint64, ctypes.c_uint64]
     lib.oracle_map_index.restype = ctypes.c_uint64
+    lib.oracle_map_indices.argtypes = [ctypes.c_int, u64p, ctypes.c_uint64, u64p, u64p,
+                                       ctypes.c_size_t]
+    lib.oracle_map_indices.restype = None
     lib.oracle_bmmc_apply.argtypes = [ctypes.c_int, u64p, ctypes.c_uint64, ctypes.c_size_t,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_bmmc_apply.restype = ctypes.c_int
@@ -101,6 +104,18 @@ def map_index(A, c: int, i: int) -> int:
     """y = A.i XOR c for one index."""
     a = _rows(A)
     return int(_load().oracle_map_index(len(a), _p(a), int(c), int(i)))
+
+
+def map_indices(A, c: int, idx) -> np.ndarray:
+    """y[k] = A.idx[k] XOR c for an array of indices (uint64)."""
+    a = _rows(A)
+    x = np.ascontiguousarray(np.asarray(idx, dtype=np.uint64))
+    y = np.empty_like(x)
+    _load().oracle_map_indices(len(a), _p(a), ctypes.c_uint64(int(c)),
+                               x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                               y.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                               ctypes.c_size_t(x.size))
+    return y
 
 
 def apply(A, c: int, x: np.ndarray, threads: int = 1) -> np.ndarray:

@@ -91,6 +91,13 @@ uint64_t oracle_map_index(int n, const uint64_t *A, uint64_t c, uint64_t x)
     return y ^ c;
 }
 
+/* y[k] = A.x[k] XOR c for `count` indices: the same definition per index. */
+void oracle_map_indices(int n, const uint64_t *A, uint64_t c, const uint64_t *x, uint64_t *y,
+                        size_t count)
+{
+    for (size_t k = 0; k < count; ++k) y[k] = oracle_map_index(n, A, c, x[k]);
+}
+
 static int check_args(int n, const uint64_t *A, uint64_t c, size_t elem_bytes)
 {
     if (n < 1 || n > 40 || !A || elem_bytes == 0) return ORACLE_BAD_ARG;

@@ -248,3 +248,80 @@ def tiled_write_addresses(d):
                 a ^= d.ld_lds[p]
         out.append(a)
     return out
+
+
+def check_pass_sampled(d, A, c, elem_log2: int, blocks, map_indices) -> int:
+    """Sampled replay for passes too large to replay whole: for each block in
+    `blocks` (tiles of a TILED pass, chunks of a CHUNK/NAIVE pass) every chunk
+    and unit is replayed through the tables, checked for alignment and range
+    (global offsets below 2^(nbits + unit_log2) bytes, LDS slots inside the
+    tile, each slot written and read once), and each unit's destination is
+    compared with `map_indices(A, c, elements)` of the pass's element-level
+    factor (A, c).  Returns the number of units checked."""
+    ul, nb = d.unit_log2, d.nbits
+    U = 1 << ul
+    k = ul - elem_log2  # element-index bits inside a unit
+    total_bytes = np.uint64(U) << np.uint64(nb)
+    checked = 0
+    blocks = np.asarray(sorted(set(int(b) for b in blocks)), dtype=np.uint64)
+    if np.any(blocks >= np.uint64(1 << d.blk_bits)):
+        raise ReplayError("sampled block out of range")
+
+    def expect(src_units, dst_units):
+        want = map_indices(A, c, src_units.astype(np.uint64) << np.uint64(k)) >> np.uint64(k)
+        if not np.array_equal(want, dst_units.astype(np.uint64)):
+            raise ReplayError("unit sent to the wrong place")
+
+    if d.kernel in (KERNEL_CHUNK, KERNEL_NAIVE):
+        wl = d.chunk_log2
+        W = 1 << wl
+        off = _xor_table(blocks, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)
+        if np.any(off % np.uint64(U * W)) or np.any(off + np.uint64(U * W) > total_bytes):
+            raise ReplayError("chunk store misaligned or out of range")
+        for e in range(W):
+            src = blocks * np.uint64(W) + np.uint64(e ^ d.unit_xor)
+            expect(src, off // np.uint64(U) + np.uint64(e))
+            checked += src.size
+        return checked
+    if d.kernel != KERNEL_TILED:
+        raise ReplayError("no sampled replay for kernel %d" % d.kernel)
+
+    t = d.t
+    g = tiled_geometry(ul, t)
+    wl, ntl, jl = g["wl"], g["ntl"], g["jl"]
+    W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
+    cbits = ntl + jl
+    TILE = U << (2 * t)
+    cidx = np.arange(NT * J, dtype=np.uint64)
+    ld_in = _xor_table(cidx, d.ld_in, cbits)
+    ld_lds = _xor_table(cidx, d.ld_lds, cbits)
+    st_out = _xor_table(cidx, d.st_out, cbits)
+    st_lds = _xor_table(cidx, d.st_lds, cbits)
+    if np.any(ld_lds % np.uint64(CB)) or np.any(ld_lds + np.uint64(CB) > np.uint64(TILE)):
+        raise ReplayError("LDS write misaligned or out of range")
+    for b in blocks:
+        in_off = _xor_table(b, d.in_blk, d.blk_bits) ^ ld_in
+        if np.any(in_off % np.uint64(CB)) or np.any(in_off + np.uint64(CB) > total_bytes):
+            raise ReplayError("global read misaligned or out of range")
+        lds = np.full(TILE // U, -1, dtype=np.int64)
+        for e in range(W):
+            slot = (ld_lds // np.uint64(U) + np.uint64(e)).astype(np.int64)
+            if np.any(lds[slot] != -1):
+                raise ReplayError("LDS slot written twice")
+            lds[slot] = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
+        out_off = (_xor_table(b, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)) ^ st_out
+        rbase = (_xor_table(b, d.lds_blk, d.blk_bits) ^ np.uint64(d.lds_c)) ^ st_lds
+        if np.any(out_off % np.uint64(CB)) or np.any(out_off + np.uint64(CB) > total_bytes):
+            raise ReplayError("global write misaligned or out of range")
+        reads = np.zeros(TILE // U, dtype=np.int64)
+        for e in range(W):
+            rd = rbase ^ _xor_table(np.uint64(e), d.st_unit, wl)
+            if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(TILE)):
+                raise ReplayError("LDS read misaligned or out of range")
+            slot = (rd // np.uint64(U)).astype(np.int64)
+            np.add.at(reads, slot, 1)
+            expect(lds[slot], out_off // np.uint64(U) + np.uint64(e))
+            checked += slot.size
+        if np.any(reads != 1) or np.any(lds < 0):
+            raise ReplayError("LDS slot not written and read exactly once")
+    return checked

@@ -439,3 +439,87 @@ def test_workload_c5_random_bpc_records():
             bad, first = oracle.check_sampled(A, c, x, got, _sample_idx(n, 1 << 18, k))
             assert bad == 0, (k, first, P.describe())
         del got
+
+
+# --------------------------------------------------------------------------
+# the largest arrays the ABI accepts, checked on sampled indices on the device
+# --------------------------------------------------------------------------
+
+GPU_MAX_CASES = [  # (n, elem_bytes, kind, plan options, tune)
+    (32, 1, "general", {}, False),                        # 4 GiB per array
+    (32, 1, "general", dict(route=bm.ROUTE_TWO_PASS), False),
+    (32, 2, "transpose", {}, False),                      # 8 GiB
+    (31, 8, "bpc", {}, True),                             # 16 GiB
+    (32, 16, "bitrev", {}, False),                        # 64 GiB = 2^36 bytes
+    (32, 16, "general", {}, True),
+    # 2^28 workgroups of 16 threads: more work-items than one launch may
+    # hold, so the pass is split into several launches
+    (32, 16, "general", dict(tile_log2=2, launch=bm.LAUNCH_ONE_TILE), False),
+]
+
+
+def _max_matrix(kind, n, seed):
+    if kind == "bitrev":
+        return wl.bit_reverse_matrix(n), 0
+    if kind == "transpose":
+        return wl.transpose_matrix(n // 2, n - n // 2), 0
+    if kind == "bpc":
+        return wl.random_bpc(n, seed)
+    return _inv(n, seed)
+
+
+@pytest.mark.parametrize("case", GPU_MAX_CASES, ids=lambda c: "n%d-e%d-%s-%s%s" % (
+    c[0], c[1], c[2], "-".join("%s%s" % kv for kv in sorted(c[3].items())),
+    "-tuned" if c[4] else ""))
+def test_maximum_sizes_sampled(case):
+    """Arrays of up to 2^36 bytes (the ABI's limit): random bytes filled on the
+    device, one execute (after tuning for the tuned cases, whose tuning also
+    writes the output), then 2^20 sampled source indices plus the ends of the
+    array, mapped by the oracle on the host, compared element by element on
+    the device (out[map(i)] == in[i])."""
+    torch = _torch()
+    n, e, kind, kw, tune = case
+    nbytes = e << n
+    scratch = nbytes if kw.get("route") == bm.ROUTE_TWO_PASS else 0
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * nbytes + scratch + (4 << 30):
+        pytest.skip("needs %d GiB of free device memory, %d GiB free"
+                    % ((2 * nbytes + scratch) >> 30, free >> 30))
+    A, c = _max_matrix(kind, n, 4100 + n + e)
+    _note("max n=%d e=%d %s %s: allocate and fill %d GiB" % (n, e, kind, kw, nbytes >> 30))
+    d_in = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(n * 131 + e)
+    step = 1 << 30
+    for off in range(0, nbytes, step):
+        d_in[off:off + step].random_(0, 256, generator=gen)
+    d_out = torch.full_like(d_in, SENTINEL)
+    P = bm.Plan(n, A, c, e, **kw)
+    _note("max: plan %s" % P.describe())
+    if tune:
+        P.tune(d_in, d_out, reps=1)
+        torch.cuda.synchronize()
+        _note("max: tuned %s" % P.describe())
+        d_out.fill_(SENTINEL)
+    P(d_in, d_out)
+    torch.cuda.synchronize()
+    _note("max: check")
+    N = 1 << n
+    rng = np.random.Generator(np.random.PCG64(n + e))
+    idx = np.concatenate([np.array([0, 1, N - 2, N - 1, N // 2], dtype=np.uint64),
+                          rng.integers(0, N, size=1 << 20, dtype=np.uint64)])
+    dst = oracle.map_indices(A, c, idx)
+    src_t = torch.from_numpy(idx.astype(np.int64)).to("cuda:0")
+    dst_t = torch.from_numpy(dst.astype(np.int64)).to("cuda:0")
+    vin, vout = d_in.view(N, e), d_out.view(N, e)
+    same = (vin.index_select(0, src_t) == vout.index_select(0, dst_t)).all(dim=1)
+    bad = int((~same).sum())
+    assert bad == 0, (bad, P.describe())
+    # the copy ceiling at the same size
+    d_out.fill_(SENTINEL)
+    assert bm.bmmc_copy(d_in, d_out, nbytes, None) == bm.OK
+    torch.cuda.synchronize()
+    assert bool((vin.index_select(0, src_t) == vout.index_select(0, src_t)).all())
+    del d_in, d_out, vin, vout
+    torch.cuda.empty_cache()

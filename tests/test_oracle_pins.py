@@ -86,6 +86,27 @@ def test_golden_maps():
     assert seen == 2
 
 
+def test_map_indices_is_map_index_per_index():
+    """The batched map used for sampled checks at large n gives the printed
+    examples and agrees with the one-index map everywhere it is sampled,
+    including indices with bit 31 set."""
+    for kind, d in _golden():
+        if kind == "map":
+            A = _matrix_for(d["case"], d)
+            assert int(oracle.map_indices(A, 0, [d["in"]])[0]) == d["out"]
+    A = wl.bit_reverse_matrix(15)
+    ys = oracle.map_indices(A, 0, [1 << k for k in range(15)])
+    assert [int(y) for y in ys] == [1 << (14 - k) for k in range(15)]
+    rng = np.random.Generator(np.random.PCG64(77))
+    for n in (5, 20, 32):
+        A, c = wl.random_bmmc(n, n, lambda r: oracle.rank(r) == len(r))
+        idx = rng.integers(0, 1 << n, size=500, dtype=np.uint64)
+        idx[:2] = [0, (1 << n) - 1]
+        ys = oracle.map_indices(A, c, idx)
+        assert [int(y) for y in ys] == [oracle.map_index(A, c, int(i)) for i in idx]
+    assert oracle.map_indices(A, c, np.zeros(0, dtype=np.uint64)).size == 0
+
+
 def test_golden_reverse16():
     facts = [d for k, d in _golden() if k == "reverse"]
     assert facts

@@ -11,8 +11,8 @@ import oracle
 import bmmc_affine_index_amd as bm
 from bmmc_affine_index_amd import workloads as wl
 
-from emulate import (ReplayError, bank_cycles, run_plan_on_host, tiled_read_addresses,
-                     tiled_write_addresses)
+from emulate import (ReplayError, bank_cycles, check_pass_sampled, run_plan_on_host,
+                     tiled_read_addresses, tiled_write_addresses)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -469,3 +469,84 @@ def test_locality_block_orders(seed):
     # that the concurrent picks already span
     low = _top_bits(d6.in_blk, m)[:m - g]
     assert low == sorted(low) and set(low) <= set(ins)
+
+
+# --------------------------------------------------------------------------
+# Maximum sizes: sampled replay of the kernel tables against the oracle
+# --------------------------------------------------------------------------
+
+MAX_CASES = [  # (n, elem_bytes, kind, plan options): up to 2^36 bytes per array
+    (32, 1, "general", {}),
+    (32, 1, "general", dict(launch=bm.LAUNCH_ONE_TILE)),
+    (32, 1, "general", dict(route=bm.ROUTE_TWO_PASS)),
+    (32, 16, "general", {}),
+    (32, 16, "general", dict(launch=bm.LAUNCH_ONE_TILE, block_map=5)),
+    (32, 16, "bitrev", {}),
+    (32, 4, "bitrev", dict(tile_log2=7, block_map=6)),
+    (31, 8, "bpc", dict(block_map=3)),
+    (32, 2, "transpose", dict(launch=bm.LAUNCH_STREAMED)),
+    (32, 1, "general", dict(route=bm.ROUTE_NAIVE)),
+    (32, 16, "general", dict(tile_log2=2, launch=bm.LAUNCH_ONE_TILE)),
+]
+
+
+def _max_matrix(kind, n, seed):
+    if kind == "bitrev":
+        return wl.bit_reverse_matrix(n), 0
+    if kind == "transpose":
+        return wl.transpose_matrix(n // 2, n - n // 2), 0
+    if kind == "bpc":
+        return wl.random_bpc(n, seed)
+    return wl.random_bmmc(n, seed, lambda r: oracle.rank(r) == n)
+
+
+def _sampled_blocks(nblk, seed, count=48):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    edge = [0, 1, 2, nblk - 1, nblk - 2, nblk // 2, nblk // 2 - 1]
+    return [b for b in edge if 0 <= b < nblk] + [int(v) for v in rng.integers(0, nblk, size=count)]
+
+
+@pytest.mark.parametrize("case", MAX_CASES, ids=lambda c: "n%d-e%d-%s-%s" % (
+    c[0], c[1], c[2], "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
+def test_maximum_size_plans_sampled(case):
+    """Plans at the largest sizes the ABI accepts (2^32 elements, 2^36 bytes):
+    sampled tiles or chunks of every pass, including the first and last
+    blocks, replayed through the tables and compared with the oracle's map
+    of that pass's factor; all offsets must stay below the array's size."""
+    n, e, kind, kw = case
+    A, c = _max_matrix(kind, n, 3100 + n + e)
+    P = bm.Plan(n, A, c, e, **kw)
+    assert (e << n) <= 1 << 36
+    elog = e.bit_length() - 1
+    total = 0
+    for k, d in enumerate(P.passes()):
+        fa, fc = P.factors()[k]
+        total += check_pass_sampled(d, fa, fc, elog, _sampled_blocks(1 << d.blk_bits, k + n),
+                                    oracle.map_indices)
+    assert total > 0
+
+
+def test_sampled_replay_catches_planted_mistakes():
+    """A wrong table entry, a wrong factor or a misaligned base each fail the
+    sampled replay (the mistakes are planted in the host copy of the tables)."""
+    n, e = 24, 4
+    A, c = _max_matrix("general", n, 9)
+    P = bm.Plan(n, A, c, e)
+    d = P.passes()[0]
+    fa, fc = P.factors()[0]
+    blocks = _sampled_blocks(1 << d.blk_bits, 1)
+    assert check_pass_sampled(d, fa, fc, 2, blocks, oracle.map_indices) > 0
+    with pytest.raises(ReplayError):
+        check_pass_sampled(d, fa, fc ^ 1, 2, blocks, oracle.map_indices)
+    bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+    bad.out_blk[3] ^= bad.out_blk[4]
+    with pytest.raises(ReplayError):
+        check_pass_sampled(bad, fa, fc, 2, blocks, oracle.map_indices)
+    bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+    bad.in_blk[0] ^= 16
+    with pytest.raises(ReplayError):
+        check_pass_sampled(bad, fa, fc, 2, blocks, oracle.map_indices)
+    bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+    bad.st_lds[2], bad.st_lds[3] = bad.st_lds[3], bad.st_lds[2]
+    with pytest.raises(ReplayError):
+        check_pass_sampled(bad, fa, fc, 2, blocks, oracle.map_indices)
