@@ -429,7 +429,10 @@ def main():
                     raise bm.BmmcError(st, "bmmc_execute")
             msk = time_loop(torch, stepk, bufs, args.steps, args.warmup, stream, graph=graph)
             vals.append(algo_bytes / (msk * 1e-3) / 1e9)
-            print("perm %d: %.1f GB/s" % (k, vals[-1]), file=sys.stderr, flush=True)
+            dk = pk.describe()
+            print("perm %d: %.1f GB/s (%s t=%s order %s)" % (k, vals[-1], dk["kernels"][-1],
+                                                            dk["tile_log2"], dk["block_map"]),
+                  file=sys.stderr, flush=True)
         sv = sorted(vals)
         perm_stats = {"perms": len(vals), "min_gbs": round(sv[0], 2),
                       "median_gbs": round(sv[len(sv) // 2], 2), "max_gbs": round(sv[-1], 2),

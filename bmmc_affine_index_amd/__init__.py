@@ -45,7 +45,7 @@ EXPORTED = (
     "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_plan_tune", "bmmc_plan_tune_pairs",
     "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
-    "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_parm_matrix",
+    "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_plan_get_options", "bmmc_parm_matrix",
     "bmmc_matrix_inverse", "bmmc_tensor_permute_matrix",
 )
 
@@ -140,6 +140,8 @@ def lib():
     L.bmmc_plan_get_pass.argtypes = [ctypes.c_void_p, ctypes.c_int,
                                      ctypes.POINTER(bmmc_pass_desc)]
     L.bmmc_plan_get_pass.restype = ctypes.c_int
+    L.bmmc_plan_get_options.argtypes = [ctypes.c_void_p, ctypes.POINTER(bmmc_plan_options)]
+    L.bmmc_plan_get_options.restype = ctypes.c_int
     L.bmmc_parm_matrix.argtypes = [ctypes.c_int, ctypes.c_uint64, u64p]
     L.bmmc_parm_matrix.restype = ctypes.c_int
     L.bmmc_matrix_inverse.argtypes = [ctypes.c_int, u64p, u64p]
@@ -262,6 +264,14 @@ def bmmc_plan_get_factor(plan: int, pass_index: int, n: int):
     return [int(a) for a in A], int(c.value)
 
 
+def bmmc_plan_get_options(plan: int) -> dict:
+    o = bmmc_plan_options()
+    st = lib().bmmc_plan_get_options(plan, ctypes.byref(o))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_get_options")
+    return {name: int(getattr(o, name)) for name, _ in bmmc_plan_options._fields_}
+
+
 def bmmc_plan_get_pass(plan: int, pass_index: int) -> bmmc_pass_desc:
     d = bmmc_pass_desc()
     st = lib().bmmc_plan_get_pass(plan, int(pass_index), ctypes.byref(d))
@@ -329,6 +339,11 @@ class Plan:
     @property
     def nbytes(self) -> int:
         return self.elem_bytes << self.n
+
+    def options(self) -> dict:
+        """Keyword arguments that rebuild this plan's current tables
+        (bmmc_plan_get_options): ``Plan(n, A, c, elem_bytes, **p.options())``."""
+        return bmmc_plan_get_options(self.handle)
 
     def passes(self):
         return [bmmc_plan_get_pass(self.handle, k) for k in range(self.info.passes)]

@@ -292,6 +292,27 @@ int bmmc_plan_get_info(const bmmc_plan *p, bmmc_plan_info *info) {
     return BMMC_OK;
 }
 
+int bmmc_plan_get_options(const bmmc_plan *p, bmmc_plan_options *opt) {
+    if (!p || !opt) return BMMC_ERR_INVALID_ARG;
+    bmmc_plan_options o = p->opt;  // the caller's, then every choice made explicit
+    for (int k = 0; k < p->npasses; ++k) {
+        const bmmc_pass_desc &d = p->pass[k];
+        if (d.kernel != BMMC_KERNEL_TILED) continue;
+        o.tile_log2 = d.t;
+        o.launch = d.launch;
+        o.iters_log2 = d.iters_log2;
+        o.block_map = d.block_map;
+        o.cache_hint = d.cache_hint ? 2 : 1;
+        if (d.launch != BMMC_LAUNCH_ONE_TILE) {
+            o.grid_log2 = d.grid_log2;
+            o.walk = d.walk;
+        }
+        if (d.launch == BMMC_LAUNCH_STREAMED) o.depth = d.depth;
+    }
+    *opt = o;
+    return BMMC_OK;
+}
+
 int bmmc_plan_get_factor(const bmmc_plan *p, int pass, uint64_t *A_out, uint64_t *c_out) {
     if (!p || !A_out || !c_out || pass < 0 || pass >= p->npasses) return BMMC_ERR_INVALID_ARG;
     std::memcpy(A_out, p->factor_A[pass], sizeof(uint64_t) * (size_t)p->n);

@@ -249,6 +249,13 @@ const char *bmmc_status_string(int status);
 /* Describe a plan (host-only). */
 int bmmc_plan_get_info(const bmmc_plan *plan, bmmc_plan_info *info);
 
+/* The options that rebuild this plan's current kernel tables: the caller's
+ * options with every choice the planner or bmmc_plan_tune made written out
+ * (tile side, launch style, grid, walk, depth, tile order, cache hint), so
+ * bmmc_plan_create_ex(n, A, c, elem_bytes, opt) gives the same tables without
+ * timing anything again.  Host-only. */
+int bmmc_plan_get_options(const bmmc_plan *plan, bmmc_plan_options *opt);
+
 /* The matrix and complement that pass `pass` applies, at element granularity
  * (n rows); the passes compose to the planned (A, c).  Host-only. */
 int bmmc_plan_get_factor(const bmmc_plan *plan, int pass, uint64_t *A_out, uint64_t *c_out);

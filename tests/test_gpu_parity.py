@@ -269,6 +269,30 @@ def test_tune_keeps_results_and_fixed_options(case):
             assert (d.kernel, d.launch, d.block_map) in before
 
 
+@pytest.mark.parametrize("kind,n,e", [("general", 20, 4), ("bpc", 20, 16), ("bitrev", 22, 4)])
+def test_tuned_options_rebuild_the_tuned_plan(kind, n, e):
+    """After tuning, the plan's options rebuild the tuned tables exactly (no
+    timing), and the rebuilt plan gives the oracle's result."""
+    import ctypes
+    torch = _torch()
+    A, c = _matrix(kind, n, 8100 + n)
+    x = wl.fill_random_bytes(n, e, seed=n + e)
+    raw = np.ascontiguousarray(x).view(np.uint8).reshape(-1)
+    d_in = torch.from_numpy(raw.copy()).to("cuda:0")
+    d_out = torch.full_like(d_in, SENTINEL)
+    P = bm.Plan(n, A, c, e)
+    P.tune(d_in, d_out, reps=2)
+    Q = bm.Plan(n, A, c, e, **P.options())
+    for dp, dq in zip(P.passes(), Q.passes()):
+        assert (ctypes.string_at(ctypes.addressof(dp), ctypes.sizeof(dp)) ==
+                ctypes.string_at(ctypes.addressof(dq), ctypes.sizeof(dq)))
+    d_out.fill_(SENTINEL)
+    Q(d_in, d_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_out.cpu().numpy().view(x.dtype).reshape(x.shape),
+                          oracle.apply(A, c, x)), Q.describe()
+
+
 @pytest.mark.parametrize("route", [bm.ROUTE_AUTO, bm.ROUTE_TWO_PASS])
 def test_tune_over_rotating_pairs(route):
     """bmmc_plan_tune_pairs: outs[0] holds the permutation of ins[0]; every

@@ -550,3 +550,45 @@ def test_sampled_replay_catches_planted_mistakes():
     bad.st_lds[2], bad.st_lds[3] = bad.st_lds[3], bad.st_lds[2]
     with pytest.raises(ReplayError):
         check_pass_sampled(bad, fa, fc, 2, blocks, oracle.map_indices)
+
+
+
+def _desc_bytes(d):
+    import ctypes
+    return ctypes.string_at(ctypes.addressof(d), ctypes.sizeof(d))
+
+
+@pytest.mark.parametrize("case", [
+    ("general", 20, 4, {}), ("general", 16, 1, dict(route=bm.ROUTE_TWO_PASS)),
+    ("bitrev", 24, 4, {}), ("bitrev", 12, 16, {}), ("bpc", 27, 16, {}),
+    ("general", 18, 8, dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
+    ("general", 22, 2, dict(block_map=5, tile_log2=7)), ("bpc", 14, 4, dict(no_swizzle=1)),
+    ("general", 20, 4, dict(launch=bm.LAUNCH_STREAMED, depth=1, grid_log2=6, walk=2)),
+    ("general", 9, 4, dict(route=bm.ROUTE_NAIVE)), ("identity", 12, 4, {}),
+    ("complement", 12, 4, {}), ("general", 30, 4, dict(cache_hint=1)),
+], ids=lambda c: "%s-n%d-e%d-%s" % (c[0], c[1], c[2],
+                                    "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
+def test_options_rebuild_the_same_tables(case):
+    """bmmc_plan_get_options writes every choice out; creating a plan from
+    them gives byte-identical kernel tables, and the explicit options are a
+    fixed point."""
+    kind, n, e, kw = case
+    if kind == "identity":
+        A, c = wl.identity_matrix(n), 0
+    elif kind == "complement":
+        A, c = wl.identity_matrix(n), 0x5A5 & ((1 << n) - 1)
+    elif kind == "bitrev":
+        A, c = wl.bit_reverse_matrix(n), 0
+    elif kind == "bpc":
+        A, c = wl.random_bpc(n, n)
+    else:
+        A, c = wl.random_bmmc(n, n, lambda r: oracle.rank(r) == n)
+    P = bm.Plan(n, A, c, e, **kw)
+    opts = P.options()
+    Q = bm.Plan(n, A, c, e, **opts)
+    assert Q.info.passes == P.info.passes and Q.info.tile_log2 == P.info.tile_log2
+    for dp, dq in zip(P.passes(), Q.passes()):
+        assert _desc_bytes(dp) == _desc_bytes(dq)
+    assert Q.options() == opts
+    for k, v in kw.items():
+        assert opts[k] == v
