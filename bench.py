@@ -277,7 +277,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--kind", default=None,
-                    choices=["bitrev", "transpose", "bpc", "bmmc", "blockperm"],
+                    choices=["bitrev", "transpose", "bpc", "bmmc", "blockperm", "reverse"],
                     help="custom workload instead of --workload: the matrix kind "
                          "(blockperm: identity on the low --seg-log2 bits, random on the rest)")
     ap.add_argument("--seg-log2", type=int, default=10, help="blockperm: block size, log2 elements")
@@ -339,6 +339,9 @@ def main():
             A, c = wl.transpose_matrix(n // 2, n - n // 2), 0
         elif args.kind == "bpc":
             A, c = wl.random_bpc(n, args.seed)
+        elif args.kind == "reverse":
+            # the whole array reversed: A = I with every complement bit set
+            A, c = wl.identity_matrix(n), (1 << n) - 1
         elif args.kind == "blockperm":
             sl = args.seg_log2
             Q, _ = wl.random_bmmc(n - sl, args.seed, lib_accepts(n - sl))

@@ -479,10 +479,15 @@ GPU_MAX_CASES = [  # (n, elem_bytes, kind, plan options, tune)
     # 2^28 workgroups of 16 threads: more work-items than one launch may
     # hold, so the pass is split into several launches
     (32, 16, "general", dict(tile_log2=2, launch=bm.LAUNCH_ONE_TILE), False),
+    # the naive pass: 2^24 one-byte groups of 256 lanes, also split in two launches
+    (32, 1, "general", dict(route=bm.ROUTE_NAIVE), False),
+    (32, 4, "reverse", {}, False),                        # complement only: chunk kernel
 ]
 
 
 def _max_matrix(kind, n, seed):
+    if kind == "reverse":
+        return wl.identity_matrix(n), (1 << n) - 1
     if kind == "bitrev":
         return wl.bit_reverse_matrix(n), 0
     if kind == "transpose":
