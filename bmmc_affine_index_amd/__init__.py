@@ -31,7 +31,7 @@ KIND_IDENTITY, KIND_BPC, KIND_TILED, KIND_GENERAL = 0, 1, 2, 3
 KIND_NAMES = {0: "identity", 1: "bpc", 2: "tiled", 3: "general"}
 ROUTE_AUTO, ROUTE_NAIVE, ROUTE_TWO_PASS, ROUTE_FUSED = 0, 1, 2, 3
 ROUTE_NAMES = {0: "auto", 1: "naive", 2: "two_pass", 3: "fused"}
-KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE = 0, 1, 2, 3
+KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE, KERNEL_CHUNK_SCATTER = 0, 1, 2, 3, 4
 LAUNCH_AUTO, LAUNCH_ONE_TILE, LAUNCH_PERSISTENT, LAUNCH_STREAMED = 0, 1, 2, 3
 WALK_AUTO, WALK_RANGES, WALK_INTERLEAVED = 0, 1, 2
 
@@ -82,7 +82,7 @@ class bmmc_pass_desc(ctypes.Structure):
                 ("ld_lds", ctypes.c_uint32 * MAX_CHUNK_BITS),
                 ("st_out", ctypes.c_uint64 * MAX_CHUNK_BITS),
                 ("st_lds", ctypes.c_uint32 * MAX_CHUNK_BITS),
-                ("st_unit", ctypes.c_uint32 * 4)]
+                ("st_unit", ctypes.c_uint32 * 4), ("in_c", ctypes.c_uint64)]
 
 
 class BmmcError(RuntimeError):
@@ -394,7 +394,8 @@ class Plan:
         i = self.info
         launch = [{1: "one_tile", 2: "persistent", 3: "streamed"}.get(d.launch, "-")
                   if d.kernel == KERNEL_TILED
-                  else {0: "copy", 1: "chunk", 3: "naive"}.get(d.kernel, "?") for d in self.passes()]
+                  else {0: "copy", 1: "chunk", 3: "naive", 4: "chunk_scatter"}.get(d.kernel, "?")
+                  for d in self.passes()]
         grid = [d.grid_log2 for d in self.passes() if d.kernel == KERNEL_TILED]
         walk = [{1: "ranges", 2: "interleaved"}.get(d.walk) for d in self.passes()
                 if d.kernel == KERNEL_TILED and d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED)]

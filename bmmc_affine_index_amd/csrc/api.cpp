@@ -20,6 +20,7 @@ int run_pass(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) 
     case BMMC_KERNEL_COPY:
         return bmmc::launch_copy(in, out, (size_t)1 << (d.nbits + d.unit_log2), s);
     case BMMC_KERNEL_CHUNK:
+    case BMMC_KERNEL_CHUNK_SCATTER:
     case BMMC_KERNEL_NAIVE:
         return bmmc::launch_chunk(d, in, out, s);
     case BMMC_KERNEL_TILED:

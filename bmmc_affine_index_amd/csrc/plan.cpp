@@ -634,12 +634,22 @@ void build_chunk(const Mat &A, u64 c, int ulog2, int wl, int kernel, bmmc_pass_d
     d->nbits = nb;
     d->chunk_log2 = wl;
     d->blk_bits = nb - wl;
-    for (int k = 0; k < nb - wl; ++k) d->out_blk[k] = A.apply(u64(1) << (k + wl)) << ulog2;
-    d->out_c = (c & ~low_mask(wl)) << ulog2;
     d->unit_xor = (int32_t)(c & low_mask(wl));
+    if (kernel == BMMC_KERNEL_CHUNK) {
+        // gather: output chunk y comes from input A^-1.(y XOR c); A keeps
+        // the low wl bits, so A^-1 maps chunk bits to chunk bits and the
+        // complement's low bits permute the units inside a chunk
+        Mat Ainv;
+        inverse(A, Ainv);
+        for (int k = 0; k < nb - wl; ++k) d->in_blk[k] = Ainv.apply(u64(1) << (k + wl)) << ulog2;
+        d->in_c = (Ainv.apply(c) & ~low_mask(wl)) << ulog2;
+    } else {
+        for (int k = 0; k < nb - wl; ++k) d->out_blk[k] = A.apply(u64(1) << (k + wl)) << ulog2;
+        d->out_c = (c & ~low_mask(wl)) << ulog2;
+    }
     // whole chunks stream through with non-temporal hints; the naive pass's
     // scattered one-unit stores measured far slower with them
-    d->cache_hint = kernel == BMMC_KERNEL_CHUNK ? 3 : 0;
+    d->cache_hint = kernel == BMMC_KERNEL_NAIVE ? 0 : 3;
 }
 
 void build_copy(int nb, int ulog2, bmmc_pass_desc *d) {
@@ -755,7 +765,10 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     const int sid = low_identity_bits(m.A);
     if (sid >= t) {
         const int wl = std::min(4 - m.ulog2, sid);
-        build_chunk(m.A, m.c, m.ulog2, wl, BMMC_KERNEL_CHUNK, &p->pass[0]);
+        // complement only (A = I after the unit merge): read in order, store
+        // reversed; segment moves: write in order, gather
+        build_chunk(m.A, m.c, m.ulog2, wl,
+                    ident ? BMMC_KERNEL_CHUNK_SCATTER : BMMC_KERNEL_CHUNK, &p->pass[0]);
         single(BMMC_ROUTE_FUSED);
         return BMMC_OK;
     }

@@ -57,9 +57,11 @@ extern "C" {
 
 /* ---- kernels a pass may run -------------------------------------------- */
 #define BMMC_KERNEL_COPY 0  /* identity order */
-#define BMMC_KERNEL_CHUNK 1 /* chunks move as units: segment relabel / complement only */
+#define BMMC_KERNEL_CHUNK 1 /* chunks move as units (a gather): segment relabel, block moves */
 #define BMMC_KERNEL_TILED 2 /* LDS-staged tile pass */
 #define BMMC_KERNEL_NAIVE 3 /* one unit per lane */
+#define BMMC_KERNEL_CHUNK_SCATTER 4 /* chunks read in order, stored at permuted places:
+                                       complement-only maps (A = I, c != 0) */
 
 #define BMMC_MAX_N 32      /* largest index width accepted */
 #define BMMC_MAX_BITS 36   /* index bits at byte-merged unit granularity */
@@ -137,10 +139,15 @@ typedef struct bmmc_plan_info {
  * XOR_k out_blk[k] XOR out_c XOR_p st_out[p], its unit e read from LDS
  * address XOR_k lds_blk[k] XOR lds_c XOR_p st_lds[p] XOR_b st_unit[b] over
  * the set bits b of e.
- * CHUNK: chunk index bit k moves the output by out_blk[k]; out_c is the
- * constant; unit_xor permutes the units inside a chunk (unit e goes to
- * e XOR unit_xor).  The input chunk is read at chunk_index * chunk_bytes.
- * NAIVE: unit index bit k moves the output by out_blk[k]; out_c constant.
+ * CHUNK (a gather): output chunk y is written at y * chunk_bytes and read
+ * from input offset XOR_k in_blk[k] over the set bits k of y, XOR in_c; unit
+ * e of the output chunk is unit e XOR unit_xor of the input chunk.  Writing
+ * in order and reading in permuted order is the faster way round on MI355X.
+ * NAIVE and CHUNK_SCATTER (scatters): input chunk (one unit for NAIVE)
+ * index bit k moves the output by out_blk[k]; out_c is the constant; the
+ * input chunk is read at chunk_index * chunk_bytes; units inside a chunk as
+ * for CHUNK.  For complement-only maps the scatter is the faster form (a
+ * gather would read each wave's chunks in descending order).
  * COPY: nothing but nbits/unit_log2. */
 #define BMMC_MAX_CHUNK_BITS 16
 typedef struct bmmc_pass_desc {
@@ -170,6 +177,7 @@ typedef struct bmmc_pass_desc {
     uint64_t st_out[BMMC_MAX_CHUNK_BITS];
     uint32_t st_lds[BMMC_MAX_CHUNK_BITS];
     uint32_t st_unit[4];
+    uint64_t in_c;       /* CHUNK: input offset of output chunk 0 */
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE = 0, 1, 2, 3
+KERNEL_COPY, KERNEL_CHUNK, KERNEL_TILED, KERNEL_NAIVE, KERNEL_CHUNK_SCATTER = 0, 1, 2, 3, 4
 
 
 def _xor_table(vals: np.ndarray, table, nbits: int) -> np.ndarray:
@@ -163,14 +163,30 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
 
 
 def replay_chunk(d) -> np.ndarray:
+    """CHUNK (a gather): output chunk x is read from XOR in_blk over x's bits
+    XOR in_c; NAIVE and CHUNK_SCATTER (scatters): input chunk x is stored at
+    XOR out_blk over x's bits XOR out_c.  Either way unit e of the output chunk is unit
+    e XOR unit_xor of the input chunk."""
     ul, nb, wl = d.unit_log2, d.nbits, d.chunk_log2
     U, W = 1 << ul, 1 << wl
     nchunks = 1 << d.blk_bits
     x = np.arange(nchunks, dtype=np.uint64)
+    result = np.full(1 << nb, -1, dtype=np.int64)
+    if d.kernel == KERNEL_CHUNK:
+        src = _xor_table(x, d.in_blk, d.blk_bits) ^ np.uint64(d.in_c)
+        if np.any(src % np.uint64(U * W)) or np.any(src // np.uint64(U) >= np.uint64(1 << nb)):
+            raise ReplayError("chunk load misaligned or out of range")
+        seen = np.zeros(nchunks, dtype=np.int64)
+        np.add.at(seen, (src // np.uint64(U * W)).astype(np.int64), 1)
+        if np.any(seen != 1):
+            raise ReplayError("input chunk not read exactly once")
+        for e in range(W):
+            dst = (x * np.uint64(W) + np.uint64(e)).astype(np.int64)
+            result[dst] = (src // np.uint64(U) + np.uint64(e ^ d.unit_xor)).astype(np.int64)
+        return result
     off = _xor_table(x, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)
     if np.any(off % np.uint64(U * W)):
         raise ReplayError("misaligned chunk store")
-    result = np.full(1 << nb, -1, dtype=np.int64)
     for e in range(W):
         dst = (off // np.uint64(U) + np.uint64(e)).astype(np.int64)
         src = (x * np.uint64(W) + np.uint64(e ^ d.unit_xor)).astype(np.int64)
@@ -185,7 +201,7 @@ def replay_chunk(d) -> np.ndarray:
 def replay_pass(d) -> np.ndarray:
     if d.kernel == KERNEL_TILED:
         return replay_tiled(d)
-    if d.kernel in (KERNEL_CHUNK, KERNEL_NAIVE):
+    if d.kernel in (KERNEL_CHUNK, KERNEL_NAIVE, KERNEL_CHUNK_SCATTER):
         return replay_chunk(d)
     if d.kernel == KERNEL_COPY:
         return np.arange(1 << d.nbits, dtype=np.int64)
@@ -272,7 +288,18 @@ def check_pass_sampled(d, A, c, elem_log2: int, blocks, map_indices) -> int:
         if not np.array_equal(want, dst_units.astype(np.uint64)):
             raise ReplayError("unit sent to the wrong place")
 
-    if d.kernel in (KERNEL_CHUNK, KERNEL_NAIVE):
+    if d.kernel == KERNEL_CHUNK:  # gather: sampled output chunks
+        wl = d.chunk_log2
+        W = 1 << wl
+        src = _xor_table(blocks, d.in_blk, d.blk_bits) ^ np.uint64(d.in_c)
+        if np.any(src % np.uint64(U * W)) or np.any(src + np.uint64(U * W) > total_bytes):
+            raise ReplayError("chunk load misaligned or out of range")
+        for e in range(W):
+            expect(src // np.uint64(U) + np.uint64(e ^ d.unit_xor),
+                   blocks * np.uint64(W) + np.uint64(e))
+            checked += blocks.size
+        return checked
+    if d.kernel in (KERNEL_NAIVE, KERNEL_CHUNK_SCATTER):  # scatter: sampled input chunks
         wl = d.chunk_log2
         W = 1 << wl
         off = _xor_table(blocks, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)

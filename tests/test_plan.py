@@ -159,7 +159,12 @@ def test_classification_of_named_cases():
     P = bm.Plan(12, wl.identity_matrix(12), 0, 4)
     assert P.info.kind == bm.KIND_IDENTITY and P.passes()[0].kernel == bm.KERNEL_COPY
     P = bm.Plan(12, wl.identity_matrix(12), 0xABC, 4)
-    assert P.info.kind == bm.KIND_IDENTITY and P.passes()[0].kernel == bm.KERNEL_CHUNK
+    assert P.info.kind == bm.KIND_IDENTITY and P.passes()[0].kernel == bm.KERNEL_CHUNK_SCATTER
+    # whole 2^10-element blocks moved by a random map of the block index: a gather
+    Q, _ = _inv(10, 10)
+    A = [1 << r for r in range(10)] + [int(q) << 10 for q in Q]
+    P = bm.Plan(20, A, 5, 4)
+    assert P.passes()[0].kernel == bm.KERNEL_CHUNK
     A, c = _inv(20, 20)
     P = bm.Plan(20, A, c, 4)
     assert P.info.kind == bm.KIND_GENERAL and P.info.passes == 1
