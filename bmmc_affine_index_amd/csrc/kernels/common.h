@@ -195,6 +195,38 @@ __device__ __forceinline__ T xor_bits_uniform(const T *tab, uint64_t v) {
     return acc;
 }
 
+// XOR over the 64 lanes of a wave (every lane must be active); the result is
+// the same in every lane.  Row-wise inclusive XOR scan with DPP shifts of 1,
+// 2, 4 and 8 (invalid sources read as 0), then the row totals are carried
+// across rows with the row_bcast:15 and row_bcast:31 patterns; lane 63 then
+// holds the total.
+__device__ __forceinline__ uint32_t wave_xor_u32(uint32_t v) {
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, true);  // row_bcast:15
+    v ^= __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, true);  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// xor_bits_uniform computed by a whole wave: lane k loads entry k when bit k
+// of v is set, and the wave XOR-reduces.  One vector load replaces a chain of
+// dependent scalar loads, one per set bit, which a workgroup alone on its
+// compute unit pays in full at the start of a short kernel.  Every lane of
+// the wave must be active.
+template <typename T>
+__device__ __forceinline__ T xor_bits_wave(const T *tab, uint64_t v) {
+    const uint32_t lane = __lane_id();
+    const T e = (lane < BMMC_MAX_BITS && ((v >> lane) & 1u)) ? tab[lane] : T(0);
+    if constexpr (sizeof(T) == 8) {
+        const uint32_t lo = wave_xor_u32((uint32_t)e), hi = wave_xor_u32((uint32_t)(e >> 32));
+        return ((T)hi << 32) | lo;
+    } else {
+        return (T)wave_xor_u32((uint32_t)e);
+    }
+}
+
 // XOR of the first NB table entries selected by the bits of a per-lane value.
 template <int NB, typename T>
 __device__ __forceinline__ T xor_bits_lane(const T *tab, uint32_t v) {
