@@ -214,17 +214,34 @@ __device__ __forceinline__ uint32_t wave_xor_u32(uint32_t v) {
 // of v is set, and the wave XOR-reduces.  One vector load replaces a chain of
 // dependent scalar loads, one per set bit, which a workgroup alone on its
 // compute unit pays in full at the start of a short kernel.  Every lane of
-// the wave must be active.
+// the wave must be active.  The load and the reduction are apart so that a
+// kernel can issue the loads of several such sums before it waits for any.
 template <typename T>
-__device__ __forceinline__ T xor_bits_wave(const T *tab, uint64_t v) {
+__device__ __forceinline__ T wave_load(const T *tab) {
+    // every lane loads an in-bounds entry, so no branch splits the waits
     const uint32_t lane = __lane_id();
-    const T e = (lane < BMMC_MAX_BITS && ((v >> lane) & 1u)) ? tab[lane] : T(0);
+    return tab[lane < BMMC_MAX_BITS ? lane : BMMC_MAX_BITS - 1];
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_select_xor(T x, uint64_t v) {
+    const uint32_t lane = __lane_id();
+    const T e = (lane < BMMC_MAX_BITS && ((v >> lane) & 1u)) ? x : T(0);
     if constexpr (sizeof(T) == 8) {
         const uint32_t lo = wave_xor_u32((uint32_t)e), hi = wave_xor_u32((uint32_t)(e >> 32));
         return ((T)hi << 32) | lo;
     } else {
         return (T)wave_xor_u32((uint32_t)e);
     }
+}
+
+// The same sum with the load under the lane's condition: lanes whose bit is
+// clear load nothing.
+template <typename T>
+__device__ __forceinline__ T xor_bits_wave(const T *tab, uint64_t v) {
+    const uint32_t lane = __lane_id();
+    const bool on = lane < BMMC_MAX_BITS && ((v >> lane) & 1u);
+    return wave_select_xor(on ? tab[lane] : T(0), v);
 }
 
 // XOR of the first NB table entries selected by the bits of a per-lane value.

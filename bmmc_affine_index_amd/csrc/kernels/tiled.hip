@@ -48,7 +48,24 @@ template <int UL, int T, int IT> struct TiledCfg {
 // Tile bases: the wave reduction when the workgroup is made of full waves,
 // the scalar loop otherwise.  A one-tile launch of a small array runs one
 // workgroup per compute unit, whose scalar cache is cold: the loop's chain
-// of dependent table loads measured 13-16% of a 4 MiB pass.
+// of dependent table loads measured 13-16% of a 4 MiB pass.  A base comes in
+// two steps, the lane's table load (base_issue) and the reduction
+// (base_finish), so that a kernel needing several bases issues all their
+// loads before it waits: left to itself the compiler waits for each base's
+// load before it issues the next, one memory round trip per base.
+template <class C, typename T>
+__device__ __forceinline__ T base_issue(const T *tab, uint64_t blk) {
+    if constexpr (C::NT >= 64) return dev::wave_load(tab);
+    else return dev::xor_bits_uniform(tab, blk);
+}
+
+template <class C, typename T>
+__device__ __forceinline__ T base_finish(T e, uint64_t blk) {
+    if constexpr (C::NT >= 64) return dev::wave_select_xor(e, blk);
+    else return e;
+}
+
+// Both steps at once, with the table load under each lane's condition.
 template <class C, typename T>
 __device__ __forceinline__ T tile_base(const T *tab, uint64_t blk) {
     if constexpr (C::NT >= 64) return dev::xor_bits_wave(tab, blk);
@@ -135,11 +152,17 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s) stage_tile<C, T>(lds + s * C::TILE, v[s], d, p);
     __syncthreads();
+    // The output and LDS bases are computed here, after the barrier, one
+    // after the other.  Issued with the input base, before the tile's loads,
+    // they made the 4096 x 4096 4-byte transpose (t = 7, two workgroups per
+    // compute unit, two rounds of them) 7% slower, and issued together here
+    // 2% slower: its stores gain from starting later.  Small arrays, which
+    // would gain from the earlier bases, run faster on the streamed launch.
 #pragma unroll
     for (int s = 0; s < (1 << IT); ++s) {
         const uint64_t blk = tile0 | (uint64_t)s;
         drain_tile<C, T, NT>(out, lds + s * C::TILE, tile_base<C>(d.out_blk, blk) ^ d.out_c,
-                         tile_base<C>(d.lds_blk, blk) ^ d.lds_c, d, p);
+                             tile_base<C>(d.lds_blk, blk) ^ d.lds_c, d, p);
     }
 }
 
@@ -165,12 +188,17 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
     const int shift = interleaved ? d.grid_log2 : 0;  // the walked block bits start here
     const uint64_t count = uint64_t(1) << r;
 
-    uint64_t in_base = tile_base<C>(d.in_blk, first);
-    uint64_t out_base = tile_base<C>(d.out_blk, first) ^ d.out_c;
-    uint32_t rd_base = tile_base<C>(d.lds_blk, first) ^ d.lds_c;
+    const uint64_t e_in = base_issue<C>(d.in_blk, first);
+    const uint64_t e_out = base_issue<C>(d.out_blk, first);
+    const uint32_t e_rd = base_issue<C>(d.lds_blk, first);
+    __builtin_amdgcn_sched_barrier(0);
+    uint64_t in_base = base_finish<C>(e_in, first);
 
     dev::Chunk<C::CB> v[C::J];
     load_tile<C, T, NT>(v, in, in_base, d, p);
+    __builtin_amdgcn_sched_barrier(0);
+    uint64_t out_base = base_finish<C>(e_out, first) ^ d.out_c;
+    uint32_t rd_base = base_finish<C>(e_rd, first) ^ d.lds_c;
     // Every tile but the last refills the registers with the next tile's
     // loads before draining.  Loads and stores share one counter, which
     // completes in issue order; the staging wait can leave the previous
@@ -229,13 +257,6 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     const int shift = interleaved ? d.grid_log2 : 0;
     const uint64_t count = uint64_t(1) << r;
 
-    // loaders: running input base of the last tile loaded (tiles are loaded
-    // in walk order, DEPTH ahead of the one being staged)
-    uint64_t in_base = tile_base<C>(d.in_blk, first);
-    uint64_t loaded = 0;  // tiles loaded so far
-    // storers: running bases of the next tile to drain
-    uint64_t out_base = tile_base<C>(d.out_blk, first) ^ d.out_c;
-    uint32_t rd_base = tile_base<C>(d.lds_blk, first) ^ d.lds_c;
 
     // Each role runs its own loop with exactly `count` barriers, so every
     // wave meets the same barriers; keeping the roles' code apart leaves each
@@ -243,6 +264,10 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     // loads only (a shared loop body merges both roles' paths and its waits
     // fall back to "everything outstanding").
     if (loader) {
+        // running input base of the last tile loaded (tiles are loaded in
+        // walk order, DEPTH ahead of the one being staged)
+        uint64_t in_base = base_finish<C>(base_issue<C>(d.in_blk, first), first);
+        uint64_t loaded = 0;  // tiles loaded so far
         dev::Chunk<C::CB> v[DEPTH][C::J];
         // next tile in walk order: one table entry per step (Gray code)
         auto advance = [&]() {
@@ -287,6 +312,12 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
             __syncthreads();
         }
     } else {
+        // running bases of the next tile to drain
+        const uint64_t e_out = base_issue<C>(d.out_blk, first);
+        const uint32_t e_rd = base_issue<C>(d.lds_blk, first);
+        __builtin_amdgcn_sched_barrier(0);
+        uint64_t out_base = base_finish<C>(e_out, first) ^ d.out_c;
+        uint32_t rd_base = base_finish<C>(e_rd, first) ^ d.lds_c;
         for (uint64_t k = 0; k < count; ++k) {
             __syncthreads();
             drain_tile<C, T, NT>(out, lds + (k & 1) * C::TILE, out_base, rd_base, d, p);
