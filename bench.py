@@ -60,9 +60,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, plan_options: dict):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none or the kernels changed since it was taken."""
+    None when there is none, the kernels changed since it was taken, or it
+    was taken with another plan (launch style, tile side, tile order ...)."""
     path = TRAFFIC_FILE % workload
     if not os.path.exists(path):
         return None
@@ -73,6 +74,11 @@ def read_traffic(workload: str):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        if json.loads(kv.get("plan_options", "null")) != plan_options:
+            return None
+    except ValueError:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -298,6 +304,9 @@ def main():
     ap.add_argument("--block-map", type=int, default=0)
     ap.add_argument("--depth", type=int, default=0)
     ap.add_argument("--cache-hint", type=int, default=0)
+    ap.add_argument("--plan-options", default=None,
+                    help="JSON object of plan options, as printed in config.plan_options: "
+                         "build exactly that plan and skip the tuning")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer pair")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,11 +374,15 @@ def main():
     t0 = time.perf_counter()
     launch = {"auto": bm.LAUNCH_AUTO, "one_tile": bm.LAUNCH_ONE_TILE,
               "persistent": bm.LAUNCH_PERSISTENT, "streamed": bm.LAUNCH_STREAMED}[args.launch]
-    plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
-                   no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
-                   grid_log2=args.grid_log2,
-                   walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
-                   block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
+    if args.plan_options:
+        plan = bm.Plan(n, A, c, elem, **json.loads(args.plan_options))
+        args.no_tune = True
+    else:
+        plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
+                       no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
+                       grid_log2=args.grid_log2,
+                       walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
+                       block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
     plan_us = (time.perf_counter() - t0) * 1e6
     if name == "c4" and not args.kind and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2
@@ -463,7 +476,8 @@ def main():
         if parity.startswith("MISMATCH"):
             print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
 
-    traffic = None if args.kind else read_traffic(name)
+    plan_options = plan.options()
+    traffic = None if args.kind else read_traffic(name, plan_options)
     passes = plan.info.passes
     roofline = {
         "bound": "hbm",
@@ -498,6 +512,7 @@ def main():
                           "%d rotating buffer pairs, %.2f GiB working set (HBM)"
                           % (pairs, 2 * pairs * nbytes / 2**30)),
             "plan": plan.describe(),
+            "plan_options": plan_options,
             "timing": ("eager calls from Python" if args.no_graph else
                        "one HIP graph of the %d steps, replayed" % args.steps),
         },

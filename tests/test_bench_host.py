@@ -42,12 +42,37 @@ def test_ablation_variants_plan_on_host():
                 assert P.info.passes in (1, 2)
 
 
-def test_traffic_reader_and_digest():
+def test_traffic_reader_and_digest(tmp_path, monkeypatch):
     d = bench.kernel_source_digest()
     assert isinstance(d, str) and len(d) == 16
+    A, c = wl.workload_matrix("c2")
+    opts = bm.Plan(24, A, c, 4).options()
     for w in ("c2", "c4"):
-        t = bench.read_traffic(w)
+        t = bench.read_traffic(w, opts)
         assert t is None or t > 0
+    # a summary counts only for the plan it was taken with, at these sources
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic_%s.txt"))
+
+    def write(digest, options):
+        (tmp_path / "hbm_traffic_c2.txt").write_text(
+            "# comment = ignored\nkernel_source_digest=%s\nplan_options=%s\n"
+            "hbm_bytes_per_launch=134618399\n" % (digest, json.dumps(options)))
+    write(d, opts)
+    assert bench.read_traffic("c2", opts) == 134618399.0
+    other = dict(opts, tile_log2=opts["tile_log2"] + 1)
+    assert bench.read_traffic("c2", other) is None
+    write("0" * 16, opts)
+    assert bench.read_traffic("c2", opts) is None
+    assert bench.read_traffic("c3", opts) is None  # no summary at all
+
+
+def test_plan_options_rebuild_the_plan():
+    A, c = wl.workload_matrix("c3")
+    P = bm.Plan(28, A, c, 4, launch=bm.LAUNCH_PERSISTENT, tile_log2=7, block_map=6)
+    Q = bm.Plan(28, A, c, 4, **json.loads(json.dumps(P.options())))
+    assert Q.describe() == P.describe()
+    for a, b in zip(P.passes(), Q.passes()):
+        assert bytes(a) == bytes(b)
 
 
 def test_more_than_one_gpu_is_refused():
@@ -60,5 +85,6 @@ def test_help_lists_protocol_options():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0
-    for opt in ("--steps", "--warmup", "--no-graph", "--no-tune", "--ablation", "--perms"):
+    for opt in ("--steps", "--warmup", "--no-graph", "--no-tune", "--ablation", "--perms",
+                "--plan-options"):
         assert opt in r.stdout
