@@ -196,9 +196,10 @@ def cpu_model() -> str:
 ABLATION_VARIANTS = [
     # name, plan options; the paper's Figure 9 columns, then this library's default
     ("naive", dict(route=bm.ROUTE_NAIVE)),
-    ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True)),
-    ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE)),
-    ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2)),
+    # (the paper's kernels take the tiles in their natural order: block_map 1)
+    ("tile", dict(launch=bm.LAUNCH_ONE_TILE, no_swizzle=True, block_map=1)),
+    ("tile+banks", dict(launch=bm.LAUNCH_ONE_TILE, block_map=1)),
+    ("tile+banks+iters", dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=2, block_map=1)),
     ("planner, untuned", dict()),
     ("tuned (default)", dict(tune=True)),
 ]
@@ -212,6 +213,14 @@ def run_ablation(args, torch):
     import oracle
     stream = torch.cuda.current_stream()
     s_handle = int(stream.cuda_stream)
+    # about 0.1 s of copies first, so that the first size is not timed while
+    # the GPU's clocks are still rising
+    wbuf = torch.empty(2 << 28, dtype=torch.uint8, device="cuda:0")
+    for _ in range(60):
+        if bm.bmmc_copy(wbuf[: 1 << 28], wbuf[1 << 28:], 1 << 28, s_handle) != bm.OK:
+            raise bm.BmmcError(bm.ERR_HIP, "bmmc_copy")
+    torch.cuda.synchronize()
+    del wbuf
     for n in [int(v) for v in args.sizes.split(",")]:
         elem = 4
         nbytes = elem << n
@@ -227,7 +236,9 @@ def run_ablation(args, torch):
             st = bm.bmmc_copy(i, o, nbytes, h)
             if st != bm.OK:
                 raise bm.BmmcError(st, "bmmc_copy")
-        ms_copy = time_loop(torch, copy, bufs, steps, 3, stream, graph=not args.no_graph)
+        # the ceiling: the faster of two timings
+        ms_copy = min(time_loop(torch, copy, bufs, steps, 3, stream, graph=not args.no_graph)
+                      for _ in range(2))
         copy_gbs = 2.0 * nbytes / (ms_copy * 1e-3) / 1e9
         kinds = [("random_bpc", wl.random_bpc(n, 7)), ("bit_reverse", (wl.bit_reverse_matrix(n), 0)),
                  ("random_bmmc", wl.random_bmmc(n, 7, lib_accepts(n)))]

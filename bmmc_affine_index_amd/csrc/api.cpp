@@ -158,7 +158,7 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     if (p->opt.launch) launches = {p->opt.launch};
     else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
     if (p->opt.block_map) maps = {p->opt.block_map};
-    else maps = {1, 3, 5, 6};
+    else maps = {bmmc::kDefaultBlockMap, 1, 3, 6};  // the planner's own first
     tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
     std::vector<std::unique_ptr<bmmc_plan>> cand;
     for (size_t ti = 0; ti < tiles.size(); ++ti)

@@ -699,7 +699,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     // large workloads: +1% to +5% over no hint; loads alone lose).
     lc.cache_hint = o.cache_hint == 1 ? 0 : 3;
     lc.depth = o.depth ? o.depth : 2;
-    lc.block_map = o.block_map ? o.block_map : 1;
+    lc.block_map = o.block_map ? o.block_map : kDefaultBlockMap;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);

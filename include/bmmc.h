@@ -82,7 +82,7 @@ typedef struct bmmc_plan_options {
                        0 = planner's choice */
     int cache_hint; /* tile pass: 0 = planner's choice (non-temporal loads and stores),
                        1 = none, 2 = non-temporal loads and stores */
-    int block_map;  /* re-indexing of the tiles: 0 = planner's choice, 1 = identity,
+    int block_map;  /* re-indexing of the tiles: 0 = planner's choice (5), 1 = identity,
                        2 = reversed bit order, 3 = tiles in flight together form a
                        patch dense on both the input and the output side, 4 = dense on
                        the input side, 5 = dense on the output side, 6 = (range walk)
@@ -215,8 +215,8 @@ int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream)
  * running time varied with the permutation).  Every candidate computes the
  * same permutation; they differ in the tile side (the planner's and the next
  * larger), the launch style (the planner's persistent or streamed walk, or
- * one workgroup per tile) and the block order (bmmc_plan_options.block_map 1,
- * 3, 5 and 6): up to 16 candidates.  An option the caller fixed at plan
+ * one workgroup per tile) and the block order (bmmc_plan_options.block_map 5,
+ * the planner's, and 1, 3 and 6): up to 16 candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, twice over, timed with HIP
  * events; the fastest replaces the plan's kernel tables if it beats the
