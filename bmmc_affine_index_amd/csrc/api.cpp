@@ -158,7 +158,10 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     if (p->opt.launch) launches = {p->opt.launch};
     else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
     if (p->opt.block_map) maps = {p->opt.block_map};
-    else maps = {bmmc::kDefaultBlockMap, 1, 3, 6};  // the planner's own first
+    // the planner's own first; the two seeded random orders spread the tiles
+    // in flight over the whole array, which lifts the matrices whose
+    // structured orders crowd them (random 16-byte BPCs: up to +6%)
+    else maps = {bmmc::kDefaultBlockMap, 1, 3, 6, 8, 9};
     tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
     std::vector<std::unique_ptr<bmmc_plan>> cand;
     for (size_t ti = 0; ti < tiles.size(); ++ti)

@@ -216,7 +216,8 @@ int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream)
  * same permutation; they differ in the tile side (the planner's and the next
  * larger), the launch style (the planner's persistent or streamed walk, or
  * one workgroup per tile) and the block order (bmmc_plan_options.block_map 5,
- * the planner's, and 1, 3 and 6): up to 16 candidates.  An option the caller fixed at plan
+ * the planner's, 1, 3 and 6, and the random orders 8 and 9): up to 24
+ * candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, twice over, timed with HIP
  * events; the fastest replaces the plan's kernel tables if it beats the

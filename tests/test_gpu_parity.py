@@ -264,7 +264,7 @@ def test_tune_keeps_results_and_fixed_options(case):
             if "block_map" in kw:
                 assert d.block_map == kw["block_map"]
             else:
-                assert d.block_map in (1, 3, 5, 6)
+                assert d.block_map in (1, 3, 5, 6, 8, 9)
         else:
             assert (d.kernel, d.launch, d.block_map) in before
 
@@ -426,7 +426,7 @@ def test_workload_c4_every_tuning_candidate():
     d_out = torch.empty_like(d_in)
     idx = _sample_idx(n, 1 << 18, 31)
     for launch in (bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE):
-        for bmap in (1, 3, 5, 6):
+        for bmap in (1, 3, 5, 6, 8, 9):
             _note("c4 launch=%d block_map=%d" % (launch, bmap))
             P = bm.Plan(n, A, c, 4, launch=launch, block_map=bmap)
             d_out.fill_(SENTINEL)
