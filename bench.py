@@ -50,20 +50,29 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt")
 
 
 def kernel_source_digest() -> str:
-    """Digest of the sources that decide what the kernels read and write."""
+    """Digest of the device code: the kernels and what they include."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bmmc_affine_index_amd", "csrc")
-    for rel in sorted(["plan.cpp", "gf2.h", "kernels/tiled.hip", "kernels/chunk.hip",
+    for rel in sorted(["launch.h", "kernels/tiled.hip", "kernels/chunk.hip",
                        "kernels/copy.hip", "kernels/common.h"]):
         with open(os.path.join(csrc, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, plan_options: dict):
+def plan_tables_digest(plan) -> str:
+    """Digest of the kernel tables of every pass of a plan: with the device
+    code, they decide every address the kernels touch."""
+    h = hashlib.sha256()
+    for d in plan.passes():
+        h.update(bytes(d))
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, plan_options: dict, tables_digest: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none, the kernels changed since it was taken, or it
-    was taken with another plan (launch style, tile side, tile order ...)."""
+    None when there is none, or it was taken with other device code, another
+    plan (launch style, tile side, tile order ...) or other kernel tables."""
     path = TRAFFIC_FILE % workload
     if not os.path.exists(path):
         return None
@@ -74,6 +83,8 @@ def read_traffic(workload: str, plan_options: dict):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    if kv.get("plan_tables_digest") != tables_digest:
         return None
     try:
         if json.loads(kv.get("plan_options", "null")) != plan_options:
@@ -488,7 +499,7 @@ def main():
             print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
 
     plan_options = plan.options()
-    traffic = None if args.kind else read_traffic(name, plan_options)
+    traffic = None if args.kind else read_traffic(name, plan_options, plan_tables_digest(plan))
     passes = plan.info.passes
     roofline = {
         "bound": "hbm",

@@ -549,10 +549,11 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     d->blk_bits = blk_bits;
     const u64 tile_bytes = u64(1) << (2 * t + ulog2);
     int launch = lc.persistent;
-    // Planner's choice, measured on the benchmark workloads: below 2^14 tiles
-    // the streamed launch with loads two tiles ahead (the 64 MiB transpose:
-    // 0.914 of copy against 0.887 persistent); above, the persistent launch
-    // (bit-reversal n = 28: 0.865 against 0.78 streamed).
+    // Planner's choice, measured untuned with the default tile order: below
+    // 2^14 tiles the streamed launch with loads two tiles ahead (the 64 MiB
+    // transpose: 0.87 of copy against 0.84 persistent; random BPC and BMMC
+    // at n = 24 alike); above, the persistent launch (the 16384 x 16384
+    // transpose: 0.90 against 0.85 streamed; random BMMC n = 28 even).
     if (lc.auto_launch && launch) launch = blk_bits < 14 ? BMMC_LAUNCH_STREAMED
                                                          : BMMC_LAUNCH_PERSISTENT;
     // the streamed launch splits waves by role, so each role needs whole waves

@@ -46,24 +46,30 @@ def test_traffic_reader_and_digest(tmp_path, monkeypatch):
     d = bench.kernel_source_digest()
     assert isinstance(d, str) and len(d) == 16
     A, c = wl.workload_matrix("c2")
-    opts = bm.Plan(24, A, c, 4).options()
+    P = bm.Plan(24, A, c, 4)
+    opts, tabs = P.options(), bench.plan_tables_digest(P)
+    assert tabs == bench.plan_tables_digest(bm.Plan(24, A, c, 4, **opts))
+    Q = bm.Plan(24, A, c, 4, tile_log2=opts["tile_log2"] + 1)
+    assert bench.plan_tables_digest(Q) != tabs
     for w in ("c2", "c4"):
-        t = bench.read_traffic(w, opts)
+        t = bench.read_traffic(w, opts, tabs)
         assert t is None or t > 0
-    # a summary counts only for the plan it was taken with, at these sources
+    # a summary counts only for the plan and tables it was taken with, at
+    # this device code
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic_%s.txt"))
 
-    def write(digest, options):
+    def write(digest, options, tables):
         (tmp_path / "hbm_traffic_c2.txt").write_text(
             "# comment = ignored\nkernel_source_digest=%s\nplan_options=%s\n"
-            "hbm_bytes_per_launch=134618399\n" % (digest, json.dumps(options)))
-    write(d, opts)
-    assert bench.read_traffic("c2", opts) == 134618399.0
-    other = dict(opts, tile_log2=opts["tile_log2"] + 1)
-    assert bench.read_traffic("c2", other) is None
-    write("0" * 16, opts)
-    assert bench.read_traffic("c2", opts) is None
-    assert bench.read_traffic("c3", opts) is None  # no summary at all
+            "plan_tables_digest=%s\nhbm_bytes_per_launch=134618399\n"
+            % (digest, json.dumps(options), tables))
+    write(d, opts, tabs)
+    assert bench.read_traffic("c2", opts, tabs) == 134618399.0
+    assert bench.read_traffic("c2", Q.options(), tabs) is None
+    assert bench.read_traffic("c2", opts, bench.plan_tables_digest(Q)) is None
+    write("0" * 16, opts, tabs)
+    assert bench.read_traffic("c2", opts, tabs) is None
+    assert bench.read_traffic("c3", opts, tabs) is None  # no summary at all
 
 
 def test_plan_options_rebuild_the_plan():
