@@ -1,0 +1,114 @@
+"""Seeded random (matrix, data, plan options) cases over the whole option
+space: every matrix class, element size, route, launch style, tile side, tile
+order, grid, walk, depth, cache hint and LDS layout, drawn together.  Holds
+none of the method's arithmetic: matrices come from the seeded generators of
+the workloads module (or simple block-diagonal compositions of them), and the
+oracle supplies every expected value.
+
+A case is only handed to the GPU after the host replay of its kernel tables
+(tests/emulate.py) has checked every global and LDS access for range and
+exactly-once coverage and reproduced the oracle's permutation."""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+import bmmc_affine_index_amd as bm
+from bmmc_affine_index_amd import workloads as wl
+
+KINDS = ("general", "bpc", "bitrev", "transpose", "complement", "blockperm", "lowkeep")
+ELEMS = (1, 2, 4, 8, 16)
+N_CASES = 600
+MASTER_SEED = 0x5EED_B44C
+
+
+@dataclass
+class Case:
+    index: int
+    kind: str
+    n: int
+    elem: int
+    seed: int
+    options: dict = field(default_factory=dict)
+
+    def matrix(self):
+        n, s = self.n, self.seed
+        if self.kind == "bitrev":
+            return wl.bit_reverse_matrix(n), 0
+        if self.kind == "transpose":
+            return wl.transpose_matrix(n // 2, n - n // 2), 0
+        if self.kind == "bpc":
+            return wl.random_bpc(n, s)
+        if self.kind == "complement":
+            return wl.identity_matrix(n), (s * 0x9E3779B97F4A7C15) & ((1 << n) - 1)
+        if self.kind in ("blockperm", "lowkeep"):
+            # the low k index bits map to themselves; a random invertible map
+            # of the other n - k bits (whole blocks move, or, with k small,
+            # units merge over the kept low bits)
+            k = max(0, min(n - 1, (s % 7) + (3 if self.kind == "blockperm" else 0)))
+            Q, cq = wl.random_bmmc(n - k, s, lambda r: oracle.rank(r) == n - k)
+            A = np.array([1 << r for r in range(k)] + [int(q) << k for q in Q], dtype=np.uint64)
+            return A, (int(cq) << k) if self.kind == "lowkeep" else 0
+        return wl.random_bmmc(n, s, lambda r: oracle.rank(r) == n)
+
+    def data(self):
+        return wl.fill_random_bytes(self.n, self.elem, self.seed ^ 0xDA7A)
+
+    def ident(self):
+        return "case%03d-%s-n%d-e%d-%s" % (self.index, self.kind, self.n, self.elem, "-".join(
+            "%s%d" % (k, v) for k, v in sorted(self.options.items())))
+
+
+def cases():
+    """The fixed list of N_CASES cases (the same on every call)."""
+    rng = np.random.Generator(np.random.PCG64(MASTER_SEED))
+    out = []
+    for i in range(N_CASES):
+        kind = KINDS[int(rng.integers(len(KINDS)))]
+        elem = ELEMS[int(rng.integers(len(ELEMS)))]
+        n = int(rng.integers(1, 19))
+        if kind == "blockperm" and n < 5:
+            n += 5
+        opts = {}
+        route = int(rng.choice([bm.ROUTE_AUTO, bm.ROUTE_AUTO, bm.ROUTE_FUSED,
+                                bm.ROUTE_TWO_PASS, bm.ROUTE_NAIVE]))
+        if route:
+            opts["route"] = route
+        launch = int(rng.choice([bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE, bm.LAUNCH_PERSISTENT,
+                                 bm.LAUNCH_STREAMED]))
+        if launch:
+            opts["launch"] = launch
+        t = int(rng.choice([0, 0, 0, 3, 4, 5, 6, 7]))
+        if t:
+            opts["tile_log2"] = t
+        bmap = int(rng.choice([0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 13]))
+        if bmap:
+            opts["block_map"] = bmap
+        if launch in (bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE) and rng.random() < 0.3:
+            opts["iters_log2"] = int(rng.integers(1, 3))
+        if launch in (bm.LAUNCH_PERSISTENT, bm.LAUNCH_STREAMED):
+            g = int(rng.choice([0, 0, 1, 3, 5]))
+            if g:
+                opts["grid_log2"] = g
+            w = int(rng.choice([0, bm.WALK_RANGES, bm.WALK_INTERLEAVED]))
+            if w:
+                opts["walk"] = w
+        if launch == bm.LAUNCH_STREAMED and rng.random() < 0.5:
+            opts["depth"] = int(rng.integers(1, 3))
+        hint = int(rng.choice([0, 0, 1, 2]))
+        if hint:
+            opts["cache_hint"] = hint
+        if rng.random() < 0.15:
+            opts["no_swizzle"] = 1
+        out.append(Case(i, kind, n, elem, int(rng.integers(1, 1 << 30)), opts))
+    return out
+
+
+def plan_or_none(case: Case):
+    """The case's plan, or None when the library rejects the combination of
+    options (an argument error, not a fault: no GPU call is involved)."""
+    A, c = case.matrix()
+    try:
+        return bm.Plan(case.n, A, c, case.elem, **case.options)
+    except bm.BmmcError:
+        return None

@@ -1,0 +1,39 @@
+"""Host replay of the seeded random option cases (tests/random_cases.py):
+every plan the library accepts is replayed from its kernel tables, with every
+global and LDS access checked for range and exactly-once coverage, and must
+reproduce the oracle's permutation.  No GPU call is made."""
+import numpy as np
+import pytest
+
+import oracle
+from emulate import run_plan_on_host
+from random_cases import N_CASES, cases, plan_or_none
+
+BATCHES = 6
+
+
+def test_cases_are_fixed_and_span_the_options():
+    a, b = cases(), cases()
+    assert [c.ident() for c in a] == [c.ident() for c in b]
+    assert len(a) == N_CASES
+    seen = {k for c in a for k in c.options}
+    assert {"route", "launch", "tile_log2", "block_map", "iters_log2", "grid_log2", "walk",
+            "depth", "cache_hint", "no_swizzle"} <= seen
+    assert {c.kind for c in a} == {"general", "bpc", "bitrev", "transpose", "complement",
+                                   "blockperm", "lowkeep"}
+    assert {c.elem for c in a} == {1, 2, 4, 8, 16}
+
+
+@pytest.mark.parametrize("batch", range(BATCHES))
+def test_random_cases_replay_on_host(batch):
+    mine = cases()[batch::BATCHES]
+    ran = 0
+    for case in mine:
+        P = plan_or_none(case)
+        if P is None:
+            continue
+        A, c = case.matrix()
+        x = case.data()
+        assert np.array_equal(run_plan_on_host(P, x), oracle.apply(A, c, x)), case.ident()
+        ran += 1
+    assert ran >= 0.9 * len(mine)
