@@ -129,9 +129,10 @@ typedef struct bmmc_plan_info {
  * TILED: the array is cut into 2^blk_bits tiles of 2^(2t) units; tile b
  * starts at input offset XOR_k in_blk[k] over the set bits k of b.  With the
  * one-tile launch a workgroup moves tiles b = (w << iters_log2) | s; with
- * the persistent launch workgroup w walks, for k < 2^r with
- * r = blk_bits - grid_log2 and gray(k) = k XOR (k >> 1), the tiles
- * w * 2^r XOR gray(k) (ranges) or gray(k) * 2^grid_log2 XOR w (interleaved).
+ * the persistent and streamed launches workgroup w, as walker
+ * v = w XOR ((w >> 3) & 7), walks, for k < 2^r with r = blk_bits - grid_log2
+ * and gray(k) = k XOR (k >> 1), the tiles v * 2^r XOR gray(k) (ranges) or
+ * gray(k) * 2^grid_log2 XOR v (interleaved).
  * A tile is moved in chunks of 2^chunk_log2 units: chunk c = (j << T) | tid
  * (T = log2 threads per workgroup, j the pass) is loaded from input offset
  * tile base XOR_p ld_in[p] and written to LDS address XOR_p ld_lds[p] over

@@ -43,8 +43,9 @@ LAUNCH_ONE_TILE, LAUNCH_PERSISTENT, LAUNCH_STREAMED = 1, 2, 3
 
 
 def check_persistent_walk(d):
-    """Replays the persistent launch's walk: workgroup w starts at block
-    w << r and moves to the next block by XORing block bit ctz(k + 1) into its
+    """Replays the persistent launch's walk: workgroup w, as walker
+    v = w ^ ((w >> 3) & 7), starts at block v << r (ranges) or v (interleaved)
+    and moves to the next block by XORing block bit ctz(k + 1) into its
     running bases.  Every block must be visited exactly once, and the running
     input base must equal the directly computed one at every step."""
     r = d.blk_bits - d.grid_log2
@@ -55,7 +56,8 @@ def check_persistent_walk(d):
     shift = d.grid_log2 if d.walk == 2 else 0
     seen = np.zeros(1 << d.blk_bits, dtype=np.int64)
     for w in range(1 << d.grid_log2):
-        blk = w if d.walk == 2 else w << r
+        v = w ^ ((w >> 3) & 7)
+        blk = v if d.walk == 2 else v << r
         base = int(_xor_table(np.uint64(blk), d.in_blk, d.blk_bits))
         for k in range(1 << r):
             if base != int(_xor_table(np.uint64(blk), d.in_blk, d.blk_bits)):
