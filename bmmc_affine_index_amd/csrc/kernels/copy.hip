@@ -10,13 +10,20 @@ namespace bmmc {
 constexpr int kCopyNTL = 8;  // 256 threads
 
 // Non-temporal loads and stores: the data is streamed once.  Measured on
-// MI355X with buffers rotating over 2 GiB (GB/s of bytes read + written):
+// MI355X with buffers rotating over 2 GiB (GB/s of bytes read + written,
+// three runs each agreeing within 1%):
 //   bytes   one-shot, 1 x 16 B/lane   grid-stride, 2048 groups, 4 x 16 B/lane
-//   4 MiB        3012                      2802
-//   16 MiB       4647                      5650
-//   64 MiB       5882                      5884
+//   4 MiB        2976                      2700
+//   8 MiB        4300                      4070
+//   16 MiB       4590                      5620
+//   32 MiB       5160                      5290
+//   64 MiB       5770                      5865
+//   128 MiB      6160                      6100
 //   1 GiB        6491                      5897
-// and the hints add 5-15% over plain loads and stores from 4 MiB up.
+// and the hints add 5-15% over plain loads and stores from 4 MiB up.  (At
+// 32 MiB a one-shot launch with 4 x 16 B per lane measured 5560, faster than
+// the grid-stride loop's one trip over the same 2048 workgroups; the reason
+// is not known, and that size keeps the loop.)
 template <int CPTL>
 __global__ void __launch_bounds__(1 << kCopyNTL)
     bmmc_copy_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, uint64_t n16,
@@ -59,7 +66,7 @@ __global__ void __launch_bounds__(1 << kCopyNTL)
 }
 
 // the grid-stride form serves (kCopyStrideMinBytes, kCopyStrideMaxBytes]
-constexpr uint64_t kCopyStrideMinBytes = uint64_t(4) << 20;
+constexpr uint64_t kCopyStrideMinBytes = uint64_t(8) << 20;
 constexpr uint64_t kCopyStrideMaxBytes = uint64_t(64) << 20;
 constexpr int kCopyStrideCPTL = 2;
 constexpr uint32_t kCopyStrideBlocks = 2048;  // 8 per compute unit on a 256-CU MI355X
