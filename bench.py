@@ -71,30 +71,34 @@ def plan_tables_digest(plan) -> str:
 
 def read_traffic(workload: str, plan_options: dict, tables_digest: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none, or it was taken with other device code, another
-    plan (launch style, tile side, tile order ...) or other kernel tables."""
+    None when there is none, or it holds no entry taken with this device code,
+    this plan (launch style, tile side, tile order ...) and these kernel
+    tables.  A summary holds one entry per plan counted, each opened by a line
+    "[entry]" and made of key=value lines; '#' lines are comments."""
     path = TRAFFIC_FILE % workload
     if not os.path.exists(path):
         return None
-    kv = {}
+    entries, kv = [], None
     with open(path) as f:
         for line in f:
-            if "=" in line and not line.startswith("#"):
+            line = line.strip()
+            if line == "[entry]":
+                kv = {}
+                entries.append(kv)
+            elif kv is not None and "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_digest") != kernel_source_digest():
-        return None
-    if kv.get("plan_tables_digest") != tables_digest:
-        return None
-    try:
-        if json.loads(kv.get("plan_options", "null")) != plan_options:
-            return None
-    except ValueError:
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    digest = kernel_source_digest()
+    for kv in entries:
+        if kv.get("kernel_source_digest") != digest or kv.get("plan_tables_digest") != tables_digest:
+            continue
+        try:
+            if json.loads(kv.get("plan_options", "null")) != plan_options:
+                continue
+            return float(kv["hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            continue
+    return None
 
 
 def lib_accepts(n: int):

@@ -58,16 +58,23 @@ def test_traffic_reader_and_digest(tmp_path, monkeypatch):
     # this device code
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic_%s.txt"))
 
-    def write(digest, options, tables):
-        (tmp_path / "hbm_traffic_c2.txt").write_text(
-            "# comment = ignored\nkernel_source_digest=%s\nplan_options=%s\n"
-            "plan_tables_digest=%s\nhbm_bytes_per_launch=134618399\n"
-            % (digest, json.dumps(options), tables))
-    write(d, opts, tabs)
+    def entry(digest, options, tables, nbytes):
+        return ("[entry]\n# comment = ignored\nkernel_source_digest=%s\nplan_options=%s\n"
+                "plan_tables_digest=%s\nhbm_bytes_per_launch=%d\n"
+                % (digest, json.dumps(options), tables, nbytes))
+
+    def write(*entries):
+        (tmp_path / "hbm_traffic_c2.txt").write_text("# header = ignored\n" + "".join(entries))
+    write(entry(d, opts, tabs, 134618399))
     assert bench.read_traffic("c2", opts, tabs) == 134618399.0
     assert bench.read_traffic("c2", Q.options(), tabs) is None
     assert bench.read_traffic("c2", opts, bench.plan_tables_digest(Q)) is None
-    write("0" * 16, opts, tabs)
+    # several plans counted: each finds its own entry
+    qtabs = bench.plan_tables_digest(Q)
+    write(entry(d, Q.options(), qtabs, 134300000), entry(d, opts, tabs, 134618399))
+    assert bench.read_traffic("c2", opts, tabs) == 134618399.0
+    assert bench.read_traffic("c2", Q.options(), qtabs) == 134300000.0
+    write(entry("0" * 16, opts, tabs, 134618399))
     assert bench.read_traffic("c2", opts, tabs) is None
     assert bench.read_traffic("c3", opts, tabs) is None  # no summary at all
 
