@@ -112,6 +112,16 @@ __device__ __forceinline__ void load_tile(dev::Chunk<C::CB> (&v)[C::J], const ui
     }
 }
 
+// load_tile with the per-pass input offsets given (the XORs of the table
+// entries of the pass bits, read beforehand).
+template <class C, int T, bool NT>
+__device__ __forceinline__ void load_tile_jo(dev::Chunk<C::CB> (&v)[C::J], const uint8_t *in,
+                                             uint64_t in_base, const uint64_t (&jo)[C::J],
+                                             const LaneParts &p) {
+#pragma unroll
+    for (int j = 0; j < C::J; ++j) v[j] = dev::gload_nt<C::CB, NT>(in + ((in_base ^ jo[j]) ^ p.in_lane));
+}
+
 // Write the tile's chunks to LDS through the swizzle.
 template <class C, int T>
 __device__ __forceinline__ void stage_tile(uint8_t *tile_lds, const dev::Chunk<C::CB> (&v)[C::J],
@@ -251,7 +261,16 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
 // for.  One barrier per tile orders the halves: the loaders write buffer k&1
 // before barrier k, the storers read it after barrier k and have finished
 // before barrier k+1, after which the loaders may write it again (tile k+2).
-template <int UL, int T, int DEPTH, bool NT>
+// Launches of at most 2^kSmallBlkBits tiles (arrays of a few MiB) have a
+// variant of the streamed kernel whose loader waves take their input base from
+// that many table entries by scalar loads, issued with the kernel's other
+// argument loads.  The wave's vector load of the table otherwise costs a memory
+// round trip before the first tile load, which a pass of a few microseconds
+// pays in full: measured on MI355X, a 4 MiB pass spent 0.41 us on it, and 0.08 us
+// on the scalar form (0.19 us when the choice was a run-time branch).
+constexpr int kSmallBlkBits = 8;
+
+template <int UL, int T, int DEPTH, bool NT, bool SB>
 __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     bmmc_tiled_streamed_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                const bmmc_pass_desc d) {
@@ -263,14 +282,42 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     // reading it from the first lane tells the compiler so, which keeps the
     // loaders' running tile index in scalar registers.
     const bool loader = __builtin_amdgcn_readfirstlane((int)threadIdx.x) < C::NT;
-    const LaneParts p = lane_parts<C, T>(d, threadIdx.x & (C::NT - 1));
-    const int r = d.blk_bits - d.grid_log2;
-    const bool interleaved = d.walk == BMMC_WALK_INTERLEAVED;
+    // each role computes only its own lane parts: fewer table loads per wave,
+    // which the compiler can then issue together
+    const uint32_t tid = threadIdx.x & (C::NT - 1);
+    // small arrays: the loaders' table entries are read with the pass's own
+    // parameters, before anything waits for either (one round trip in all)
+    uint64_t blk[kSmallBlkBits], lin[C::NTL + C::JL];
+    uint32_t llds[C::NTL];
+    if constexpr (SB) {
+#pragma unroll
+        for (int k = 0; k < kSmallBlkBits; ++k) blk[k] = d.in_blk[k];
+#pragma unroll
+        for (int k = 0; k < C::NTL + C::JL; ++k) lin[k] = d.ld_in[k];
+#pragma unroll
+        for (int k = 0; k < C::NTL; ++k) llds[k] = d.ld_lds[k];
+    }
+    const int blk_bits = d.blk_bits, grid_log2 = d.grid_log2, walk = d.walk;
+    if constexpr (SB) {
+        // an empty asm that takes an XOR of every entry (and of the input
+        // pointer) keeps the reads here,
+        // where they wait together with the parameters' (the compiler would
+        // otherwise sink them into the loaders' branch, behind that wait)
+        uint64_t keep = (uint64_t)(uintptr_t)in;
+#pragma unroll
+        for (int k = 0; k < kSmallBlkBits; ++k) keep ^= blk[k];
+#pragma unroll
+        for (int k = 0; k < C::NTL + C::JL; ++k) keep ^= lin[k];
+#pragma unroll
+        for (int k = 0; k < C::NTL; ++k) keep ^= llds[k];
+        asm volatile("" ::"s"(keep));
+    }
+    const int r = blk_bits - grid_log2;
+    const bool interleaved = walk == BMMC_WALK_INTERLEAVED;
     const uint64_t walker = walker_index(blockIdx.x);
     const uint64_t first = interleaved ? walker : (walker << r);
-    const int shift = interleaved ? d.grid_log2 : 0;
+    const int shift = interleaved ? grid_log2 : 0;
     const uint64_t count = uint64_t(1) << r;
-
 
     // Each role runs its own loop with exactly `count` barriers, so every
     // wave meets the same barriers; keeping the roles' code apart leaves each
@@ -278,9 +325,25 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
     // loads only (a shared loop body merges both roles' paths and its waits
     // fall back to "everything outstanding").
     if (loader) {
+        LaneParts p;
+        p.out_lane = 0;
+        p.rd_lane = 0;
         // running input base of the last tile loaded (tiles are loaded in
         // walk order, DEPTH ahead of the one being staged)
-        uint64_t in_base = base_finish<C>(base_issue<C>(d.in_blk, first), first);
+        uint64_t in_base;
+        uint64_t jo[C::J];  // small-array path: per-pass offsets of the first tile
+        if constexpr (SB) {
+            in_base = dev::xor_bits_lane<kSmallBlkBits>(blk, (uint32_t)first);
+            p.in_lane = dev::xor_bits_lane<C::NTL>(lin, tid);
+            p.wr_lane = dev::xor_bits_lane<C::NTL>(llds, tid);
+#pragma unroll
+            for (int j = 0; j < C::J; ++j)
+                jo[j] = dev::xor_bits_lane<C::JL>(lin + C::NTL, (uint32_t)j);
+        } else {
+            p.in_lane = dev::xor_bits_lane<C::NTL>(d.ld_in, tid);
+            p.wr_lane = dev::xor_bits_lane<C::NTL>(d.ld_lds, tid);
+            in_base = base_finish<C>(base_issue<C>(d.in_blk, first), first);
+        }
         uint64_t loaded = 0;  // tiles loaded so far
         dev::Chunk<C::CB> v[DEPTH][C::J];
         // next tile in walk order: one table entry per step (Gray code)
@@ -288,7 +351,10 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
             in_base ^= d.in_blk[shift + __builtin_ctzll(loaded)];
             ++loaded;
         };
-        load_tile<C, T, NT>(v[0], in, in_base, d, p);
+        if constexpr (SB)
+            load_tile_jo<C, T, NT>(v[0], in, in_base, jo, p);
+        else
+            load_tile<C, T, NT>(v[0], in, in_base, d, p);
         loaded = 1;
         if (count == 1) {
             stage_tile<C, T>(lds, v[0], d, p);
@@ -326,6 +392,11 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
             __syncthreads();
         }
     } else {
+        LaneParts p;
+        p.in_lane = 0;
+        p.wr_lane = 0;
+        p.out_lane = dev::xor_bits_lane<C::NTL>(d.st_out, tid);
+        p.rd_lane = dev::xor_bits_lane<C::NTL>(d.st_lds, tid);
         // running bases of the next tile to drain
         const uint64_t e_out = base_issue<C>(d.out_blk, first);
         const uint32_t e_rd = base_issue<C>(d.lds_blk, first);
@@ -360,14 +431,23 @@ template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
     using C = TiledCfg<UL, T, IT>;
     if (a.d->launch == BMMC_LAUNCH_STREAMED) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072 && C::NT >= 64 && 2 * C::NT <= 1024) {
-            if (a.d->depth == 2)
-                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT>),
-                                   dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
-                                   a.out, *a.d);
-            else
-                hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT>),
-                                   dim3(1u << a.d->grid_log2), dim3(2 * C::NT), 0, a.s, a.in,
-                                   a.out, *a.d);
+            const dim3 grid(1u << a.d->grid_log2), block(2 * C::NT);
+            const bool small = a.d->blk_bits <= kSmallBlkBits;
+            if (a.d->depth == 2) {
+                if (small)
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, true>), grid,
+                                       block, 0, a.s, a.in, a.out, *a.d);
+                else
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, false>), grid,
+                                       block, 0, a.s, a.in, a.out, *a.d);
+            } else {
+                if (small)
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, true>), grid,
+                                       block, 0, a.s, a.in, a.out, *a.d);
+                else
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, false>), grid,
+                                       block, 0, a.s, a.in, a.out, *a.d);
+            }
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
         } else {
             return BMMC_ERR_UNSUPPORTED;
