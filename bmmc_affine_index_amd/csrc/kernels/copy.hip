@@ -20,10 +20,10 @@ constexpr int kCopyNTL = 8;  // 256 threads
 //   64 MiB       5770                      5865
 //   128 MiB      6160                      6100
 //   1 GiB        6491                      5897
-// and the hints add 5-15% over plain loads and stores from 4 MiB up.  (At
+// and the hints add 5-15% over plain loads and stores from 4 MiB up.  At
 // 32 MiB a one-shot launch with 4 x 16 B per lane measured 5560, faster than
-// the grid-stride loop's one trip over the same 2048 workgroups; the reason
-// is not known, and that size keeps the loop.)
+// the grid-stride loop's one trip over the same 2048 workgroups (the reason is
+// not known); arrays in (16 MiB, 32 MiB] take that launch.
 template <int CPTL>
 __global__ void __launch_bounds__(1 << kCopyNTL)
     bmmc_copy_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, uint64_t n16,
@@ -65,7 +65,12 @@ __global__ void __launch_bounds__(1 << kCopyNTL)
     }
 }
 
-// the grid-stride form serves (kCopyStrideMinBytes, kCopyStrideMaxBytes]
+// the one-shot form with 4 x 16 B per lane serves (kCopyWideMinBytes,
+// kCopyWideMaxBytes], the grid-stride form the rest of
+// (kCopyStrideMinBytes, kCopyStrideMaxBytes]
+constexpr uint64_t kCopyWideMinBytes = uint64_t(16) << 20;
+constexpr uint64_t kCopyWideMaxBytes = uint64_t(32) << 20;
+constexpr int kCopyWideCPTL = 2;
 constexpr uint64_t kCopyStrideMinBytes = uint64_t(8) << 20;
 constexpr uint64_t kCopyStrideMaxBytes = uint64_t(64) << 20;
 constexpr int kCopyStrideCPTL = 2;
@@ -86,7 +91,12 @@ int launch_copy(const void *in_v, void *out_v, size_t nbytes, hipStream_t s) {
     uint64_t done = 0;
     if (aligned) {
         const uint64_t n16 = nbytes / 16;
-        if (nbytes > kCopyStrideMinBytes && nbytes <= kCopyStrideMaxBytes) {
+        if (nbytes > kCopyWideMinBytes && nbytes <= kCopyWideMaxBytes) {
+            const uint64_t per = uint64_t(1) << (kCopyNTL + kCopyWideCPTL);
+            const uint64_t blocks = (n16 + per - 1) / per;  // at most 2048
+            hipLaunchKernelGGL(bmmc_copy_kernel<kCopyWideCPTL>, dim3((uint32_t)blocks),
+                               dim3(1 << kCopyNTL), 0, s, in, out, n16, uint64_t(0));
+        } else if (nbytes > kCopyStrideMinBytes && nbytes <= kCopyStrideMaxBytes) {
             const uint64_t per = uint64_t(1) << (kCopyNTL + kCopyStrideCPTL);
             const uint64_t blocks = (n16 + per - 1) / per;
             const uint32_t g = blocks < kCopyStrideBlocks ? (uint32_t)blocks : kCopyStrideBlocks;

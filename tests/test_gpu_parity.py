@@ -148,12 +148,14 @@ def test_random_general_sweep(seed):
 
 def test_copy_ceiling_kernel():
     torch = _torch()
-    # both launch shapes (one-shot up to 8 MiB and above 64 MiB, grid-stride
-    # between), their edges, and ragged byte tails; each buffer has 64 spare
-    # bytes that must keep the sentinel
+    # every launch shape (one-shot up to 8 MiB and above 64 MiB, grid-stride
+    # in (8, 16] and (32, 64] MiB, one-shot with four vectors per lane in
+    # (16, 32] MiB), their edges, and ragged byte tails; each buffer has 64
+    # spare bytes that must keep the sentinel
     for nbytes in (0, 1, 15, 16, 4096 + 7, (1 << 20) + 48, 3 << 20, 4 << 20, (4 << 20) + 16,
-                   (6 << 20) + 3, 8 << 20, (8 << 20) + 16, (17 << 20) + 5, 64 << 20,
-                   (64 << 20) + 16, (200 << 20) + 9):
+                   (6 << 20) + 3, 8 << 20, (8 << 20) + 16, 16 << 20, (16 << 20) + 16,
+                   (17 << 20) + 5, 32 << 20, (32 << 20) + 16, 64 << 20, (64 << 20) + 16,
+                   (200 << 20) + 9):
         src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda:0")
         dst = torch.full_like(src, SENTINEL)
         bm.copy(src, dst, nbytes)
