@@ -26,6 +26,8 @@ ERR_UNSUPPORTED = 3
 ERR_ALIAS = 4
 ERR_OUT_OF_MEMORY = 5
 ERR_HIP = 6
+ERR_SCRATCH_LIMIT = 7
+NOALLOC_SCRATCH_BYTES = 1 << 26
 
 KIND_IDENTITY, KIND_BPC, KIND_TILED, KIND_GENERAL = 0, 1, 2, 3
 KIND_NAMES = {0: "identity", 1: "bpc", 2: "tiled", 3: "general"}
@@ -42,7 +44,8 @@ MAX_CHUNK_BITS = 16
 MAX_PASSES = 2
 
 EXPORTED = (
-    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_plan_tune", "bmmc_plan_tune_pairs",
+    "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_execute_noalloc",
+    "bmmc_plan_tune", "bmmc_plan_tune_pairs",
     "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
     "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_plan_get_options", "bmmc_parm_matrix",
@@ -118,6 +121,9 @@ def lib():
     L.bmmc_execute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p]
     L.bmmc_execute.restype = ctypes.c_int
+    L.bmmc_execute_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    L.bmmc_execute_noalloc.restype = ctypes.c_int
     L.bmmc_plan_tune.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int]
     L.bmmc_plan_tune.restype = ctypes.c_int
@@ -214,6 +220,10 @@ def bmmc_plan_create_ex(n: int, A: Sequence[int], c: int, elem_bytes: int,
 
 def bmmc_execute(plan: int, inp, out, stream=None) -> int:
     return lib().bmmc_execute(plan, _ptr(inp), _ptr(out), _stream(stream))
+
+
+def bmmc_execute_noalloc(plan: int, inp, out, stream=None) -> int:
+    return lib().bmmc_execute_noalloc(plan, _ptr(inp), _ptr(out), _stream(stream))
 
 
 def bmmc_plan_tune(plan: int, inp, out, stream=None, reps: int = 0) -> int:

@@ -29,7 +29,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) +
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) + glob.glob(os.path.join(CSRC, "*.hip")) +
                   glob.glob(os.path.join(CSRC, "kernels", "*.hip")))
 
 

@@ -90,6 +90,28 @@ int run_passes(const bmmc_pass_desc *pass, int npasses, const void *in, void *ou
 
 }  // namespace
 
+namespace bmmc {
+
+int check_execute_buffers(const bmmc_plan *p, const void *in, const void *out) {
+    return check_buffers(p, in, out);
+}
+
+// bmmc_execute with the caller's scratch array (at least one array's bytes on
+// the current device) in place of the plan's own; used by the entry point
+// that allocates nothing.
+int execute_with_scratch(const bmmc_plan *p, const void *in, void *out, void *scratch,
+                         hipStream_t s) {
+    int st = check_buffers(p, in, out);
+    if (st != BMMC_OK) return st;
+    if (p->npasses == 1) return run_pass(p->pass[0], in, out, s);
+    if (!scratch) return BMMC_ERR_INVALID_ARG;
+    if (overlaps(in, scratch, bytes_of(p)) || overlaps(out, scratch, bytes_of(p)))
+        return BMMC_ERR_ALIAS;
+    return run_passes(p->pass, p->npasses, in, out, scratch, s);
+}
+
+}  // namespace bmmc
+
 extern "C" {
 
 bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem_bytes,
@@ -286,6 +308,8 @@ const char *bmmc_status_string(int status) {
     case BMMC_ERR_ALIAS: return "input and output overlap";
     case BMMC_ERR_OUT_OF_MEMORY: return "out of memory";
     case BMMC_ERR_HIP: return "HIP runtime error";
+    case BMMC_ERR_SCRATCH_LIMIT:
+        return "two-pass plan larger than the fixed no-allocation scratch buffer";
     default: return "unknown status";
     }
 }

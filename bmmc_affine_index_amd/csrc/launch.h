@@ -16,6 +16,13 @@ int launch_chunk(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t
 // Identity-order copy of nbytes.
 int launch_copy(const void *in, void *out, size_t nbytes, hipStream_t s);
 
+// bmmc_execute's argument checks (NULL, alignment, overlap), host-only.
+int check_execute_buffers(const bmmc_plan *p, const void *in, const void *out);
+// bmmc_execute through a scratch array the caller provides (one array's
+// bytes on the current device; one-pass plans ignore it).  Defined in api.cpp.
+int execute_with_scratch(const bmmc_plan *p, const void *in, void *out, void *scratch,
+                         hipStream_t s);
+
 // Whether the tile kernel is compiled for this unit size, side, iteration
 // count and launch style.
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch);

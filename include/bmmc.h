@@ -42,6 +42,8 @@ extern "C" {
 #define BMMC_ERR_ALIAS 4         /* the in and out byte ranges overlap */
 #define BMMC_ERR_OUT_OF_MEMORY 5 /* scratch allocation failed */
 #define BMMC_ERR_HIP 6           /* a HIP runtime call or kernel launch failed */
+#define BMMC_ERR_SCRATCH_LIMIT 7 /* bmmc_execute_noalloc: the plan needs more scratch than
+                                    the fixed BMMC_NOALLOC_SCRATCH_BYTES */
 
 /* ---- classification of A (at the granularity the kernels move) --------- */
 #define BMMC_KIND_IDENTITY 0 /* A = I: a copy, or a complement-only XOR */
@@ -208,6 +210,22 @@ bmmc_plan *bmmc_plan_create_ex(int n, const uint64_t *A, uint64_t c, size_t elem
  * Launch failures return BMMC_ERR_HIP; faults inside a kernel surface at the
  * caller's next synchronisation, as HIP reports them. */
 int bmmc_execute(const bmmc_plan *plan, const void *in, void *out, void *stream);
+
+/* bmmc_execute for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, result and errors as bmmc_execute, and the same kernels;
+ * it calls no hipMalloc, hipFree or other allocating routine.  One-pass plans
+ * need nothing beyond in and out.  A two-pass plan stages the array between
+ * its passes in a fixed device buffer of BMMC_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends;
+ * plans whose array (2^n * elem_bytes) is larger return
+ * BMMC_ERR_SCRATCH_LIMIT before any GPU call.  Every call on one GPU shares
+ * that GPU's buffer: two-pass calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * serialised by the caller.  Nothing in the buffer needs clearing: the first
+ * pass writes all of it that the second pass reads. */
+#define BMMC_NOALLOC_SCRATCH_BYTES ((size_t)1 << 26)
+int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void *stream);
 
 /* Measure and keep the fastest tile order for this plan on this device.
  * Which tiles run together decides how well the DRAM pages of HBM are reused,

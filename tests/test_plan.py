@@ -108,6 +108,27 @@ def test_execute_argument_errors_without_gpu():
             bm.bmmc_plan_get_pass(p.handle, k)
 
 
+def test_execute_noalloc_refuses_without_gpu():
+    """bmmc_execute_noalloc makes every check before its first HIP call: the
+    buffer rules of bmmc_execute, and a two-pass plan larger than the fixed
+    scratch buffer (these fake addresses are never touched)."""
+    p = bm.Plan(10, wl.bit_reverse_matrix(10), 0, 4)
+    assert bm.bmmc_execute_noalloc(p.handle, 0, 4096, None) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_execute_noalloc(0, 4096, 8192, None) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_execute_noalloc(p.handle, 1 << 20 | 4, 1 << 24, None) == bm.ERR_INVALID_ARG
+    assert bm.bmmc_execute_noalloc(p.handle, 1 << 20, (1 << 20) + 2048, None) == bm.ERR_ALIAS
+    n = 25  # 2^25 int32: twice the buffer
+    A, c = _inv(n, 25)
+    q = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    assert q.info.passes == 2 and q.info.scratch_bytes > bm.NOALLOC_SCRATCH_BYTES
+    assert bm.bmmc_execute_noalloc(q.handle, 1 << 40, 1 << 41, None) == bm.ERR_SCRATCH_LIMIT
+    assert "scratch" in bm.bmmc_status_string(bm.ERR_SCRATCH_LIMIT)
+    # the header's size is the binding's
+    header = open(os.path.join(ROOT, "include", "bmmc.h")).read()
+    assert re.search(r"#define BMMC_NOALLOC_SCRATCH_BYTES \(\(size_t\)1 << 26\)", header)
+    assert bm.NOALLOC_SCRATCH_BYTES == 1 << 26
+
+
 def test_tune_argument_errors_without_gpu():
     """bmmc_plan_tune validates before any HIP call: the same buffer rules as
     bmmc_execute and reps in [0, 1000] (these fake addresses are never
