@@ -110,10 +110,12 @@ def lib_accepts(n: int):
     return accept
 
 
-def time_loop(torch, fn, bufs, steps, warmup, stream, graph=True):
-    """Warm up, then time exactly `steps` calls fn(in, out, stream_handle)
-    with events on `stream`.  graph=True captures the `steps` calls once into
-    a HIP graph and the timed region replays it, so the host's per-call cost
+def time_replays(torch, fn, bufs, steps, warmup, stream, replays=5, graph=True):
+    """Warm up, then time `replays` regions of exactly `steps` calls
+    fn(in, out, stream_handle) each, with events on `stream` and a
+    synchronisation on both sides of every region; returns the milliseconds
+    per step of each region.  graph=True captures the `steps` calls once into
+    a HIP graph and each region replays it, so the host's per-call cost
     (ctypes, argument checks, the launch itself) stays out of the measurement
     of arrays whose steps take microseconds."""
     h = int(stream.cuda_stream)
@@ -121,6 +123,7 @@ def time_loop(torch, fn, bufs, steps, warmup, stream, graph=True):
         fn(*bufs[k % len(bufs)], h)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
     if graph:
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -130,18 +133,37 @@ def time_loop(torch, fn, bufs, steps, warmup, stream, graph=True):
                 fn(*bufs[k % len(bufs)], hc)
         g.replay()  # first replay uploads the graph
         torch.cuda.synchronize()
-        start.record(stream)
-        g.replay()
-        stop.record(stream)
-        torch.cuda.synchronize()
+        for _ in range(replays):
+            start.record(stream)
+            g.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            out.append(start.elapsed_time(stop) / steps)
         del g
     else:
-        start.record(stream)
-        for k in range(steps):
-            fn(*bufs[k % len(bufs)], h)
-        stop.record(stream)
-        torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+        for _ in range(replays):
+            start.record(stream)
+            for k in range(steps):
+                fn(*bufs[k % len(bufs)], h)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            out.append(start.elapsed_time(stop) / steps)
+    return out
+
+
+def time_loop(torch, fn, bufs, steps, warmup, stream, graph=True):
+    """Milliseconds per step of one timed region of `steps` calls."""
+    return time_replays(torch, fn, bufs, steps, warmup, stream, replays=1, graph=graph)[0]
+
+
+def replay_stats(ms_list, algo_bytes):
+    """Median, min and max over timed regions, as ms per step and GB/s."""
+    v = sorted(ms_list)
+    med = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    gbs = lambda ms: algo_bytes / (ms * 1e-3) / 1e9  # noqa: E731
+    return {"ms_per_step": med, "ms_min": v[0], "ms_max": v[-1],
+            "ms_mean": sum(v) / len(v), "gbs": gbs(med), "gbs_min": gbs(v[-1]),
+            "gbs_max": gbs(v[0]), "replays": len(v)}
 
 
 def per_launch_ms(torch, fn, bufs, reps, stream):
@@ -158,11 +180,52 @@ def per_launch_ms(torch, fn, bufs, reps, stream):
     return ms[len(ms) // 2], ms[0], ms[-1]
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle: the cores this process may run on (its
+    CPU affinity), or OMP_NUM_THREADS where the host sets the process's CPU
+    share that way."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def sampled_parity(torch, A, c, x, out, samples=1 << 20, seed=1):
+    """Check out[A.i XOR c] = x[i] on `samples` seeded input indices plus the
+    first and last: the oracle maps each sampled index, the device gathers
+    those output elements, and the host compares them with the input's.
+    Returns (mismatches, checked)."""
+    import oracle
+    n = len(A)
+    N = 1 << n
+    elem = x.nbytes >> n
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = np.concatenate([np.array([0, N - 1], dtype=np.uint64),
+                          rng.integers(0, N, size=samples, dtype=np.uint64)])
+    pos = oracle.map_indices(A, c, idx)
+    rows = out.view(torch.uint8).reshape(N, elem)
+    got = rows.index_select(0, torch.from_numpy(pos.astype(np.int64)).to(out.device)).cpu().numpy()
+    want = np.ascontiguousarray(x).reshape(-1).view(np.uint8).reshape(N, elem)[idx.astype(np.int64)]
+    bad = int(np.count_nonzero(np.any(got != want, axis=1)))
+    return bad, int(idx.size)
+
+
+def full_parity(A, c, x, got_host):
+    """The whole output against the oracle's; True when every byte agrees."""
+    import oracle
+    want = oracle.apply(A, c, x, threads=oracle_threads())
+    return np.array_equal(np.ascontiguousarray(got_host).view(np.uint8).reshape(-1),
+                          want.view(np.uint8).reshape(-1))
+
+
 def cpu_baseline(A, c, x, budget_s: float):
     """The oracle, as it stands, on the host cores: repeated full-array
     scatters (or index ranges for big arrays) for about budget_s seconds."""
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = oracle_threads()
     n = len(A)
     N = 1 << n
     elem = x.nbytes >> n
@@ -300,14 +363,189 @@ def run_ablation(args, torch):
         torch.cuda.empty_cache()
 
 
+# The configurations measured beside the headline, in the order they run:
+# (key, workload, route).  c4's two-pass route reuses the headline's buffers.
+CONFIG_CASES = [
+    ("c4_two_pass", "c4", bm.ROUTE_TWO_PASS),
+    ("c1a_fused", "c1a", bm.ROUTE_AUTO),
+    ("c1a_two_pass", "c1a", bm.ROUTE_TWO_PASS),
+    ("c1b", "c1b", bm.ROUTE_AUTO),
+    ("c2", "c2", bm.ROUTE_AUTO),
+    ("c3", "c3", bm.ROUTE_AUTO),
+    ("c5", "c5", bm.ROUTE_AUTO),
+]
+C5_PERMS = 32
+
+
+def log(msg):
+    print("bench.py: " + msg, file=sys.stderr, flush=True)
+
+
+class Runner:
+    """Buffers, timing and parity checks shared by the headline and the
+    configurations; the copy ceiling is timed once per array size."""
+
+    def __init__(self, torch, args):
+        self.torch, self.args = torch, args
+        self.stream = torch.cuda.current_stream()
+        self.h = int(self.stream.cuda_stream)
+        self.graph = not args.no_graph
+        self.copies = {}
+
+    def buffers(self, x, nbytes):
+        """Rotating (input, output) pairs with at least 1 GiB of working set
+        (four times the 256 MB Infinity Cache), or one pair with --warm."""
+        torch = self.torch
+        pairs = 1 if self.args.warm else max(1, -(-(1 << 30) // (2 * nbytes)))
+        raw = torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.uint8)).to("cuda:0")
+        ins = [raw] + [raw.clone() for _ in range(pairs - 1)]
+        outs = [torch.empty_like(raw) for _ in range(pairs)]
+        return list(zip(ins, outs))
+
+    def steps_for(self, nbytes, headline):
+        """The headline times exactly --steps steps per region; the other
+        configurations take more steps on small arrays, so that a region
+        lasts about 2 ms (1000 steps at most)."""
+        if headline:
+            return self.args.steps
+        return max(self.args.steps, min(1000, int(2e-3 * 5e12 / (2.0 * nbytes))))
+
+    def time_plan(self, plan, bufs, nbytes, steps):
+        def step(i, o, h):
+            st = bm.bmmc_execute(plan.handle, i, o, h)
+            if st != bm.OK:
+                raise bm.BmmcError(st, "bmmc_execute")
+        ms = time_replays(self.torch, step, bufs, steps, self.args.warmup, self.stream,
+                          self.args.replays, graph=self.graph)
+        return replay_stats(ms, 2.0 * nbytes)
+
+    def copy_ceiling(self, bufs, nbytes, steps):
+        key = (nbytes, steps)
+        if key not in self.copies:
+            def copy(i, o, h):
+                st = bm.bmmc_copy(i, o, nbytes, h)
+                if st != bm.OK:
+                    raise bm.BmmcError(st, "bmmc_copy")
+            ms = time_replays(self.torch, copy, bufs, steps, self.args.warmup, self.stream,
+                              self.args.replays, graph=self.graph)
+            self.copies[key] = replay_stats(ms, 2.0 * nbytes)
+        return self.copies[key]
+
+    def parity(self, plan, A, c, x, bufs):
+        """Run the plan once more on the first pair and check it against the
+        oracle: the whole array up to n = 24, 2^20 + 2 sampled elements
+        (gathered on the device) above.  Returns (ok, text)."""
+        torch = self.torch
+        i0, o0 = bufs[0]
+        o0.fill_(0xA5)
+        plan(i0, o0, self.h)
+        torch.cuda.synchronize()
+        n = len(A)
+        if self.args.no_check:
+            return True, "skipped"
+        if n <= 24:
+            ok = full_parity(A, c, x, o0.cpu().numpy())
+            return ok, ("bit-exact vs oracle (all %d elements)" % (1 << n) if ok else "MISMATCH")
+        bad, checked = sampled_parity(torch, A, c, x, o0)
+        return bad == 0, ("bit-exact vs oracle (%d sampled elements)" % checked if bad == 0
+                          else "MISMATCH (%d of %d samples)" % (bad, checked))
+
+
+def plan_brief(plan):
+    d = plan.describe()
+    return {"route": d["route"], "passes": d["passes"], "kernels": d["kernels"],
+            "tile_log2": d["tile_log2"], "block_map": d["block_map"],
+            "unit_bytes": d["unit_bytes"]}
+
+
+def measure_case(run, name, route, x=None, bufs=None, A=None, c=None):
+    """One configuration at its own size: plan, tune over the rotating pairs,
+    time, and check; returns its entry of the configs object."""
+    w = wl.WORKLOADS[name]
+    n, elem = w.n, w.elem_bytes
+    nbytes = elem << n
+    if A is None:
+        A, c = wl.workload_matrix(name, accept=lib_accepts(n))
+    if x is None:
+        x = wl.workload_data(name)
+    if bufs is None:
+        bufs = run.buffers(x, nbytes)
+    plan = bm.Plan(n, A, c, elem, route=route)
+    t0 = time.perf_counter()
+    if not run.args.no_tune:
+        plan.tune(pairs=bufs, stream=run.h)
+    tune_ms = (time.perf_counter() - t0) * 1e3
+    steps = run.steps_for(nbytes, headline=False)
+    r = run.time_plan(plan, bufs, nbytes, steps)
+    cp = run.copy_ceiling(bufs, nbytes, steps)
+    ok, parity = run.parity(plan, A, c, x, bufs)
+    e = {"workload": WORKLOAD_NAMES[name], "n": n, "elem_bytes": elem,
+         "gbs": round(r["gbs"], 2), "gbs_min": round(r["gbs_min"], 2),
+         "gbs_max": round(r["gbs_max"], 2), "ms_per_step": round(r["ms_per_step"], 6),
+         "frac_of_copy": round(r["gbs"] / cp["gbs"], 4),
+         "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
+         "copy_gbs": round(cp["gbs"], 2), "steps": steps, "replays": r["replays"],
+         "plan": plan_brief(plan), "plan_options": plan.options(),
+         "tune_ms": round(tune_ms, 1), "parity": parity}
+    if plan.info.passes > 1:
+        e["transfer_gbs"] = round(plan.info.passes * r["gbs"], 2)
+    return e, ok
+
+
+def measure_c5(run):
+    """c5's protocol: each of the 32 seeded bit permutations planned, tuned,
+    timed and checked on the same buffers; min / median / max."""
+    w = wl.WORKLOADS["c5"]
+    n, elem = w.n, w.elem_bytes
+    nbytes = elem << n
+    x = wl.workload_data("c5")
+    bufs = run.buffers(x, nbytes)
+    steps = run.steps_for(nbytes, headline=False)
+    cp = run.copy_ceiling(bufs, nbytes, steps)
+    vals, okays, plans = [], 0, []
+    for k in range(C5_PERMS):
+        A, c = wl.workload_matrix("c5", perm_index=k)
+        plan = bm.Plan(n, A, c, elem)
+        if not run.args.no_tune:
+            plan.tune(pairs=bufs, stream=run.h)
+        r = run.time_plan(plan, bufs, nbytes, steps)
+        ok, parity = run.parity(plan, A, c, x, bufs)
+        okays += ok
+        vals.append(r["gbs"])
+        d = plan.describe()
+        plans.append("%s t=%s order %s" % (d["kernels"][-1], d["tile_log2"], d["block_map"]))
+        log("c5 perm %d: %.1f GB/s (%.3f of copy) %s, %s" % (k, r["gbs"], r["gbs"] / cp["gbs"],
+                                                          plans[-1], parity))
+    order = sorted(range(len(vals)), key=lambda i: vals[i])
+    med = 0.5 * (vals[order[len(vals) // 2 - 1]] + vals[order[len(vals) // 2]])
+    e = {"workload": WORKLOAD_NAMES["c5"], "n": n, "elem_bytes": elem, "perms": len(vals),
+         "min_gbs": round(vals[order[0]], 2), "median_gbs": round(med, 2),
+         "max_gbs": round(vals[order[-1]], 2),
+         "min_frac_of_copy": round(vals[order[0]] / cp["gbs"], 4),
+         "median_frac_of_copy": round(med / cp["gbs"], 4),
+         "max_frac_of_copy": round(vals[order[-1]] / cp["gbs"], 4),
+         "median_frac_of_hbm_peak": round(med / HBM_PEAK_GBS, 4),
+         "min_perm": order[0], "max_perm": order[-1], "copy_gbs": round(cp["gbs"], 2),
+         "steps": steps, "replays": run.args.replays,
+         "per_perm_gbs": [round(v, 1) for v in vals], "per_perm_plan": plans,
+         "parity": ("bit-exact vs oracle on %d of %d permutations (2^20 + 2 sampled "
+                    "elements each)" % (okays, len(vals)))}
+    return e, okays == len(vals)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 200; 1000 for the 4 MiB workloads, whose "
-                         "single steps take microseconds)")
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps per timed region of the headline (the other "
+                         "configurations take more on small arrays)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replays", type=int, default=5,
+                    help="timed regions per measurement; the median is reported, with min and max")
+    ap.add_argument("--workload", default="c4", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--configs", default="auto", choices=["auto", "all", "none"],
+                    help="also measure every other configuration (auto: only with the "
+                         "default headline)")
     ap.add_argument("--kind", default=None,
                     choices=["bitrev", "transpose", "bpc", "bmmc", "blockperm", "reverse"],
                     help="custom workload instead of --workload: the matrix kind "
@@ -318,7 +556,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1, help="custom workload: matrix seed")
     ap.add_argument("--perm", type=int, default=0, help="c5: permutation index 0..31")
     ap.add_argument("--perms", type=int, default=0,
-                    help="c5: time permutations 0..PERMS-1 and report min/median/max")
+                    help="c5 as --workload: time permutations 0..PERMS-1 and report "
+                         "min/median/max")
     ap.add_argument("--route", default="auto", choices=["auto", "naive", "two_pass", "fused"])
     ap.add_argument("--tile-log2", type=int, default=0)
     ap.add_argument("--iters-log2", type=int, default=0)
@@ -346,13 +585,19 @@ def main():
                          "one JSON line each (not the headline line)")
     ap.add_argument("--sizes", default="20,24,28", help="ablation: comma-separated n")
     args = ap.parse_args()
-    if args.steps is None:
-        args.steps = 1000 if (args.workload in ("c1a", "c1b") and not args.kind) else 200
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.replays < 1:
+        print("bench.py: --steps and --replays must be positive", file=sys.stderr)
+        sys.exit(2)
+    explicit_workload = "--workload" in sys.argv[1:] or any(
+        a.startswith("--workload=") for a in sys.argv[1:])
+    with_configs = args.configs == "all" or (
+        args.configs == "auto" and not (args.kind or args.plan_options or explicit_workload
+                                        or args.perms or args.warm))
 
     import torch
     if not torch.cuda.is_available():
@@ -396,30 +641,26 @@ def main():
     nbytes = elem << n
     route = {"auto": bm.ROUTE_AUTO, "naive": bm.ROUTE_NAIVE, "two_pass": bm.ROUTE_TWO_PASS,
              "fused": bm.ROUTE_FUSED}[args.route]
-
-    t0 = time.perf_counter()
     launch = {"auto": bm.LAUNCH_AUTO, "one_tile": bm.LAUNCH_ONE_TILE,
               "persistent": bm.LAUNCH_PERSISTENT, "streamed": bm.LAUNCH_STREAMED}[args.launch]
+    plan_kw = dict(route=route, tile_log2=args.tile_log2, no_swizzle=args.no_swizzle,
+                   iters_log2=args.iters_log2, launch=launch, grid_log2=args.grid_log2,
+                   walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
+                   block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
+
+    t0 = time.perf_counter()
     if args.plan_options:
         plan = bm.Plan(n, A, c, elem, **json.loads(args.plan_options))
         args.no_tune = True
     else:
-        plan = bm.Plan(n, A, c, elem, route=route, tile_log2=args.tile_log2,
-                       no_swizzle=args.no_swizzle, iters_log2=args.iters_log2, launch=launch,
-                       grid_log2=args.grid_log2,
-                       walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
-                       block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
+        plan = bm.Plan(n, A, c, elem, **plan_kw)
     plan_us = (time.perf_counter() - t0) * 1e6
     if name == "c4" and not args.kind and route == bm.ROUTE_TWO_PASS:
         assert plan.info.passes == 2
 
-    pairs = 1 if args.warm else max(1, -(-(1 << 30) // (2 * nbytes)))
-    raw = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
-    ins = [raw] + [raw.clone() for _ in range(pairs - 1)]
-    outs = [torch.empty_like(raw) for _ in range(pairs)]
-    bufs = list(zip(ins, outs))
-    stream = torch.cuda.current_stream()
-    s_handle = int(stream.cuda_stream)
+    run = Runner(torch, args)
+    log("headline %s: %s" % (workload_name, plan.describe()["kernels"]))
+    bufs = run.buffers(x, nbytes)
 
     # bmmc_plan_tune_pairs: time the candidate tile orders over the same
     # rotating buffer pairs and keep the fastest (outside the timed region,
@@ -427,7 +668,7 @@ def main():
     tune_ms = None
     if not args.no_tune:
         t0 = time.perf_counter()
-        plan.tune(pairs=bufs, stream=s_handle)
+        plan.tune(pairs=bufs, stream=run.h)
         tune_ms = (time.perf_counter() - t0) * 1e3
 
     def step(i, o, h):
@@ -435,85 +676,63 @@ def main():
         if st != bm.OK:
             raise bm.BmmcError(st, "bmmc_execute")
 
-    def copy(i, o, h):
-        st = bm.bmmc_copy(i, o, nbytes, h)
-        if st != bm.OK:
-            raise bm.BmmcError(st, "bmmc_copy")
-
-    graph = not args.no_graph
-    ms = time_loop(torch, step, bufs, args.steps, args.warmup, stream, graph=graph)
-    ms_copy = time_loop(torch, copy, bufs, args.steps, args.warmup, stream, graph=graph)
-    med, mn, mx = per_launch_ms(torch, step, bufs, 20, stream)
-    cmed, _, _ = per_launch_ms(torch, copy, bufs, 20, stream)
-
+    r = run.time_plan(plan, bufs, nbytes, args.steps)
+    cp = run.copy_ceiling(bufs, nbytes, args.steps)
+    med, mn, mx = per_launch_ms(torch, step, bufs, 20, run.stream)
     algo_bytes = 2.0 * nbytes
-    value = algo_bytes / (ms * 1e-3) / 1e9
-    copy_gbs = algo_bytes / (ms_copy * 1e-3) / 1e9
+    value = r["gbs"]
+    copy_gbs = cp["gbs"]
+    log("headline: %.1f GB/s (%.3f of copy)" % (value, value / copy_gbs))
 
     perm_stats = None
     if args.perms and name == "c5" and not args.kind:
-        # the workload's protocol: every permutation planned and timed the
-        # same way on the same buffers; min / median / max of the throughput
-        vals = []
+        # the workload's protocol: every permutation planned, tuned, timed and
+        # checked the same way on the same buffers; min / median / max
+        vals, okays = [], 0
         for k in range(args.perms):
             Ak, ck = wl.workload_matrix(name, perm_index=k)
-            pk = bm.Plan(n, Ak, ck, elem, route=route, tile_log2=args.tile_log2,
-                         no_swizzle=args.no_swizzle, iters_log2=args.iters_log2,
-                         launch=launch, grid_log2=args.grid_log2,
-                         walk={"auto": 0, "ranges": 1, "interleaved": 2}[args.walk],
-                         block_map=args.block_map, depth=args.depth, cache_hint=args.cache_hint)
+            pk = bm.Plan(n, Ak, ck, elem, **plan_kw)
             if not args.no_tune:
-                pk.tune(pairs=bufs, stream=s_handle)
-
-            def stepk(i, o, h, pk=pk):
-                st = bm.bmmc_execute(pk.handle, i, o, h)
-                if st != bm.OK:
-                    raise bm.BmmcError(st, "bmmc_execute")
-            msk = time_loop(torch, stepk, bufs, args.steps, args.warmup, stream, graph=graph)
-            vals.append(algo_bytes / (msk * 1e-3) / 1e9)
+                pk.tune(pairs=bufs, stream=run.h)
+            rk = run.time_plan(pk, bufs, nbytes, args.steps)
+            okk, park = run.parity(pk, Ak, ck, x, bufs)
+            okays += okk
+            vals.append(rk["gbs"])
             dk = pk.describe()
-            print("perm %d: %.1f GB/s (%s t=%s order %s)" % (k, vals[-1], dk["kernels"][-1],
-                                                            dk["tile_log2"], dk["block_map"]),
-                  file=sys.stderr, flush=True)
+            log("perm %d: %.1f GB/s (%s t=%s order %s) %s" % (
+                k, vals[-1], dk["kernels"][-1], dk["tile_log2"], dk["block_map"], park))
         sv = sorted(vals)
+        pmed = 0.5 * (sv[(len(sv) - 1) // 2] + sv[len(sv) // 2])
         perm_stats = {"perms": len(vals), "min_gbs": round(sv[0], 2),
-                      "median_gbs": round(sv[len(sv) // 2], 2), "max_gbs": round(sv[-1], 2),
+                      "median_gbs": round(pmed, 2), "max_gbs": round(sv[-1], 2),
                       "min_frac_of_copy": round(sv[0] / copy_gbs, 4),
-                      "median_frac_of_copy": round(sv[len(sv) // 2] / copy_gbs, 4),
-                      "max_frac_of_copy": round(sv[-1] / copy_gbs, 4)}
+                      "median_frac_of_copy": round(pmed / copy_gbs, 4),
+                      "max_frac_of_copy": round(sv[-1] / copy_gbs, 4),
+                      "parity": "bit-exact on %d of %d permutations" % (okays, len(vals))}
+        if okays != len(vals):
+            perm_stats["parity"] = "MISMATCH: " + perm_stats["parity"]
 
-    parity = "skipped"
-    if not args.no_check:
-        step(*bufs[0], s_handle)
-        torch.cuda.synchronize()
-        got = outs[0].cpu().numpy().view(x.dtype).reshape(x.shape)
-        import oracle
-        if n <= 24:
-            want = oracle.apply(A, c, x, threads=max(1, min(16, os.cpu_count() or 1)))
-            ok = np.array_equal(got.view(np.uint8), want.view(np.uint8))
-            parity = "bit-exact vs oracle (all %d elements)" % (1 << n) if ok else "MISMATCH"
-        else:
-            rng = np.random.Generator(np.random.PCG64(1))
-            idx = rng.integers(0, 1 << n, size=1 << 20, dtype=np.uint64)
-            bad, _ = oracle.check_sampled(A, c, x, got, idx)
-            parity = ("bit-exact vs oracle (2^20 sampled elements)" if bad == 0
-                      else "MISMATCH (%d of 2^20 samples)" % bad)
-        del got
-        if parity.startswith("MISMATCH"):
-            print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
+    ok, parity = run.parity(plan, A, c, x, bufs)
+    if not ok:
+        print("bench.py: output does not match the oracle: %s" % parity, file=sys.stderr)
+    all_ok = ok and not (perm_stats and perm_stats["parity"].startswith("MISMATCH"))
 
     plan_options = plan.options()
     traffic = None if args.kind else read_traffic(name, plan_options, plan_tables_digest(plan))
     passes = plan.info.passes
+    # average launch duration over every timed region (one launch per step
+    # for a one-pass plan)
+    achieved = algo_bytes / (r["ms_mean"] * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
-        "achieved": round(algo_bytes / (ms * 1e-3) / 1e9, 2),
+        "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-normalised)",
         "algorithmic_bytes_per_launch": int(algo_bytes),
+        "kernel": plan.describe()["kernels"][-1],
     }
     if passes > 1:
         roofline["kernel"] = "both passes of the two-pass plan (one step)"
@@ -525,7 +744,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": round(r["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -536,17 +755,23 @@ def main():
             "n": n, "elem_bytes": elem, "bytes_per_step": int(algo_bytes),
             "residency": ("one buffer pair, repeated (cache-warm)" if args.warm else
                           "%d rotating buffer pairs, %.2f GiB working set (HBM)"
-                          % (pairs, 2 * pairs * nbytes / 2**30)),
+                          % (len(bufs), 2 * len(bufs) * nbytes / 2**30)),
             "plan": plan.describe(),
             "plan_options": plan_options,
-            "timing": ("eager calls from Python" if args.no_graph else
-                       "one HIP graph of the %d steps, replayed" % args.steps),
+            "timing": ("%d timed regions of %d eager calls from Python; median"
+                       % (args.replays, args.steps) if args.no_graph else
+                       "one HIP graph of the %d steps, replayed in %d timed regions; median"
+                       % (args.steps, args.replays)),
         },
+        "replays": {"count": r["replays"], "value_min": round(r["gbs_min"], 2),
+                    "value_max": round(r["gbs_max"], 2),
+                    "ms_per_step_min": round(r["ms_min"], 6),
+                    "ms_per_step_max": round(r["ms_max"], 6)},
         "frac_of_copy": round(value / copy_gbs, 4),
         "copy_ceiling_gbs": round(copy_gbs, 2),
+        "copy_ceiling_min_max_gbs": [round(cp["gbs_min"], 2), round(cp["gbs_max"], 2)],
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "launch_ms": {"median": round(med, 5), "min": round(mn, 5), "max": round(mx, 5),
-                      "copy_median": round(cmed, 5)},
+        "launch_ms": {"median": round(med, 5), "min": round(mn, 5), "max": round(mx, 5)},
         "plan_create_us": round(plan_us, 1),
         "plan_tune_ms": round(tune_ms, 1) if tune_ms is not None else None,
         "parity": parity,
@@ -557,11 +782,51 @@ def main():
     if passes > 1:
         # bytes the passes move in total (each reads and writes the array)
         result["transfer_gbs"] = round(passes * value, 2)
+
+    configs = None
+    if with_configs:
+        configs = {"c4_fused": {"workload": workload_name, "gbs": result["value"],
+                                "frac_of_copy": result["frac_of_copy"],
+                                "frac_of_hbm_peak": result["frac_of_hbm_peak"],
+                                "parity": parity, "see": "headline"}}
+        for key, cname, croute in CONFIG_CASES:
+            if key == "c5":
+                continue
+            if cname != "c4":
+                continue
+            e, okc = measure_case(run, cname, croute, x=x, bufs=bufs, A=A, c=c)
+            configs[key] = e
+            all_ok &= okc
+            log("%s: %.1f GB/s (%.3f of copy), %s" % (key, e["gbs"], e["frac_of_copy"],
+                                                      e["parity"]))
     if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, %d threads, about %.0f s)" % (oracle_threads(),
+                                                                   1.2 * args.cpu_budget))
         result["cpu_baseline"] = cpu_baseline(A, c, x, args.cpu_budget)
+    if with_configs:
+        del bufs, step
+        plan.close()
+        x = None
+        torch.cuda.empty_cache()
+        for key, cname, croute in CONFIG_CASES:
+            if cname == "c4":
+                continue
+            if key == "c5":
+                e, okc = measure_c5(run)
+            else:
+                e, okc = measure_case(run, cname, croute)
+            configs[key] = e
+            all_ok &= okc
+            log("%s: %s, %s" % (key, ("%.1f GB/s (%.3f of copy)" % (e["gbs"], e["frac_of_copy"])
+                                      if "gbs" in e else
+                                      "min/median/max %.3f/%.3f/%.3f of copy"
+                                      % (e["min_frac_of_copy"], e["median_frac_of_copy"],
+                                         e["max_frac_of_copy"])), e["parity"]))
+            torch.cuda.empty_cache()
+        result["configs"] = configs
     print(json.dumps(result))
     sys.stdout.flush()
-    if parity.startswith("MISMATCH"):
+    if not all_ok:
         sys.exit(3)
 
 

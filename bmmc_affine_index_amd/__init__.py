@@ -429,9 +429,35 @@ def copy(inp, out, nbytes: Optional[int] = None, stream=None) -> None:
         raise BmmcError(st, "bmmc_copy")
 
 
+def _ordered(run, tensors, stream) -> None:
+    """Call run(stream_handle) on `stream` (None = torch's current stream)
+    in order with torch's current stream: the launch waits for work already
+    queued on the current stream (the producers of the inputs), the current
+    stream then waits for the launch (so its later work sees the outputs),
+    and the tensors are recorded as used on `stream` for the caching
+    allocator."""
+    import torch
+    cur = torch.cuda.current_stream()
+    if stream is None:
+        run(int(cur.cuda_stream))
+        return
+    side = (torch.cuda.ExternalStream(int(stream)) if isinstance(stream, int) else stream)
+    if int(side.cuda_stream) == int(cur.cuda_stream):
+        run(int(cur.cuda_stream))
+        return
+    side.wait_stream(cur)
+    run(int(side.cuda_stream))
+    for t in tensors:
+        t.record_stream(side)
+    cur.wait_stream(side)
+
+
 def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw):
     """out[A.i XOR c] = inp[i] over the first axis of a contiguous device
-    tensor with 2^n rows (a row is one element)."""
+    tensor with 2^n rows (a row is one element).  With a `stream` other than
+    torch's current one, the permutation runs there, ordered after the work
+    already queued on the current stream and before the work queued on it
+    afterwards."""
     import torch
     n = len(A)
     if inp.shape[0] != (1 << n):
@@ -439,7 +465,8 @@ def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw)
     elem = inp.numel() * inp.element_size() >> n
     if out is None:
         out = torch.empty_like(inp)
-    Plan(n, A, c, elem, **plan_kw)(inp, out, stream)
+    plan = Plan(n, A, c, elem, **plan_kw)
+    _ordered(lambda h: plan(inp, out, h), [inp, out], stream)
     return out
 
 

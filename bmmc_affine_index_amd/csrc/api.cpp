@@ -237,9 +237,12 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
         next = (next + 1) % npairs;
         return run_passes(q.pass, q.npasses, ins[k], outs[k], scratch, s);
     };
-    std::vector<float> best(cand.size(), 1e30f);
+    // every candidate is timed in kTuneRounds rounds, the candidates
+    // interleaved within a round, and judged by its median round
+    constexpr int kTuneRounds = 5;
+    std::vector<std::vector<float>> times(cand.size());
     int st = BMMC_OK;
-    for (int round = 0; round < 2 && st == BMMC_OK; ++round)
+    for (int round = 0; round < kTuneRounds && st == BMMC_OK; ++round)
         for (size_t i = 0; i < cand.size() && st == BMMC_OK; ++i) {
             const bmmc_plan &q = *cand[i];
             st = run(q);  // warm-up
@@ -250,8 +253,15 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
                 (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                  hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
                 st = BMMC_ERR_HIP;
-            if (st == BMMC_OK && ms < best[i]) best[i] = ms;
+            if (st == BMMC_OK) times[i].push_back(ms);
         }
+    std::vector<float> best(cand.size(), 1e30f);
+    for (size_t i = 0; i < cand.size(); ++i) {
+        std::vector<float> &v = times[i];
+        if (v.empty()) continue;
+        std::sort(v.begin(), v.end());
+        best[i] = v[v.size() / 2];
+    }
     // the first candidate is the planner's own choice; another replaces it
     // only when faster by more than the margin, so that timing noise between
     // near-equal orders does not change the plan from run to run

@@ -238,8 +238,9 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * the planner's, 1, 3 and 6, and the random orders 8 and 9): up to 24
  * candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
- * for about 2 ms of work, 3 to 200) on `stream`, twice over, timed with HIP
- * events; the fastest replaces the plan's kernel tables if it beats the
+ * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
+ * interleave the candidates, timed with HIP events; the candidate with the
+ * fastest median round replaces the plan's kernel tables if it beats the
  * planner's own choice by more than 2%, and the chosen tables are then run
  * once on ins[0] -> outs[0].
  *

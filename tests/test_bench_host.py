@@ -101,3 +101,42 @@ def test_help_lists_protocol_options():
     for opt in ("--steps", "--warmup", "--no-graph", "--no-tune", "--ablation", "--perms",
                 "--plan-options"):
         assert opt in r.stdout
+
+
+def test_replay_stats_median_and_range():
+    r = bench.replay_stats([2.0, 1.0, 4.0, 3.0, 5.0], 8e9)
+    assert r["ms_per_step"] == 3.0 and r["ms_min"] == 1.0 and r["ms_max"] == 5.0
+    assert r["replays"] == 5 and abs(r["ms_mean"] - 3.0) < 1e-12
+    assert abs(r["gbs"] - 8e9 / 3e-3 / 1e9) < 1e-9
+    assert r["gbs_min"] < r["gbs"] < r["gbs_max"]
+    assert bench.replay_stats([2.0, 4.0], 1e9)["ms_per_step"] == 3.0
+
+
+def test_oracle_threads_follows_the_host_share(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "5")
+    assert bench.oracle_threads() == 5
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.oracle_threads() == len(os.sched_getaffinity(0))
+
+
+def test_sampled_parity_on_host_tensors():
+    """The device-gather parity check, run on CPU tensors: it passes the
+    oracle's own output and catches a single planted misplacement."""
+    import numpy as np
+    import torch
+    n = 16
+    for elem in (4, 16):
+        A, c = wl.random_bmmc(n, 3 + elem, lambda r: oracle.rank(r) == n)
+        x = wl.fill_random_bytes(n, elem, 5)
+        want = oracle.apply(A, c, x)
+        out = torch.from_numpy(want.reshape(-1).copy())
+        bad, checked = bench.sampled_parity(torch, A, c, x, out, samples=1 << 12)
+        assert bad == 0 and checked == (1 << 12) + 2
+        # swap two output elements the sample covers (the last index is always sampled)
+        j = int(oracle.map_indices(A, c, np.array([(1 << n) - 1], dtype=np.uint64))[0])
+        k = int(oracle.map_indices(A, c, np.array([0], dtype=np.uint64))[0])
+        w2 = want.copy()
+        w2[[j, k]] = w2[[k, j]]
+        bad, _ = bench.sampled_parity(torch, A, c, x, torch.from_numpy(w2.reshape(-1).copy()),
+                                      samples=1 << 12)
+        assert bad >= 2

@@ -69,3 +69,32 @@ def test_parm_matches_definition(n, mask):
     got = bm.parm(torch.from_numpy(y).to("cuda:0"), mask, lambda t: t.flip(0))
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), _parm_reference(y, mask, lambda a: a[::-1]))
+
+
+@pytest.mark.parametrize("as_handle", [False, True])
+def test_side_stream_is_ordered_with_current_stream(as_handle):
+    """parm and permute_dims on a side stream (a torch stream, or its raw
+    handle): the inputs are produced on the current stream right before the
+    call and the results consumed there right after, with no synchronisation
+    in between; they must match the same calls on the current stream."""
+    torch = _torch()
+    side = torch.cuda.Stream()
+    stream = int(side.cuda_stream) if as_handle else side
+    n, mask = 20, 0x8421
+    rng = np.random.Generator(np.random.PCG64(77))
+    host = torch.from_numpy(rng.integers(0, 1000, size=1 << n).astype(np.int64))
+    for rep in range(3):
+        d = host.to("cuda:0")
+        d.mul_(3).add_(rep)  # producer on the current stream
+        want = bm.parm(d, mask, lambda t: torch.cumsum(t, 0))
+        got = bm.parm(d, mask, lambda t: torch.cumsum(t, 0), stream=stream)
+        got2 = got * 1  # consumer on the current stream
+        x = torch.arange(1 << 18, dtype=torch.float32, device="cuda:0").reshape(8, 64, 512)
+        x.add_(rep)
+        pw = bm.permute_dims(x, [2, 0, 1], flip=[1])
+        pg = bm.permute_dims(x, [2, 0, 1], flip=[1], stream=stream)
+        pg2 = pg + 0
+        torch.cuda.synchronize()
+        assert torch.equal(got2, want), rep
+        assert torch.equal(pg2, pw), rep
+        assert torch.equal(pw.cpu(), x.cpu().flip([1]).permute(2, 0, 1).contiguous())
