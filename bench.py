@@ -53,7 +53,7 @@ def kernel_source_digest() -> str:
     """Digest of the device code: the kernels and what they include."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bmmc_affine_index_amd", "csrc")
-    for rel in sorted(["launch.h", "kernels/tiled.hip", "kernels/chunk.hip",
+    for rel in sorted(["launch.h", "kernels/tiled.hip", "kernels/tiled_cfg.h", "kernels/chunk.hip",
                        "kernels/copy.hip", "kernels/common.h"]):
         with open(os.path.join(csrc, rel), "rb") as f:
             h.update(f.read())

@@ -16,7 +16,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbmmc.so")
+# BMMC_LIB names another build of the same library (the host-sanitized one
+# the CPU tests load); by default the in-tree libbmmc.so.
+LIB_PATH = os.environ.get("BMMC_LIB") or os.path.join(_HERE, "libbmmc.so")
 
 # status codes (include/bmmc.h)
 OK = 0
@@ -50,6 +52,7 @@ EXPORTED = (
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
     "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_plan_get_options", "bmmc_parm_matrix",
     "bmmc_matrix_inverse", "bmmc_tensor_permute_matrix",
+    "bmmc_testing_fail_scratch_allocs",
 )
 
 
@@ -156,6 +159,8 @@ def lib():
     L.bmmc_tensor_permute_matrix.argtypes = [ctypes.c_int, intp, intp, ctypes.c_uint64, u64p,
                                              u64p, intp]
     L.bmmc_tensor_permute_matrix.restype = ctypes.c_int
+    L.bmmc_testing_fail_scratch_allocs.argtypes = [ctypes.c_int]
+    L.bmmc_testing_fail_scratch_allocs.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -242,6 +247,12 @@ def bmmc_plan_tune_pairs(plan: int, pairs, stream=None, reps: int = 0) -> int:
 
 def bmmc_copy(inp, out, nbytes: int, stream=None) -> int:
     return lib().bmmc_copy(_ptr(inp), _ptr(out), int(nbytes), _stream(stream))
+
+
+def bmmc_testing_fail_scratch_allocs(count: int) -> int:
+    """Fault injection (include/bmmc_testing.h): the next `count` scratch
+    allocations of two-pass plans fail with ERR_OUT_OF_MEMORY."""
+    return lib().bmmc_testing_fail_scratch_allocs(int(count))
 
 
 def bmmc_plan_destroy(plan: int) -> None:

@@ -2,18 +2,23 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <memory>
 #include <new>
 #include <vector>
 
 #include "../../include/bmmc.h"
+#include "../../include/bmmc_testing.h"
 #include "launch.h"
 #include "plan.h"
 
 namespace {
 
 thread_local int g_last_error = BMMC_OK;
+
+// Scratch allocations still to fail on purpose (bmmc_testing_fail_scratch_allocs).
+std::atomic<int> g_fail_scratch_allocs{0};
 
 int run_pass(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
     switch (d.kernel) {
@@ -61,6 +66,14 @@ bool supported(const bmmc_plan &p) {
 // device, allocated on first use and kept until the plan is destroyed.
 int plan_scratch(const bmmc_plan *p, void **out) {
     std::lock_guard<std::mutex> lock(p->scratch_mu);
+    // an injected failure comes before any HIP call, as an allocation that
+    // the device refused would
+    if (!p->scratch) {
+        int k = g_fail_scratch_allocs.load();
+        while (k > 0 && !g_fail_scratch_allocs.compare_exchange_weak(k, k - 1)) {
+        }
+        if (k > 0) return BMMC_ERR_OUT_OF_MEMORY;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return BMMC_ERR_HIP;
     if (p->scratch && p->scratch_device != dev) {
@@ -148,6 +161,20 @@ int bmmc_execute(const bmmc_plan *p, const void *in, void *out, void *stream) {
     if (overlaps(in, scratch, bytes_of(p)) || overlaps(out, scratch, bytes_of(p)))
         return BMMC_ERR_ALIAS;
     return run_passes(p->pass, p->npasses, in, out, scratch, s);
+}
+
+int bmmc_execute_noalloc(const bmmc_plan *p, const void *in, void *out, void *stream) {
+    // every argument check comes before the first HIP call
+    const int arg = check_buffers(p, in, out);
+    if (arg != BMMC_OK) return arg;
+    void *buf = nullptr;
+    if (p->npasses > 1) {
+        // the array between the passes must fit the fixed buffer
+        if (bytes_of(p) > (size_t)BMMC_NOALLOC_SCRATCH_BYTES) return BMMC_ERR_SCRATCH_LIMIT;
+        const int st = bmmc::noalloc_scratch(&buf);
+        if (st != BMMC_OK) return st;
+    }
+    return bmmc::execute_with_scratch(p, in, out, buf, static_cast<hipStream_t>(stream));
 }
 
 int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs, int npairs,
@@ -308,6 +335,12 @@ void bmmc_plan_destroy(bmmc_plan *p) {
 }
 
 int bmmc_last_error(void) { return g_last_error; }
+
+int bmmc_testing_fail_scratch_allocs(int count) {
+    if (count < 0) return BMMC_ERR_INVALID_ARG;
+    g_fail_scratch_allocs.store(count);
+    return BMMC_OK;
+}
 
 const char *bmmc_status_string(int status) {
     switch (status) {

@@ -20,30 +20,9 @@
 //    plan so that the output-order reads hit distinct banks.
 #include "../launch.h"
 #include "common.h"
+#include "tiled_cfg.h"
 
 namespace bmmc {
-
-// log2 of the most threads one tile is moved by.  256: measured against 512
-// (within 4% either way) and 1024 (one-tile launches lose up to 55% to the
-// lower occupancy).
-constexpr int kTileMaxNTL = 8;
-
-template <int UL, int T, int IT> struct TiledCfg {
-    static constexpr int U = 1 << UL;
-    static constexpr int WL = (4 - UL) < T ? (4 - UL) : T;  // log2 units per chunk
-    static constexpr int W = 1 << WL;
-    static constexpr int CB = U << WL;                      // chunk bytes
-    static constexpr int CPSL = T - WL;                     // log2 chunks per row
-    static constexpr int CHL = 2 * T - WL;                  // log2 chunks per tile
-    static constexpr int NTL = CHL < kTileMaxNTL ? CHL : kTileMaxNTL;  // log2 threads
-    static constexpr int NT = 1 << NTL;
-    static constexpr int RPPL = NTL - CPSL;                 // log2 rows per pass
-    static constexpr int JL = CHL - NTL;                    // log2 passes per tile
-    static constexpr int J = 1 << JL;
-    static constexpr int TILE = U << (2 * T);               // bytes per tile
-    static constexpr int LDS = TILE << IT;
-    static_assert(RPPL >= 0 && JL >= 0, "tile geometry");
-};
 
 // Tile bases: the wave reduction when the workgroup is made of full waves,
 // the scalar loop otherwise.  A one-tile launch of a small array runs one
@@ -417,9 +396,6 @@ __global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
 
 namespace {
 
-constexpr int kMaxT[5] = {8, 7, 7, 6, 6};
-constexpr int kMaxIT = 3;
-
 struct TiledArgs {
     const bmmc_pass_desc *d;
     const uint8_t *in;
@@ -478,11 +454,6 @@ template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
     return a.d->cache_hint ? launch_nt<UL, T, IT, true>(a) : launch_nt<UL, T, IT, false>(a);
 }
 
-template <int UL, int T, int IT> constexpr bool valid_cfg() {
-    return UL <= 4 && T >= 1 && T <= kMaxT[UL] && IT <= kMaxIT &&
-           (TiledCfg<UL, T, IT>::LDS <= 65536);
-}
-
 // Walks the compiled (UL, T, IT) space; `launch` = false only answers
 // whether the configuration exists.
 template <int UL, int T, int IT>
@@ -500,19 +471,6 @@ int dispatch(int ul, int t, int it, const TiledArgs *a) {
 }
 
 }  // namespace
-
-bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
-    if ((launch == BMMC_LAUNCH_PERSISTENT || launch == BMMC_LAUNCH_STREAMED) &&
-        (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
-         (uint64_t(2) << (2 * t + unit_log2)) > 131072))
-        return false;
-    if (launch == BMMC_LAUNCH_STREAMED) {
-        // each role must be whole waves: 2t - (units per chunk, log2) >= 6
-        const int wl = (4 - unit_log2) < t ? (4 - unit_log2) : t;
-        if (2 * t - wl < 6) return false;
-    }
-    return dispatch<0, 1, 0>(unit_log2, t, iters_log2, nullptr) == BMMC_OK;
-}
 
 int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t s) {
     if (d.iters_log2 > d.blk_bits || d.grid_log2 > d.blk_bits || d.grid_log2 < 0)

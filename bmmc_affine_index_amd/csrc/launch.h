@@ -23,6 +23,10 @@ int check_execute_buffers(const bmmc_plan *p, const void *in, const void *out);
 int execute_with_scratch(const bmmc_plan *p, const void *in, void *out, void *scratch,
                          hipStream_t s);
 
+// The device address of the fixed scratch array of bmmc_execute_noalloc
+// (BMMC_NOALLOC_SCRATCH_BYTES) on the current device.  Defined in noalloc.hip.
+int noalloc_scratch(void **out);
+
 // Whether the tile kernel is compiled for this unit size, side, iteration
 // count and launch style.
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch);

@@ -1,6 +1,7 @@
-// noalloc.hip -- bmmc_execute_noalloc: bmmc_execute without any device
-// allocation, for callers that cannot allocate (code under stream capture,
-// tight serving loops, harnesses that forbid hipMalloc).
+// noalloc.hip -- the fixed scratch array of bmmc_execute_noalloc, the entry
+// point (in api.cpp) that allocates no device memory, for callers that cannot
+// allocate (code under stream capture, tight serving loops, harnesses that
+// forbid hipMalloc).
 //
 // Only a two-pass plan needs memory beyond its input and output: the array
 // between its two passes.  Here that array is the file-scope device array
@@ -15,7 +16,6 @@
 
 #include "../../include/bmmc.h"
 #include "launch.h"
-#include "plan.h"
 
 // The array between the two passes of every bmmc_execute_noalloc call on a
 // device (calls that overlap in time on one device race on it).
@@ -54,18 +54,8 @@ int device_scratch(void **out) {
 
 }  // namespace
 
-extern "C" int bmmc_execute_noalloc(const bmmc_plan *p, const void *in, void *out,
-                                    void *stream) {
-    // every argument check comes before the first HIP call
-    const int arg = bmmc::check_execute_buffers(p, in, out);
-    if (arg != BMMC_OK) return arg;
-    void *buf = nullptr;
-    if (p->npasses > 1) {
-        // the array between the passes must fit the fixed buffer
-        if (((size_t)p->elem_bytes << p->n) > (size_t)BMMC_NOALLOC_SCRATCH_BYTES)
-            return BMMC_ERR_SCRATCH_LIMIT;
-        const int st = device_scratch(&buf);
-        if (st != BMMC_OK) return st;
-    }
-    return bmmc::execute_with_scratch(p, in, out, buf, static_cast<hipStream_t>(stream));
-}
+namespace bmmc {
+
+int noalloc_scratch(void **out) { return device_scratch(out); }
+
+}  // namespace bmmc

@@ -1,0 +1,20 @@
+// tiled_config.cpp -- which tile-pass launches this build can run (host-only).
+#include "kernels/tiled_cfg.h"
+#include "launch.h"
+
+namespace bmmc {
+
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
+    if ((launch == BMMC_LAUNCH_PERSISTENT || launch == BMMC_LAUNCH_STREAMED) &&
+        (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
+         (uint64_t(2) << (2 * t + unit_log2)) > 131072))
+        return false;
+    if (launch == BMMC_LAUNCH_STREAMED) {
+        // each role must be whole waves: 2t - (units per chunk, log2) >= 6
+        const int wl = (4 - unit_log2) < t ? (4 - unit_log2) : t;
+        if (2 * t - wl < 6) return false;
+    }
+    return tiled_config_exists(unit_log2, t, iters_log2);
+}
+
+}  // namespace bmmc

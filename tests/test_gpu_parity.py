@@ -182,6 +182,29 @@ def test_two_pass_plan_reused_and_streams():
         assert np.array_equal(d_out.cpu().numpy().view(np.uint32), oracle.apply(A, c, x))
 
 
+def test_failed_scratch_allocation_then_recovery():
+    """A two-pass plan whose scratch allocation fails (injected from the host)
+    returns ERR_OUT_OF_MEMORY and writes nothing; the next call allocates and
+    matches the oracle."""
+    torch = _torch()
+    n = 18
+    A, c = _inv(n, 4343)
+    P = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    x = wl.fill_random_bytes(n, 4, seed=43).view(np.uint32).reshape(-1)
+    d_in = torch.from_numpy(x.view(np.int32).copy()).to("cuda:0")
+    d_out = torch.full_like(d_in, -1)
+    try:
+        assert bm.bmmc_testing_fail_scratch_allocs(1) == bm.OK
+        assert bm.bmmc_execute(P.handle, d_in, d_out) == bm.ERR_OUT_OF_MEMORY
+    finally:
+        bm.bmmc_testing_fail_scratch_allocs(0)
+    torch.cuda.synchronize()
+    assert bool((d_out == -1).all())
+    assert bm.bmmc_execute(P.handle, d_in, d_out) == bm.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(d_out.cpu().numpy().view(np.uint32), oracle.apply(A, c, x))
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(launch=bm.LAUNCH_ONE_TILE),
                                 dict(launch=bm.LAUNCH_PERSISTENT), dict(launch=bm.LAUNCH_STREAMED),
                                 dict(route=bm.ROUTE_TWO_PASS), dict(route=bm.ROUTE_NAIVE)],

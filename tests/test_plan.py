@@ -26,8 +26,10 @@ def _inv(n, seed):
 # --------------------------------------------------------------------------
 
 def test_library_exports_every_header_function():
-    header = open(os.path.join(ROOT, "include", "bmmc.h")).read()
-    names = set(re.findall(r"^\S[^;()]*?\b(bmmc_\w+)\s*\(", header, flags=re.M))
+    names = set()
+    for h in ("bmmc.h", "bmmc_testing.h"):
+        header = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"^\S[^;()]*?\b(bmmc_\w+)\s*\(", header, flags=re.M))
     assert names == set(bm.EXPORTED)
     L = bm.lib()
     for name in names:
@@ -127,6 +129,31 @@ def test_execute_noalloc_refuses_without_gpu():
     header = open(os.path.join(ROOT, "include", "bmmc.h")).read()
     assert re.search(r"#define BMMC_NOALLOC_SCRATCH_BYTES \(\(size_t\)1 << 26\)", header)
     assert bm.NOALLOC_SCRATCH_BYTES == 1 << 26
+
+
+def test_injected_scratch_failure_without_gpu():
+    """A two-pass plan whose scratch allocation fails returns
+    ERR_OUT_OF_MEMORY from bmmc_execute and bmmc_plan_tune_pairs, before any
+    HIP call (these fake addresses are never touched), and keeps no scratch;
+    each injected failure is used once."""
+    n = 16
+    A, c = _inv(n, 16)
+    p = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS)
+    assert p.info.passes == 2
+    i, o = 1 << 40, (1 << 40) + (1 << 30)
+    try:
+        assert bm.bmmc_testing_fail_scratch_allocs(-1) == bm.ERR_INVALID_ARG
+        assert bm.bmmc_testing_fail_scratch_allocs(3) == bm.OK
+        assert bm.bmmc_execute(p.handle, i, o, None) == bm.ERR_OUT_OF_MEMORY
+        assert bm.bmmc_execute(p.handle, i, o, None) == bm.ERR_OUT_OF_MEMORY
+        opts = p.options()
+        assert bm.bmmc_plan_tune_pairs(p.handle, [(i, o)], None, 3) == bm.ERR_OUT_OF_MEMORY
+        assert p.options() == opts  # a failed tuning leaves the plan as it was
+        # one-pass plans and the entry point that allocates nothing never ask
+        q = bm.Plan(n, wl.bit_reverse_matrix(n), 0, 4)
+        assert q.info.passes == 1 and q.info.scratch_bytes == 0
+    finally:
+        assert bm.bmmc_testing_fail_scratch_allocs(0) == bm.OK
 
 
 def test_tune_argument_errors_without_gpu():
