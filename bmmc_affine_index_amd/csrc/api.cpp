@@ -212,32 +212,40 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     // structured orders crowd them (random 16-byte BPCs: up to +6%)
     else maps = {bmmc::kDefaultBlockMap, 1, 3, 6, 8, 9};
     tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
+    // streamed launches: the planner's one tile of loads in flight per loader
+    // wave, and two (candidates that are not streamed come out the same for
+    // both and are dropped as duplicates)
+    std::vector<int> depths;
+    if (p->opt.depth) depths = {p->opt.depth};
+    else depths = {0, 2};
     std::vector<std::unique_ptr<bmmc_plan>> cand;
     for (size_t ti = 0; ti < tiles.size(); ++ti)
         for (int l : launches)
-            for (int m : maps) {
-                bmmc_plan_options o = p->opt;
-                o.tile_log2 = tiles[ti];
-                o.launch = l;
-                o.block_map = m;
-                std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
-                if (!q) return BMMC_ERR_OUT_OF_MEMORY;
-                if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) !=
-                        BMMC_OK ||
-                    !supported(*q))
-                    continue;
-                // the next larger side (rows twice as long), once the
-                // planner's side is known; the planner clamps it to what
-                // the LDS and the index bits allow (duplicates drop out)
-                if (!p->opt.tile_log2 && tiles.size() == 1 && q->info.tile_log2 > 0 &&
-                    q->info.tile_log2 < BMMC_MAX_TILE)
-                    tiles.push_back(q->info.tile_log2 + 1);
-                bool dup = false;  // same tables as an earlier candidate
-                for (const auto &r : cand)
-                    dup |= r->npasses == q->npasses &&
-                           std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
-                if (!dup) cand.push_back(std::move(q));
-            }
+            for (int m : maps)
+                for (int dp : depths) {
+                    bmmc_plan_options o = p->opt;
+                    o.tile_log2 = tiles[ti];
+                    o.launch = l;
+                    o.block_map = m;
+                    o.depth = dp;
+                    std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
+                    if (!q) return BMMC_ERR_OUT_OF_MEMORY;
+                    if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) !=
+                            BMMC_OK ||
+                        !supported(*q))
+                        continue;
+                    // the next larger side (rows twice as long), once the
+                    // planner's side is known; the planner clamps it to what
+                    // the LDS and the index bits allow (duplicates drop out)
+                    if (!p->opt.tile_log2 && tiles.size() == 1 && q->info.tile_log2 > 0 &&
+                        q->info.tile_log2 < BMMC_MAX_TILE)
+                        tiles.push_back(q->info.tile_log2 + 1);
+                    bool dup = false;  // same tables as an earlier candidate
+                    for (const auto &r : cand)
+                        dup |= r->npasses == q->npasses &&
+                               std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
+                    if (!dup) cand.push_back(std::move(q));
+                }
     if (cand.empty()) return BMMC_ERR_UNSUPPORTED;
 
     void *scratch = nullptr;

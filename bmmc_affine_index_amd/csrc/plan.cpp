@@ -699,7 +699,11 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     // Planner's choice: non-temporal loads and stores (measured on the four
     // large workloads: +1% to +5% over no hint; loads alone lose).
     lc.cache_hint = o.cache_hint == 1 ? 0 : 3;
-    lc.depth = o.depth ? o.depth : 2;
+    // Planner's choice: one tile of loads in flight per loader wave.  Two
+    // use every VGPR and spill 32 bytes per thread in the loop (4-byte units,
+    // t = 7); tuning tries them, and keeps them only when they win by more
+    // than its margin.
+    lc.depth = o.depth ? o.depth : 1;
     lc.block_map = o.block_map ? o.block_map : kDefaultBlockMap;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;

@@ -81,7 +81,7 @@ typedef struct bmmc_plan_options {
     int grid_log2;  /* persistent launch: log2 of workgroups; 0 = planner's choice */
     int walk;       /* persistent launch: BMMC_WALK_* order of tiles; 0 = planner's choice */
     int depth;      /* streamed launch: tiles of loads in flight per loader wave (1 or 2);
-                       0 = planner's choice */
+                       0 = planner's choice (1) */
     int cache_hint; /* tile pass: 0 = planner's choice (non-temporal loads and stores),
                        1 = none, 2 = non-temporal loads and stores */
     int block_map;  /* re-indexing of the tiles: 0 = planner's choice (5), 1 = identity,
@@ -234,8 +234,9 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * running time varied with the permutation).  Every candidate computes the
  * same permutation; they differ in the tile side (the planner's and the next
  * larger), the launch style (the planner's persistent or streamed walk, or
- * one workgroup per tile) and the block order (bmmc_plan_options.block_map 5,
- * the planner's, 1, 3 and 6, and the random orders 8 and 9): up to 24
+ * one workgroup per tile), the loads in flight of a streamed walk (one or two
+ * tiles per loader wave) and the block order (bmmc_plan_options.block_map 5,
+ * the planner's, 1, 3 and 6, and the random orders 8 and 9): up to 48
  * candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
