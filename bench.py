@@ -454,8 +454,8 @@ class Runner:
 def plan_brief(plan):
     d = plan.describe()
     return {"route": d["route"], "passes": d["passes"], "kernels": d["kernels"],
-            "tile_log2": d["tile_log2"], "block_map": d["block_map"],
-            "unit_bytes": d["unit_bytes"]}
+            "tile_log2": d["tile_log2"], "tile_skew": d["tile_skew"],
+            "block_map": d["block_map"], "unit_bytes": d["unit_bytes"]}
 
 
 def measure_case(run, name, route, x=None, bufs=None, A=None, c=None):
@@ -513,7 +513,8 @@ def measure_c5(run):
         okays += ok
         vals.append(r["gbs"])
         d = plan.describe()
-        plans.append("%s t=%s order %s" % (d["kernels"][-1], d["tile_log2"], d["block_map"]))
+        plans.append("%s t=%s skew %s order %s" % (d["kernels"][-1], d["tile_log2"],
+                                                   d["tile_skew"], d["block_map"]))
         log("c5 perm %d: %.1f GB/s (%.3f of copy) %s, %s" % (k, r["gbs"], r["gbs"] / cp["gbs"],
                                                           plans[-1], parity))
     order = sorted(range(len(vals)), key=lambda i: vals[i])
@@ -699,8 +700,9 @@ def main():
             okays += okk
             vals.append(rk["gbs"])
             dk = pk.describe()
-            log("perm %d: %.1f GB/s (%s t=%s order %s) %s" % (
-                k, vals[-1], dk["kernels"][-1], dk["tile_log2"], dk["block_map"], park))
+            log("perm %d: %.1f GB/s (%s t=%s skew %s order %s) %s" % (
+                k, vals[-1], dk["kernels"][-1], dk["tile_log2"], dk["tile_skew"],
+                dk["block_map"], park))
         sv = sorted(vals)
         pmed = 0.5 * (sv[(len(sv) - 1) // 2] + sv[len(sv) // 2])
         perm_stats = {"perms": len(vals), "min_gbs": round(sv[0], 2),

@@ -93,33 +93,35 @@ int n_over_of(const Mat &A, int t) {
     return t - rank(sub);
 }
 
-// The tile test.  With B = A^{-1}, column j < t of B is the input index that
-// lands on output index e_j.  A tile made of the 2^t input segments spanned
-// by the low t bits and a set H of t higher bits covers whole output segments
-// iff every such column lies in span(low t bits, H), i.e. iff the rows r >= t
-// that column j < t uses lie in H.  Returns that row set S; A is tiled at t
-// iff |S| <= t (then any H containing S works).
-u64 tile_rows(const Mat &B, int t) {
+// The tile test.  With B = A^{-1}, column j < b of B is the input index that
+// lands on output index e_j.  A tile made of the input rows of 2^a units
+// spanned by the low a bits and a set H of b higher bits covers whole output
+// rows of 2^b units iff every such column lies in span(low a bits, H), i.e.
+// iff the rows r >= a that column j < b uses lie in H.  Returns that row set
+// S; A is tiled for (a, b) iff |S| <= b (then any H containing S works).
+// Square tiles have a = b = t.
+u64 tile_rows(const Mat &B, int a, int b) {
     u64 S = 0;
-    for (int r = t; r < B.rows; ++r)
-        if (B.r[r] & low_mask(t)) S |= u64(1) << r;
+    for (int r = a; r < B.rows; ++r)
+        if (B.r[r] & low_mask(b)) S |= u64(1) << r;
     return S;
 }
 
-// Pad the required row set S to t rows.  With `near_out`, prefer input bits
-// whose image is a single output bit in [t, 2t) (keeps a BPC tile's output
-// segments close together); then take the lowest free bits.
-u64 pad_rows(const Mat &A, u64 S, int t, bool near_out) {
+// Pad the required row set S to b rows above the a in-row bits.  With
+// `near_out`, prefer input bits whose image is a single output bit in
+// [b, b + a), the output row bits next to the rows (keeps a BPC tile's
+// output rows close together); then take the lowest free bits.
+u64 pad_rows(const Mat &A, u64 S, int a, int b, bool near_out) {
     u64 H = S;
-    for (int pass = near_out ? 0 : 1; pass < 2 && popcount(H) < t; ++pass) {
-        for (int j = t; j < A.rows && popcount(H) < t; ++j) {
+    for (int pass = near_out ? 0 : 1; pass < 2 && popcount(H) < b; ++pass) {
+        for (int j = a; j < A.rows && popcount(H) < b; ++j) {
             if ((H >> j) & 1u) continue;
             if (pass == 0) {
                 u64 col = A.col(j);
                 bool single = col && !(col & (col - 1));
                 if (!single) continue;
                 int o = __builtin_ctzll(col);
-                if (o < t || o >= 2 * t) continue;
+                if (o < b || o >= a + b) continue;
             }
             H |= u64(1) << j;
         }
@@ -234,10 +236,7 @@ int default_tile_log2(int ulog2) {
     return t[ulog2];
 }
 
-// Build the tile pass for unit map (A, c) with tile rows W (t vectors in the
-// high coordinates, independent).  The tile of block b is the coset
-// K.b XOR span(low t bits) XOR span(W); because W contains the high parts of
-// B's first t columns, the tile's image is 2^t whole output segments.
+// How the tile pass is launched (planner's defaults and caller's options).
 struct LaunchChoice {
     int iters_log2;  // one-tile launch: tiles staged together
     int persistent;  // BMMC_LAUNCH_PERSISTENT or _STREAMED; 0: one-tile launch
@@ -349,48 +348,60 @@ std::vector<u64> block_basis(const Mat &A, const Mat &B, int t, const Basis &vb,
     return X;
 }
 
-int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W,
+// Build the tile pass for unit map (A, c) with input rows of 2^a units (the
+// low a bits) and b row vectors W (high coordinates, independent).  The tile
+// of block x is the coset x XOR span(low a bits) XOR span(W); because W
+// contains the high parts of B's first b columns, the tile's image is 2^a
+// whole output rows of 2^b units.  Square tiles have a = b = t; rectangular
+// ones keep 2^(a + b) = 2^(2t) units, the kernel's tile.
+int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<u64> &W,
                 const LaunchChoice &lc, bool swizzle, bmmc_pass_desc *d) {
     int iters_log2 = lc.iters_log2;
     const int nb = A.rows;
-    if ((int)W.size() != t || 2 * t > nb) return BMMC_ERR_INVALID_ARG;
-    const u64 lo_t = low_mask(t);
+    const int K = a + b;  // log2 units per tile
+    if (a < 1 || b < 1 || (K & 1) || (int)W.size() != b || K > nb) return BMMC_ERR_INVALID_ARG;
+    const int t = K / 2;  // the kernel's tile side: 2^(2t) units per tile
+    const u64 lo_a = low_mask(a), lo_b = low_mask(b);
     Basis wb;
     for (u64 w : W) {
-        if (w & lo_t) return BMMC_ERR_INVALID_ARG;
+        if (w & lo_a) return BMMC_ERR_INVALID_ARG;
         if (!wb.add(w)) return BMMC_ERR_INVALID_ARG;
     }
     // Block bits: high coordinates that are no pivot of W; together with W
     // they form a basis of the high coordinates.
     std::vector<int> R;
     const u64 piv = wb.pivot_mask();
-    for (int r = t; r < nb; ++r)
+    for (int r = a; r < nb; ++r)
         if (!((piv >> r) & 1u)) R.push_back(r);
-    if ((int)R.size() != nb - 2 * t) return BMMC_ERR_INVALID_ARG;
+    if ((int)R.size() != nb - K) return BMMC_ERR_INVALID_ARG;
     const int blk_bits = (int)R.size();
     if (iters_log2 > blk_bits) iters_log2 = blk_bits;
 
-    // Output segments of the tile: a basis G of the high parts of A's image
-    // of the tile's local space.
+    // Output rows of the tile: a basis G of the high parts (above the b
+    // in-row output bits) of A's image of the tile's local space.
     Basis gb;
-    for (int j = 0; j < t; ++j) gb.add(A.apply(u64(1) << j) & ~lo_t);
-    for (int k = 0; k < t; ++k) gb.add(A.apply(W[k]) & ~lo_t);
-    if (gb.size() != t) return BMMC_ERR_INVALID_ARG;
+    for (int j = 0; j < a; ++j) gb.add(A.apply(u64(1) << j) & ~lo_b);
+    for (int k = 0; k < b; ++k) gb.add(A.apply(W[k]) & ~lo_b);
+    if (gb.size() != a) return BMMC_ERR_INVALID_ARG;
 
-    // M: local input coordinates (lo bits 0..t-1, row bits t..2t-1) ->
-    // local output coordinates (position in segment, segment index g).
-    Mat M = Mat::zeros(2 * t, 2 * t);
-    for (int j = 0; j < 2 * t; ++j) {
-        u64 v = j < t ? A.apply(u64(1) << j) : A.apply(W[j - t]);
-        u64 hi = v & ~lo_t;
+    // M: local input coordinates (in-row bits 0..a-1, row bits a..K-1) ->
+    // local output coordinates (position in the output row 0..b-1, output
+    // row index b..K-1).
+    Mat M = Mat::zeros(K, K);
+    for (int j = 0; j < K; ++j) {
+        u64 v = j < a ? A.apply(u64(1) << j) : A.apply(W[j - a]);
+        u64 hi = v & ~lo_b;
         if (gb.reduce(hi) != 0) return BMMC_ERR_INVALID_ARG;
-        M.set_col(j, (v & lo_t) | (gb.coords(hi) << t));
+        M.set_col(j, (v & lo_b) | (gb.coords(hi) << b));
     }
     Mat Minv;
     if (!inverse(M, Minv)) return BMMC_ERR_INVALID_ARG;
 
     const TileGeom g = tile_geom(ulog2, t);
-    const int cbits = 2 * t - g.wl;  // chunk-index bits of a tile: thread bits, then pass bits
+    // both rows must hold whole vector chunks of the kernel's width
+    if (a < g.wl || b < g.wl) return BMMC_ERR_INVALID_ARG;
+    const int cpsl_in = a - g.wl, cpsl_out = b - g.wl;  // log2 chunks per row, each side
+    const int cbits = K - g.wl;  // chunk-index bits of a tile: thread bits, then pass bits
     const int lane_bits = std::min(6, g.ntl);
     const int lanes = 1 << lane_bits;
 
@@ -400,23 +411,24 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     // chunk's place in its output segment, then the segment bits; which
     // coordinate each thread bit takes (`rpos`) is chosen below.
     auto load_local = [&](int p) -> u64 {  // local input vector of load position p
-        return p < g.cpsl ? (u64(1) << (g.wl + p)) : (u64(1) << (t + p - g.cpsl));
+        return p < cpsl_in ? (u64(1) << (g.wl + p)) : (u64(1) << (a + p - cpsl_in));
     };
     auto drain_local = [&](int k) -> u64 {  // local output vector of drain coordinate k
-        return k < g.cpsl ? (u64(1) << (g.wl + k)) : (u64(1) << (t + k - g.cpsl));
+        return k < cpsl_out ? (u64(1) << (g.wl + k)) : (u64(1) << (b + k - cpsl_out));
     };
 
-    // LDS layout: the slot of local (lo, h) is (h << t) | (P.lo XOR S.h),
-    // with P an invertible map of the chunk index inside a row and S an XOR
-    // swizzle by row; both leave the units of a chunk together, so a chunk
-    // is written with one vector access.  Sx = S's t columns, then P's.
+    // LDS layout: the slot of local (lo, h) is (h << a) | (P.lo XOR S.h),
+    // with P an invertible map of the chunk index inside an input row and S
+    // an XOR swizzle by row; both leave the units of a chunk together, so a
+    // chunk is written with one vector access.  Sx = S's b columns, then P's
+    // a columns.
     auto slot = [&](u64 u, const std::vector<u64> &Sx) -> u64 {
-        u64 lo = u & lo_t, h = u >> t, s = 0;
-        for (int k = 0; k < t; ++k) {
+        u64 lo = u & lo_a, h = u >> a, s = 0;
+        for (int k = 0; k < b; ++k)
             if ((h >> k) & 1u) s ^= Sx[k];
-            if ((lo >> k) & 1u) s ^= Sx[t + k];
-        }
-        return (h << t) | s;
+        for (int k = 0; k < a; ++k)
+            if ((lo >> k) & 1u) s ^= Sx[b + k];
+        return (h << a) | s;
     };
 
     // Bank model.  Measured on gfx950 with the LDS bank-conflict counter:
@@ -453,30 +465,31 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     // chunk bits of the output segment so that 8 lanes store one contiguous
     // 128-byte piece; the remaining lane bits of the wave are searched.
     int cb_log2 = ulog2 + g.wl;
-    const int pc = std::min(g.cpsl, std::max(0, 7 - cb_log2));
+    const int pc = std::min(cpsl_out, std::max(0, 7 - cb_log2));
     std::vector<int> rpos(cbits);
     for (int k = 0; k < cbits; ++k) rpos[k] = k;
-    std::vector<u64> S(2 * t, 0);
-    for (int k = 0; k < t; ++k) S[t + k] = u64(1) << k;  // P = identity, S = 0
+    std::vector<u64> S(K, 0);
+    for (int k = 0; k < a; ++k) S[b + k] = u64(1) << k;  // P = identity, S = 0
     auto read_vecs = [&](const std::vector<int> &rp) {
         std::vector<u64> rv(cbits);
         for (int p = 0; p < cbits; ++p) rv[p] = Minv.apply(drain_local(rp[p]));
         return rv;
     };
-    if (swizzle && t > g.wl) {
-        const u64 colmask = lo_t & ~low_mask(g.wl);
-        u64 seed = 0x5EEDull ^ ((u64)t << 8) ^ (u64)ulog2;
-        for (int k = 0; k < 2 * t; ++k) seed = seed * 31 + Minv.r[k];
+    if (swizzle && a > g.wl) {
+        const u64 colmask = lo_a & ~low_mask(g.wl);
+        // the square tiles keep the seed they were tuned and measured with
+        u64 seed = 0x5EEDull ^ ((u64)t << 8) ^ (u64)ulog2 ^ ((u64)(b - a) << 16);
+        for (int k = 0; k < K; ++k) seed = seed * 31 + Minv.r[k];
         int best_cost = 1 << 30;
         std::vector<int> best_rpos = rpos;
-        std::vector<u64> best_S = S, cand(2 * t);
+        std::vector<u64> best_S = S, cand(K);
         auto random_p = [&](std::vector<u64> &Sx) {
             for (;;) {
-                Mat Pm = Mat::zeros(t, t);
-                for (int k = 0; k < t; ++k)
+                Mat Pm = Mat::zeros(a, a);
+                for (int k = 0; k < a; ++k)
                     Pm.set_col(k, k < g.wl ? (u64(1) << k) : (splitmix(seed) & colmask));
-                if (rank(Pm) == t) {
-                    for (int k = 0; k < t; ++k) Sx[t + k] = Pm.col(k);
+                if (rank(Pm) == a) {
+                    for (int k = 0; k < a; ++k) Sx[b + k] = Pm.col(k);
                     return;
                 }
             }
@@ -516,14 +529,15 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
                         int cc = cost(rv, Sx);
                         if (cc < best_cost) { best_cost = cc; best_rpos = rp; best_S = Sx; }
                     };
-                    for (int k = 0; k < t; ++k) { cand[k] = 0; cand[t + k] = u64(1) << k; }
+                    for (int k = 0; k < b; ++k) cand[k] = 0;
+                    for (int k = 0; k < a; ++k) cand[b + k] = u64(1) << k;
                     consider(cand);
-                    for (int k = 0; k < t; ++k) cand[k] = (u64(1) << k) & colmask;
+                    for (int k = 0; k < b; ++k) cand[k] = (u64(1) << k) & colmask;
                     consider(cand);
                     for (int tries = 0; tries < 48 && best_cost > ideal && budget > 0; ++tries) {
-                        for (int k = 0; k < t; ++k) cand[k] = splitmix(seed) & colmask;
+                        for (int k = 0; k < b; ++k) cand[k] = splitmix(seed) & colmask;
                         if (tries & 1) random_p(cand);
-                        else for (int k = 0; k < t; ++k) cand[t + k] = u64(1) << k;
+                        else for (int k = 0; k < a; ++k) cand[b + k] = u64(1) << k;
                         consider(cand);
                     }
                 }
@@ -547,7 +561,9 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
     d->t = t;
     d->chunk_log2 = g.wl;
     d->blk_bits = blk_bits;
-    const u64 tile_bytes = u64(1) << (2 * t + ulog2);
+    d->in_row_log2 = a;
+    d->out_row_log2 = b;
+    const u64 tile_bytes = u64(1) << (K + ulog2);
     int launch = lc.persistent;
     // Planner's choice, measured untuned with the default tile order: below
     // 2^14 tiles the streamed launch with loads two tiles ahead (the 64 MiB
@@ -577,47 +593,44 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int t, const std::vector<u64> &W
         d->lds_bytes = (uint32_t)(tile_bytes << iters_log2);
     }
     Basis vb, avb;  // the tile's span on the input side and on the output side
-    for (int j = 0; j < t; ++j) {
-        vb.add(u64(1) << j);
-        avb.add(u64(1) << j);
-    }
-    for (int k = 0; k < t; ++k) {
-        vb.add(W[k]);
-        avb.add(gb.vec[k]);
-    }
+    for (int j = 0; j < a; ++j) vb.add(u64(1) << j);
+    for (int j = 0; j < b; ++j) avb.add(u64(1) << j);
+    for (int k = 0; k < b; ++k) vb.add(W[k]);
+    for (int k = 0; k < a; ++k) avb.add(gb.vec[k]);
     Mat Binv;
     if (!inverse(A, Binv)) return BMMC_ERR_SINGULAR;
     const bool range_walk = d->launch != BMMC_LAUNCH_ONE_TILE && d->walk == BMMC_WALK_RANGES;
     const std::vector<u64> X =
-        block_basis(A, Binv, t, vb, avb, R, lc.block_map, range_walk ? d->grid_log2 : 0);
+        block_basis(A, Binv, std::min(a, b), vb, avb, R, lc.block_map,
+                    range_walk ? d->grid_log2 : 0);
     for (int k = 0; k < blk_bits; ++k) {
         const u64 x = X[k];
         const u64 z = A.apply(x);
         d->in_blk[k] = x << ulog2;
-        d->out_blk[k] = (z & ~lo_t) << ulog2;
-        d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_t), S) << ulog2);
+        d->out_blk[k] = (z & ~lo_b) << ulog2;
+        d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_b), S) << ulog2);
     }
     for (int p = 0; p < cbits; ++p) {
         const u64 lv = load_local(p);
-        const u64 in_local = (lv & lo_t) | [&] {
-            u64 h = lv >> t, off = 0;
-            for (int k = 0; k < t; ++k)
+        const u64 in_local = (lv & lo_a) | [&] {
+            u64 h = lv >> a, off = 0;
+            for (int k = 0; k < b; ++k)
                 if ((h >> k) & 1u) off ^= W[k];
             return off;
         }();
         d->ld_in[p] = in_local << ulog2;
         d->ld_lds[p] = (uint32_t)(slot(lv, S) << ulog2);
         const u64 ov = drain_local(rpos[p]);
-        u64 out_local = ov & lo_t;
-        for (int k = 0; k < t; ++k)
-            if (((ov >> t) >> k) & 1u) out_local ^= gb.vec[k];
+        u64 out_local = ov & lo_b;
+        for (int k = 0; k < a; ++k)
+            if (((ov >> b) >> k) & 1u) out_local ^= gb.vec[k];
         d->st_out[p] = out_local << ulog2;
         d->st_lds[p] = (uint32_t)(slot(rvec[p], S) << ulog2);
     }
-    for (int b = 0; b < g.wl; ++b)
-        d->st_unit[b] = (uint32_t)(slot(Minv.apply(u64(1) << b), S) << ulog2);
-    d->out_c = (c & ~lo_t) << ulog2;
-    d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_t), S) << ulog2);
+    for (int u = 0; u < g.wl; ++u)
+        d->st_unit[u] = (uint32_t)(slot(Minv.apply(u64(1) << u), S) << ulog2);
+    d->out_c = (c & ~lo_b) << ulog2;
+    d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_b), S) << ulog2);
     d->cache_hint = lc.cache_hint;
     d->block_map = lc.block_map;
     remap_blocks(d, lc.block_map);
@@ -685,6 +698,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         return BMMC_ERR_INVALID_ARG;
     if (o.launch >= BMMC_LAUNCH_PERSISTENT && o.iters_log2 > 0) return BMMC_ERR_INVALID_ARG;
     if (o.walk < BMMC_WALK_AUTO || o.walk > BMMC_WALK_INTERLEAVED) return BMMC_ERR_INVALID_ARG;
+    if (o.tile_skew < -BMMC_MAX_TILE || o.tile_skew > BMMC_MAX_TILE) return BMMC_ERR_INVALID_ARG;
     LaunchChoice lc;
     lc.iters_log2 = o.iters_log2;
     lc.auto_launch = o.launch == BMMC_LAUNCH_AUTO;
@@ -740,7 +754,7 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     const bool ident = m.nb == 0 || m.A.is_identity();
     Mat B;
     if (m.nb > 0) inverse(m.A, B);
-    const u64 S = (m.nb > 0 && t > 0) ? tile_rows(B, t) : 0;
+    const u64 S = (m.nb > 0 && t > 0) ? tile_rows(B, t, t) : 0;
     if (ident) info.kind = BMMC_KIND_IDENTITY;
     else if (is_permutation_matrix(m.A)) info.kind = BMMC_KIND_BPC;
     else if (t > 0 && popcount(S) <= t) info.kind = BMMC_KIND_TILED;
@@ -778,18 +792,23 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         return BMMC_OK;
     }
     const bool swz = !o.no_swizzle;
-    if (info.kind != BMMC_KIND_GENERAL) {
-        u64 H = pad_rows(m.A, S, t, true);
+    // single-pass tile shape: input rows of 2^a units, output rows of 2^b
+    const int a = t - o.tile_skew, b = t + o.tile_skew;
+    if (a < 1 || b < 1) return BMMC_ERR_INVALID_ARG;
+    const u64 Sab = o.tile_skew ? tile_rows(B, a, b) : S;
+    if (info.kind != BMMC_KIND_GENERAL && popcount(Sab) <= b) {
+        u64 H = pad_rows(m.A, Sab, a, b, true);
         std::vector<u64> W;
-        for (int r = t; r < m.nb; ++r)
+        for (int r = a; r < m.nb; ++r)
             if ((H >> r) & 1u) W.push_back(u64(1) << r);
-        int st = build_tiled(m.A, m.c, m.ulog2, t, W, lc, swz, &p->pass[0]);
+        int st = build_tiled(m.A, m.c, m.ulog2, a, b, W, lc, swz, &p->pass[0]);
         if (st != BMMC_OK) return st;
         info.tile_log2 = t;
         single(BMMC_ROUTE_FUSED);
         return BMMC_OK;
     }
     if (o.route == BMMC_ROUTE_TWO_PASS) {
+        if (o.tile_skew) return BMMC_ERR_INVALID_ARG;  // square tiles only
         Mat T1, T2;
         if (!factorize(m.A, t, T1, T2)) return BMMC_ERR_INVALID_ARG;
         // pass 0: T2 relabels segments (complement 0)
@@ -798,12 +817,12 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         // pass 1: T1 is tiled with rows inside {t, ..., 2t-1}
         Mat T1inv;
         inverse(T1, T1inv);
-        u64 H = pad_rows(T1, tile_rows(T1inv, t), t, false);
+        u64 H = pad_rows(T1, tile_rows(T1inv, t, t), t, t, false);
         if (popcount(H) != t) return BMMC_ERR_INVALID_ARG;
         std::vector<u64> W;
         for (int r = t; r < m.nb; ++r)
             if ((H >> r) & 1u) W.push_back(u64(1) << r);
-        int st = build_tiled(T1, m.c, m.ulog2, t, W, lc, swz, &p->pass[1]);
+        int st = build_tiled(T1, m.c, m.ulog2, t, t, W, lc, swz, &p->pass[1]);
         if (st != BMMC_OK) return st;
         p->npasses = 2;
         info.passes = 2;
@@ -814,15 +833,15 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         to_element_level(T1, m.c, dlow, n, p->factor_A[1], &p->factor_c[1]);
         return BMMC_OK;
     }
-    // fused single pass: tile rows span the high parts of B's first t
-    // columns (reduced basis), padded with unit vectors.
+    // fused single pass: tile rows span the high parts (above the a in-row
+    // bits) of B's first b columns (reduced basis), padded with unit vectors.
     Basis vb;
-    for (int j = 0; j < t; ++j) vb.add(B.col(j) & ~low_mask(t));
+    for (int j = 0; j < b; ++j) vb.add(B.col(j) & ~low_mask(a));
     std::vector<u64> W = vb.vec;
     Basis wb = vb;
-    for (int r = t; r < m.nb && (int)W.size() < t; ++r)
+    for (int r = a; r < m.nb && (int)W.size() < b; ++r)
         if (wb.add(u64(1) << r)) W.push_back(u64(1) << r);
-    int st = build_tiled(m.A, m.c, m.ulog2, t, W, lc, swz, &p->pass[0]);
+    int st = build_tiled(m.A, m.c, m.ulog2, a, b, W, lc, swz, &p->pass[0]);
     if (st != BMMC_OK) return st;
     info.tile_log2 = t;
     single(BMMC_ROUTE_FUSED);

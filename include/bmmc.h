@@ -93,6 +93,11 @@ typedef struct bmmc_plan_options {
                        of 6, >= 8 = a random invertible F2 map seeded with the value
                        (the set of tiles is the same; only the order in which
                        workgroups meet them changes) */
+    int tile_skew;  /* single-pass tile shape: 0 = square tiles of 2^t rows of 2^t units;
+                       s != 0 = rectangular tiles of the same 2^(2t) units whose input
+                       rows hold 2^(t-s) units and output rows 2^(t+s) (longer output
+                       pieces for s > 0); |s| < t, and both rows must hold at least one
+                       16-byte vector (or the whole row when t is small) */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */
@@ -128,7 +133,9 @@ typedef struct bmmc_plan_info {
  * affine, so the address of any element is the XOR of the contributions of
  * its block, chunk and unit bits).
  *
- * TILED: the array is cut into 2^blk_bits tiles of 2^(2t) units; tile b
+ * TILED: the array is cut into 2^blk_bits tiles of 2^(2t) units, each
+ * 2^(2t - in_row_log2) input rows of 2^in_row_log2 contiguous units and
+ * 2^(2t - out_row_log2) output rows of 2^out_row_log2 units; tile b
  * starts at input offset XOR_k in_blk[k] over the set bits k of b.  With the
  * one-tile launch a workgroup moves tiles b = (w << iters_log2) | s; with
  * the persistent and streamed launches workgroup w, as walker
@@ -181,6 +188,9 @@ typedef struct bmmc_pass_desc {
     uint32_t st_lds[BMMC_MAX_CHUNK_BITS];
     uint32_t st_unit[4];
     uint64_t in_c;       /* CHUNK: input offset of output chunk 0 */
+    int32_t in_row_log2;  /* TILED: log2 units per input row of a tile (t - skew) */
+    int32_t out_row_log2; /* TILED: log2 units per output row of a tile (t + skew);
+                             a tile holds 2^(in_row_log2 + out_row_log2) = 2^(2t) units */
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */
@@ -236,8 +246,9 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * larger), the launch style (the planner's persistent or streamed walk, or
  * one workgroup per tile), the loads in flight of a streamed walk (one or two
  * tiles per loader wave) and the block order (bmmc_plan_options.block_map 5,
- * the planner's, 1, 3 and 6, and the random orders 8 and 9): up to 48
- * candidates.  An option the caller fixed at plan
+ * the planner's, 1, 3 and 6, and the random orders 8 and 9), plus
+ * rectangular tiles (tile_skew 1, -1, 2 and -2 at the larger side, orders 5,
+ * 6 and 3): up to 72 candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events; the candidate with the

@@ -146,11 +146,16 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
         raise ReplayError("output unit never written")
 
     if check_coalescing:
-        # load: the lanes of a row read it whole; drain: every group of
-        # 2^pc lanes stores one contiguous aligned piece (128 bytes, or the
-        # whole segment when shorter)
-        pc_load = cpsl
-        pc_drain = min(cpsl, max(0, 7 - (ul + wl)))
+        # load: the lanes of an input row read it whole; drain: every group
+        # of 2^pc lanes stores one contiguous aligned piece (128 bytes, or the
+        # whole output row when shorter).  Rectangular tiles have rows of
+        # 2^in_row_log2 units on the input side and 2^out_row_log2 on the
+        # output side (both t for square tiles).
+        a, b = d.in_row_log2, d.out_row_log2
+        if a + b != 2 * t or min(a, b) < wl:
+            raise ReplayError("row lengths do not match the tile geometry")
+        pc_load = a - wl
+        pc_drain = min(b - wl, max(0, 7 - (ul + wl)))
         for arr, pcx in ((in_off, pc_load), (out_off, pc_drain)):
             G = 1 << pcx
             a = arr.reshape(nblk, (NT * J) // G, G)

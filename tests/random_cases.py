@@ -18,8 +18,11 @@ from bmmc_affine_index_amd import workloads as wl
 
 KINDS = ("general", "bpc", "bitrev", "transpose", "complement", "blockperm", "lowkeep")
 ELEMS = (1, 2, 4, 8, 16)
-N_CASES = 600
+N_SQUARE = 600
+N_SKEW = 180   # rectangular tiles (tile_skew), drawn from a stream of their own
+N_CASES = N_SQUARE + N_SKEW
 MASTER_SEED = 0x5EED_B44C
+SKEW_SEED = 0x5EED_5CE7
 
 
 @dataclass
@@ -63,7 +66,7 @@ def cases():
     """The fixed list of N_CASES cases (the same on every call)."""
     rng = np.random.Generator(np.random.PCG64(MASTER_SEED))
     out = []
-    for i in range(N_CASES):
+    for i in range(N_SQUARE):
         kind = KINDS[int(rng.integers(len(KINDS)))]
         elem = ELEMS[int(rng.integers(len(ELEMS)))]
         n = int(rng.integers(1, 19))
@@ -101,6 +104,44 @@ def cases():
         if rng.random() < 0.15:
             opts["no_swizzle"] = 1
         out.append(Case(i, kind, n, elem, int(rng.integers(1, 1 << 30)), opts))
+    # rectangular tiles: single-pass routes with input and output rows of
+    # different lengths; a skew the library refuses for the drawn size is
+    # brought towards 0 until it accepts one (planning is host-only)
+    rng = np.random.Generator(np.random.PCG64(SKEW_SEED))
+    for i in range(N_SKEW):
+        kind = KINDS[int(rng.integers(len(KINDS)))]
+        elem = ELEMS[int(rng.integers(len(ELEMS)))]
+        n = int(rng.integers(6, 19))
+        opts = {}
+        route = int(rng.choice([bm.ROUTE_AUTO, bm.ROUTE_FUSED]))
+        if route:
+            opts["route"] = route
+        launch = int(rng.choice([bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE, bm.LAUNCH_PERSISTENT,
+                                 bm.LAUNCH_STREAMED]))
+        if launch:
+            opts["launch"] = launch
+        t = int(rng.choice([0, 0, 4, 5, 6, 7]))
+        if t:
+            opts["tile_log2"] = t
+        bmap = int(rng.choice([0, 1, 3, 5, 6, 8, 11]))
+        if bmap:
+            opts["block_map"] = bmap
+        if launch == bm.LAUNCH_STREAMED and rng.random() < 0.5:
+            opts["depth"] = int(rng.integers(1, 3))
+        if rng.random() < 0.15:
+            opts["no_swizzle"] = 1
+        skew = int(rng.choice([1, -1, 2, -2, 3, -3]))
+        case = Case(N_SQUARE + i, kind, n, elem, int(rng.integers(1, 1 << 30)), opts)
+        A, c = case.matrix()
+        while skew:
+            try:
+                bm.Plan(n, A, c, elem, tile_skew=skew, **opts)
+                break
+            except bm.BmmcError:
+                skew -= 1 if skew > 0 else -1
+        if skew:
+            case.options["tile_skew"] = skew
+        out.append(case)
     return out
 
 

@@ -430,12 +430,16 @@ def test_replay_detects_planted_table_errors():
 # LDS banks under the planner's model
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kind,n,e", [("bitrev", 20, 4), ("transpose", 24, 4),
-                                      ("general", 20, 4), ("general", 30, 4),
-                                      ("bpc", 27, 16), ("bitrev", 28, 4)])
-def test_swizzle_makes_reads_conflict_free(kind, n, e):
+@pytest.mark.parametrize("kind,n,e,skew", [("bitrev", 20, 4, 0), ("transpose", 24, 4, 0),
+                                           ("general", 20, 4, 0), ("general", 30, 4, 0),
+                                           ("bpc", 27, 16, 0), ("bitrev", 28, 4, 0),
+                                           ("bitrev", 28, 4, 1), ("bitrev", 28, 4, -1),
+                                           ("general", 30, 4, 1), ("bpc", 27, 16, 1),
+                                           ("transpose", 24, 4, -1)])
+def test_swizzle_makes_reads_conflict_free(kind, n, e, skew):
     A, c = _matrix(kind, n, 7)
-    P = bm.Plan(n, A, c, e)
+    P = bm.Plan(n, A, c, e, **(dict(tile_skew=skew, tile_log2=7 if e == 4 else 6)
+                               if skew else {}))
     d = P.passes()[-1]
     assert d.kernel == bm.KERNEL_TILED
     U = 1 << d.unit_log2
@@ -452,7 +456,7 @@ def test_swizzle_makes_reads_conflict_free(kind, n, e):
         assert bank_cycles(ra, U, banks) == ideal_r, (banks, P.describe())
         assert bank_cycles(wa, CB, banks) == ideal_w
     # the plain layout is conflicted for the transpose (the ablation)
-    if kind == "transpose":
+    if kind == "transpose" and not skew:
         P0 = bm.Plan(n, A, c, e, no_swizzle=1)
         r0 = tiled_read_addresses(P0.passes()[0])
         assert bank_cycles(r0, U, 64) > bank_cycles(ra, U, 64)
@@ -541,6 +545,8 @@ MAX_CASES = [  # (n, elem_bytes, kind, plan options): up to 2^36 bytes per array
     (32, 2, "transpose", dict(launch=bm.LAUNCH_STREAMED)),
     (32, 1, "general", dict(route=bm.ROUTE_NAIVE)),
     (32, 16, "general", dict(tile_log2=2, launch=bm.LAUNCH_ONE_TILE)),
+    (32, 4, "bitrev", dict(tile_log2=7, tile_skew=1)),
+    (32, 8, "general", dict(tile_skew=-1, launch=bm.LAUNCH_PERSISTENT)),
 ]
 
 
@@ -620,6 +626,8 @@ def _desc_bytes(d):
     ("general", 20, 4, dict(launch=bm.LAUNCH_STREAMED, depth=1, grid_log2=6, walk=2)),
     ("general", 9, 4, dict(route=bm.ROUTE_NAIVE)), ("identity", 12, 4, {}),
     ("complement", 12, 4, {}), ("general", 30, 4, dict(cache_hint=1)),
+    ("bitrev", 28, 4, dict(tile_log2=7, tile_skew=1)), ("general", 24, 4, dict(tile_skew=-2)),
+    ("bpc", 27, 16, dict(tile_skew=1, launch=bm.LAUNCH_PERSISTENT)),
 ], ids=lambda c: "%s-n%d-e%d-%s" % (c[0], c[1], c[2],
                                     "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
 def test_options_rebuild_the_same_tables(case):
@@ -646,3 +654,45 @@ def test_options_rebuild_the_same_tables(case):
     assert Q.options() == opts
     for k, v in kw.items():
         assert opts[k] == v
+
+
+# --------------------------------------------------------------------------
+# Rectangular tiles (tile_skew)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,skew", [("c3", 1), ("c3", -1), ("c4", 1), ("c4", -1), ("c2", 1),
+                                       ("c5", 1), ("c5", -1)])
+def test_skewed_tiles_at_workload_size(name, skew):
+    """A skewed tile keeps the square tile's 2^(2t) units with input rows of
+    2^(t - s) units and output rows of 2^(t + s); at the workloads' full
+    sizes, sampled tiles replay to the oracle's map (range, exactly-once and
+    destination checks on every unit of each sampled tile)."""
+    w = wl.WORKLOADS[name]
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n)
+    t = 7 if w.elem_bytes == 4 else 6
+    P = bm.Plan(w.n, A, c, w.elem_bytes, tile_log2=t, tile_skew=skew)
+    assert P.info.passes == 1
+    d = P.passes()[0]
+    assert (d.t, d.in_row_log2, d.out_row_log2) == (t, t - skew, t + skew)
+    assert P.describe()["tile_skew"] == skew and P.options()["tile_skew"] == skew
+    checked = check_pass_sampled(d, *P.factors()[0], w.elem_bytes.bit_length() - 1,
+                                 _sampled_blocks(1 << d.blk_bits, 77), oracle.map_indices)
+    assert checked >= 55 * (1 << (2 * t))
+
+
+def test_skew_argument_errors():
+    n = 20
+    A = wl.bit_reverse_matrix(n)
+    for bad in (dict(tile_skew=9), dict(tile_skew=-9), dict(tile_log2=3, tile_skew=3)):
+        with pytest.raises(bm.BmmcError):
+            bm.Plan(n, A, 0, 4, **bad)
+    # rows shorter than the kernel's 16-byte chunk are refused
+    with pytest.raises(bm.BmmcError):
+        bm.Plan(n, A, 0, 4, tile_log2=6, tile_skew=5)
+    # the two-pass route of a general matrix has square tiles only; a BPC
+    # takes one tile pass whatever the route asks, skewed if asked
+    G, c = _inv(n, 3)
+    with pytest.raises(bm.BmmcError):
+        bm.Plan(n, G, c, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
+    P = bm.Plan(n, A, 0, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
+    assert P.info.passes == 1 and P.describe()["tile_skew"] == 1

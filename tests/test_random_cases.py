@@ -18,7 +18,9 @@ def test_cases_are_fixed_and_span_the_options():
     assert len(a) == N_CASES
     seen = {k for c in a for k in c.options}
     assert {"route", "launch", "tile_log2", "block_map", "iters_log2", "grid_log2", "walk",
-            "depth", "cache_hint", "no_swizzle"} <= seen
+            "depth", "cache_hint", "no_swizzle", "tile_skew"} <= seen
+    skews = {c.options.get("tile_skew", 0) for c in a}
+    assert {1, -1, 2, -2} <= skews
     assert {c.kind for c in a} == {"general", "bpc", "bitrev", "transpose", "complement",
                                    "blockperm", "lowkeep"}
     assert {c.elem for c in a} == {1, 2, 4, 8, 16}
