@@ -502,7 +502,7 @@ def measure_c5(run):
     bufs = run.buffers(x, nbytes)
     steps = run.steps_for(nbytes, headline=False)
     cp = run.copy_ceiling(bufs, nbytes, steps)
-    vals, okays, plans = [], 0, []
+    vals, okays, plans, options = [], 0, [], []
     for k in range(C5_PERMS):
         A, c = wl.workload_matrix("c5", perm_index=k)
         plan = bm.Plan(n, A, c, elem)
@@ -515,6 +515,7 @@ def measure_c5(run):
         d = plan.describe()
         plans.append("%s t=%s skew %s order %s" % (d["kernels"][-1], d["tile_log2"],
                                                    d["tile_skew"], d["block_map"]))
+        options.append(plan.options())
         log("c5 perm %d: %.1f GB/s (%.3f of copy) %s, %s" % (k, r["gbs"], r["gbs"] / cp["gbs"],
                                                           plans[-1], parity))
     order = sorted(range(len(vals)), key=lambda i: vals[i])
@@ -529,9 +530,43 @@ def measure_c5(run):
          "min_perm": order[0], "max_perm": order[-1], "copy_gbs": round(cp["gbs"], 2),
          "steps": steps, "replays": run.args.replays,
          "per_perm_gbs": [round(v, 1) for v in vals], "per_perm_plan": plans,
+         "per_perm_options": options,
          "parity": ("bit-exact vs oracle on %d of %d permutations (2^20 + 2 sampled "
                     "elements each)" % (okays, len(vals)))}
     return e, okays == len(vals)
+
+
+def run_candidates(torch, args, run, plan, n, A, c, elem, x, bufs, workload_name):
+    """Every plan bmmc_plan_tune_pairs would time, in its order: one
+    bmmc_copy of the array, then --steps executions of the candidate, on the
+    stream, one candidate after the other.  In a counter run, each candidate's
+    dispatches are those between two copies.  Prints the candidates' options
+    and table digests as one JSON line; the last execution of each is checked
+    against the oracle on sampled elements."""
+    nbytes = elem << n
+    i0, o0 = bufs[0]
+    out = []
+    ok_all = True
+    for k, opts in enumerate(bm.bmmc_plan_tune_candidates(plan.handle)):
+        q = bm.Plan(n, A, c, elem, **opts)
+        st = bm.bmmc_copy(i0, o0, nbytes, run.h)
+        if st != bm.OK:
+            raise bm.BmmcError(st, "bmmc_copy")
+        for _ in range(args.steps):
+            q(i0, o0, run.h)
+        torch.cuda.synchronize()
+        ok, parity = run.parity(q, A, c, x, bufs)
+        ok_all &= ok
+        out.append({"index": k, "plan_options": q.options(),
+                    "plan_tables_digest": plan_tables_digest(q),
+                    "kernels": q.describe()["kernels"], "parity": parity})
+        log("candidate %d: %s %s" % (k, json.dumps(q.options(), sort_keys=True), parity))
+    print(json.dumps({"workload": workload_name, "kernel_source_digest": kernel_source_digest(),
+                      "bytes": int(nbytes), "runs_per_candidate": args.steps,
+                      "candidates": out}))
+    sys.stdout.flush()
+    if not ok_all:
+        sys.exit(3)
 
 
 def main():
@@ -585,6 +620,10 @@ def main():
                     help="the paper's Figure 9/11 variants over kinds and sizes, "
                          "one JSON line each (not the headline line)")
     ap.add_argument("--sizes", default="20,24,28", help="ablation: comma-separated n")
+    ap.add_argument("--candidates", action="store_true",
+                    help="run every plan the tuning would time for the workload, each "
+                         "--steps times after one bmmc_copy of the array (a separator for "
+                         "counter runs), and print them as one JSON line (not timed)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -662,6 +701,9 @@ def main():
     run = Runner(torch, args)
     log("headline %s: %s" % (workload_name, plan.describe()["kernels"]))
     bufs = run.buffers(x, nbytes)
+    if args.candidates:
+        run_candidates(torch, args, run, plan, n, A, c, elem, x, bufs, workload_name)
+        return
 
     # bmmc_plan_tune_pairs: time the candidate tile orders over the same
     # rotating buffer pairs and keep the fastest (outside the timed region,

@@ -47,7 +47,7 @@ MAX_PASSES = 2
 
 EXPORTED = (
     "bmmc_plan_create", "bmmc_plan_create_ex", "bmmc_execute", "bmmc_execute_noalloc",
-    "bmmc_plan_tune", "bmmc_plan_tune_pairs",
+    "bmmc_plan_tune", "bmmc_plan_tune_pairs", "bmmc_plan_tune_candidates",
     "bmmc_copy",
     "bmmc_plan_destroy", "bmmc_last_error", "bmmc_status_string", "bmmc_plan_get_info",
     "bmmc_plan_get_factor", "bmmc_plan_get_pass", "bmmc_plan_get_options", "bmmc_parm_matrix",
@@ -135,6 +135,9 @@ def lib():
                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int]
     L.bmmc_plan_tune_pairs.restype = ctypes.c_int
+    L.bmmc_plan_tune_candidates.argtypes = [ctypes.c_void_p, ctypes.POINTER(bmmc_plan_options),
+                                            ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.bmmc_plan_tune_candidates.restype = ctypes.c_int
     L.bmmc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.bmmc_copy.restype = ctypes.c_int
     L.bmmc_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -244,6 +247,20 @@ def bmmc_plan_tune_pairs(plan: int, pairs, stream=None, reps: int = 0) -> int:
     outs = (ctypes.c_void_p * max(k, 1))(*[_ptr(o) for _, o in pairs])
     return lib().bmmc_plan_tune_pairs(plan, ins if k else None, outs if k else None, k,
                                       _stream(stream), int(reps))
+
+
+def bmmc_plan_tune_candidates(plan: int):
+    """Options of every candidate bmmc_plan_tune_pairs would time, in order."""
+    count = ctypes.c_int()
+    st = lib().bmmc_plan_tune_candidates(plan, None, 0, ctypes.byref(count))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_tune_candidates")
+    opts = (bmmc_plan_options * max(count.value, 1))()
+    st = lib().bmmc_plan_tune_candidates(plan, opts, count.value, ctypes.byref(count))
+    if st != OK:
+        raise BmmcError(st, "bmmc_plan_tune_candidates")
+    return [{name: int(getattr(o, name)) for name, _ in bmmc_plan_options._fields_}
+            for o in opts[:count.value]]
 
 
 def bmmc_copy(inp, out, nbytes: int, stream=None) -> int:

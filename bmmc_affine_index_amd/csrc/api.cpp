@@ -101,6 +101,81 @@ int run_passes(const bmmc_pass_desc *pass, int npasses, const void *in, void *ou
     return run_pass(pass[1], scratch, out, s);
 }
 
+// The plans bmmc_plan_tune_pairs times, the planner's own choice first:
+// (tile side, launch style, streamed depth, block order) over the options
+// the caller left open, then rectangular tiles; candidates whose tables equal
+// an earlier one's are dropped.  Host-only.
+int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> &cand) {
+    // candidates: (tile side, launch style, block order), keeping what the
+    // caller fixed; the first is the planner's own choice
+    std::vector<int> launches, maps, tiles;
+    if (p->opt.launch) launches = {p->opt.launch};
+    else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
+    if (p->opt.block_map) maps = {p->opt.block_map};
+    // the planner's own first; the two seeded random orders spread the tiles
+    // in flight over the whole array, which lifts the matrices whose
+    // structured orders crowd them (random 16-byte BPCs: up to +6%)
+    else maps = {bmmc::kDefaultBlockMap, 1, 3, 6, 8, 9};
+    tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
+    // streamed launches: the planner's one tile of loads in flight per loader
+    // wave, and two (candidates that are not streamed come out the same for
+    // both and are dropped as duplicates)
+    std::vector<int> depths;
+    if (p->opt.depth) depths = {p->opt.depth};
+    else depths = {0, 2};
+    auto add = [&](const bmmc_plan_options &o) -> int {
+        std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
+        if (!q) return BMMC_ERR_OUT_OF_MEMORY;
+        if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) != BMMC_OK ||
+            !supported(*q))
+            return BMMC_OK;
+        q->opt = o;
+        // the next larger side (rows twice as long), once the planner's side
+        // is known; the planner clamps it to what the LDS and the index bits
+        // allow (duplicates drop out)
+        if (!p->opt.tile_log2 && tiles.size() == 1 && q->info.tile_log2 > 0 &&
+            q->info.tile_log2 < BMMC_MAX_TILE)
+            tiles.push_back(q->info.tile_log2 + 1);
+        bool dup = false;  // same tables as an earlier candidate
+        for (const auto &r : cand)
+            dup |= r->npasses == q->npasses &&
+                   std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
+        if (!dup) cand.push_back(std::move(q));
+        return BMMC_OK;
+    };
+    for (size_t ti = 0; ti < tiles.size(); ++ti)
+        for (int l : launches)
+            for (int m : maps)
+                for (int dp : depths) {
+                    bmmc_plan_options o = p->opt;
+                    o.tile_log2 = tiles[ti];
+                    o.launch = l;
+                    o.block_map = m;
+                    o.depth = dp;
+                    const int st = add(o);
+                    if (st != BMMC_OK) return st;
+                }
+    // rectangular tiles of the same size at the larger side, with the
+    // output-dense orders and the two-sided one: output rows 2 or 4 times as
+    // long as input rows, or as short (measured on MI355X: random 16-byte
+    // BPCs gain up to 5%, the others within 1%)
+    if (!p->opt.tile_skew && p->opt.route != BMMC_ROUTE_TWO_PASS &&
+        p->opt.route != BMMC_ROUTE_NAIVE)
+        for (int skew : {1, -1, 2, -2})
+            for (int l : launches)
+                for (int m : {bmmc::kDefaultBlockMap, 6, 3}) {
+                    if (p->opt.block_map && m != p->opt.block_map) continue;
+                    bmmc_plan_options o = p->opt;
+                    o.tile_log2 = tiles.back();
+                    o.launch = l;
+                    o.block_map = m;
+                    o.tile_skew = skew;
+                    const int st = add(o);
+                    if (st != BMMC_OK) return st;
+                }
+    return BMMC_OK;
+}
+
 }  // namespace
 
 namespace bmmc {
@@ -201,73 +276,9 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
         return st;
     }
 
-    // candidates: (tile side, launch style, block order), keeping what the
-    // caller fixed; the first is the planner's own choice
-    std::vector<int> launches, maps, tiles;
-    if (p->opt.launch) launches = {p->opt.launch};
-    else launches = {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE};
-    if (p->opt.block_map) maps = {p->opt.block_map};
-    // the planner's own first; the two seeded random orders spread the tiles
-    // in flight over the whole array, which lifts the matrices whose
-    // structured orders crowd them (random 16-byte BPCs: up to +6%)
-    else maps = {bmmc::kDefaultBlockMap, 1, 3, 6, 8, 9};
-    tiles = {p->opt.tile_log2};  // 0: the planner's side; one larger is added below
-    // streamed launches: the planner's one tile of loads in flight per loader
-    // wave, and two (candidates that are not streamed come out the same for
-    // both and are dropped as duplicates)
-    std::vector<int> depths;
-    if (p->opt.depth) depths = {p->opt.depth};
-    else depths = {0, 2};
     std::vector<std::unique_ptr<bmmc_plan>> cand;
-    auto add = [&](const bmmc_plan_options &o) -> int {
-        std::unique_ptr<bmmc_plan> q(new (std::nothrow) bmmc_plan());
-        if (!q) return BMMC_ERR_OUT_OF_MEMORY;
-        if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) != BMMC_OK ||
-            !supported(*q))
-            return BMMC_OK;
-        // the next larger side (rows twice as long), once the planner's side
-        // is known; the planner clamps it to what the LDS and the index bits
-        // allow (duplicates drop out)
-        if (!p->opt.tile_log2 && tiles.size() == 1 && q->info.tile_log2 > 0 &&
-            q->info.tile_log2 < BMMC_MAX_TILE)
-            tiles.push_back(q->info.tile_log2 + 1);
-        bool dup = false;  // same tables as an earlier candidate
-        for (const auto &r : cand)
-            dup |= r->npasses == q->npasses &&
-                   std::memcmp(r->pass, q->pass, sizeof(q->pass[0]) * q->npasses) == 0;
-        if (!dup) cand.push_back(std::move(q));
-        return BMMC_OK;
-    };
-    for (size_t ti = 0; ti < tiles.size(); ++ti)
-        for (int l : launches)
-            for (int m : maps)
-                for (int dp : depths) {
-                    bmmc_plan_options o = p->opt;
-                    o.tile_log2 = tiles[ti];
-                    o.launch = l;
-                    o.block_map = m;
-                    o.depth = dp;
-                    const int st = add(o);
-                    if (st != BMMC_OK) return st;
-                }
-    // rectangular tiles of the same size at the larger side, with the
-    // output-dense orders and the two-sided one: output rows 2 or 4 times as
-    // long as input rows, or as short (measured on MI355X: random 16-byte
-    // BPCs gain up to 5%, the others within 1%)
-    if (!p->opt.tile_skew && p->opt.route != BMMC_ROUTE_TWO_PASS &&
-        p->opt.route != BMMC_ROUTE_NAIVE)
-        for (int skew : {1, -1, 2, -2})
-            for (int l : launches)
-                for (int m : {bmmc::kDefaultBlockMap, 6, 3}) {
-                    if (p->opt.block_map && m != p->opt.block_map) continue;
-                    bmmc_plan_options o = p->opt;
-                    o.tile_log2 = tiles.back();
-                    o.launch = l;
-                    o.block_map = m;
-                    o.tile_skew = skew;
-                    const int st = add(o);
-                    if (st != BMMC_OK) return st;
-                }
+    int cst = tune_candidates(p, cand);
+    if (cst != BMMC_OK) return cst;
     if (cand.empty()) return BMMC_ERR_UNSUPPORTED;
 
     void *scratch = nullptr;
@@ -344,6 +355,22 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     std::memcpy(p->pass, q.pass, sizeof(p->pass));
     std::memcpy(p->factor_A, q.factor_A, sizeof(p->factor_A));
     std::memcpy(p->factor_c, q.factor_c, sizeof(p->factor_c));
+    return BMMC_OK;
+}
+
+int bmmc_plan_tune_candidates(const bmmc_plan *p, bmmc_plan_options *opts, int capacity,
+                              int *count) {
+    if (!p || !count || capacity < 0 || (capacity > 0 && !opts)) return BMMC_ERR_INVALID_ARG;
+    bool tiled = false;
+    for (int k = 0; k < p->npasses; ++k) tiled |= p->pass[k].kernel == BMMC_KERNEL_TILED;
+    std::vector<std::unique_ptr<bmmc_plan>> cand;
+    if (tiled) {
+        const int st = tune_candidates(p, cand);
+        if (st != BMMC_OK) return st;
+    }
+    *count = (int)cand.size();
+    for (int i = 0; i < (int)cand.size() && i < capacity; ++i)
+        bmmc_plan_get_options(cand[i].get(), &opts[i]);
     return BMMC_OK;
 }
 

@@ -269,6 +269,15 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
 int bmmc_plan_tune_pairs(bmmc_plan *plan, const void *const *ins, void *const *outs, int npairs,
                          void *stream, int reps);
 
+/* The candidates bmmc_plan_tune_pairs would time for this plan, as the
+ * options that build each (bmmc_plan_create_ex with them gives that
+ * candidate's tables), in the order it times them, the planner's own choice
+ * first.  Writes min(count, capacity) entries to opts and the number of
+ * candidates to *count (0 for a plan with no tile pass).  Host-only; for
+ * profiling every plan a tuning may pick. */
+int bmmc_plan_tune_candidates(const bmmc_plan *plan, bmmc_plan_options *opts, int capacity,
+                              int *count);
+
 /* bmmc_plan_tune_pairs with the one pair in -> out. */
 int bmmc_plan_tune(bmmc_plan *plan, const void *in, void *out, void *stream, int reps);
 

@@ -696,3 +696,26 @@ def test_skew_argument_errors():
         bm.Plan(n, G, c, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
     P = bm.Plan(n, A, 0, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
     assert P.info.passes == 1 and P.describe()["tile_skew"] == 1
+
+
+def test_tune_candidates_rebuild_distinct_plans():
+    """bmmc_plan_tune_candidates lists options that rebuild distinct tables,
+    the planner's own plan first, including rectangular tiles; a plan with no
+    tile pass has none."""
+    for name in ("c4", "c3", "c5"):
+        w = wl.WORKLOADS[name]
+        A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n)
+        P = bm.Plan(w.n, A, c, w.elem_bytes)
+        cands = bm.bmmc_plan_tune_candidates(P.handle)
+        assert 20 <= len(cands) <= 72
+        digests = set()
+        for k, o in enumerate(cands):
+            Q = bm.Plan(w.n, A, c, w.elem_bytes, **o)
+            assert Q.options() == o
+            digests.add(b"".join(_desc_bytes(d) for d in Q.passes()))
+            if k == 0:
+                assert [_desc_bytes(d) for d in Q.passes()] == [_desc_bytes(d) for d in P.passes()]
+        assert len(digests) == len(cands)
+        assert {o["tile_skew"] for o in cands} >= {0, 1, -1, 2, -2}
+    R = bm.Plan(12, wl.identity_matrix(12), 5, 4)
+    assert bm.bmmc_plan_tune_candidates(R.handle) == []
