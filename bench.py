@@ -489,6 +489,10 @@ def measure_case(run, name, route, x=None, bufs=None, A=None, c=None):
          "tune_ms": round(tune_ms, 1), "parity": parity}
     if plan.info.passes > 1:
         e["transfer_gbs"] = round(plan.info.passes * r["gbs"], 2)
+    else:
+        # HBM bytes per launch from the committed counter summary of this
+        # plan, when there is one for this device code and these tables
+        e["traffic"] = read_traffic(name, plan.options(), plan_tables_digest(plan))
     return e, ok
 
 
