@@ -10,6 +10,7 @@
 
 #include "../../include/bmmc.h"
 #include "../../include/bmmc_testing.h"
+#include "kernels/tiled_cfg.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -56,7 +57,7 @@ bool supported(const bmmc_plan &p) {
     for (int k = 0; k < p.npasses; ++k) {
         const bmmc_pass_desc &d = p.pass[k];
         if (d.kernel == BMMC_KERNEL_TILED &&
-            !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2, d.launch))
+            !bmmc::tiled_supported(d.unit_log2, d.t, d.iters_log2, d.launch, d.threads_log2))
             return false;
     }
     return true;
@@ -170,6 +171,28 @@ int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> 
                     o.launch = l;
                     o.block_map = m;
                     o.tile_skew = skew;
+                    const int st = add(o);
+                    if (st != BMMC_OK) return st;
+                }
+    // 512 threads per tile at the larger side (twice the waves per SIMD to
+    // hide the latency between a tile's loads and its stores), square and
+    // with the output rows twice or half as long, on every launch style
+    if (!p->opt.tile_threads_log2 && p->opt.iters_log2 == 0)
+        for (int skew : {0, 1, -1})
+            for (int l : {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE, BMMC_LAUNCH_STREAMED})
+                for (int m : {bmmc::kDefaultBlockMap, 6}) {
+                    if ((p->opt.launch && l != p->opt.launch) ||
+                        (p->opt.block_map && m != p->opt.block_map) ||
+                        (p->opt.tile_skew && skew != p->opt.tile_skew) ||
+                        (skew && (p->opt.route == BMMC_ROUTE_TWO_PASS ||
+                                  p->opt.route == BMMC_ROUTE_NAIVE)))
+                        continue;
+                    bmmc_plan_options o = p->opt;
+                    o.tile_log2 = tiles.back();
+                    o.launch = l;
+                    o.block_map = m;
+                    o.tile_skew = skew;
+                    o.tile_threads_log2 = bmmc::kTileWideNTL;
                     const int st = add(o);
                     if (st != BMMC_OK) return st;
                 }
@@ -432,6 +455,7 @@ int bmmc_plan_get_options(const bmmc_plan *p, bmmc_plan_options *opt) {
         o.block_map = d.block_map;
         o.cache_hint = d.cache_hint ? 2 : 1;
         o.tile_skew = d.out_row_log2 - d.t;
+        o.tile_threads_log2 = d.threads_log2;
         if (d.launch != BMMC_LAUNCH_ONE_TILE) {
             o.grid_log2 = d.grid_log2;
             o.walk = d.walk;

@@ -136,11 +136,11 @@ __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds
 
 // One workgroup per tile, or per 2^IT tiles whose loads are all issued
 // before the barrier (the pages' iterated variant).
-template <int UL, int T, int IT, bool NT>
-__global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
+template <int UL, int T, int IT, bool NT, int TL>
+__global__ void __launch_bounds__((TiledCfg<UL, T, IT, TL>::NT))
     bmmc_tiled_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                       const bmmc_pass_desc d, uint64_t blk0) {
-    using C = TiledCfg<UL, T, IT>;
+    using C = TiledCfg<UL, T, IT, TL>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
     const LaneParts p = lane_parts<C, T>(d, threadIdx.x);
     const uint64_t tile0 = (blk0 + blockIdx.x) << IT;
@@ -176,11 +176,11 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, IT>::NT))
 // already in flight.  One barrier per tile suffices: a buffer is rewritten
 // two tiles later, after every thread has passed the barrier that follows
 // its reads.
-template <int UL, int T, bool NT>
-__global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
+template <int UL, int T, bool NT, int TL>
+__global__ void __launch_bounds__((TiledCfg<UL, T, 0, TL>::NT))
     bmmc_tiled_persistent_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                  const bmmc_pass_desc d) {
-    using C = TiledCfg<UL, T, 0>;
+    using C = TiledCfg<UL, T, 0, TL>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE];
     const LaneParts p = lane_parts<C, T>(d, threadIdx.x);
     const int r = d.blk_bits - d.grid_log2;
@@ -249,11 +249,11 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, 0>::NT))
 // on the scalar form (0.19 us when the choice was a run-time branch).
 constexpr int kSmallBlkBits = 8;
 
-template <int UL, int T, int DEPTH, bool NT, bool SB>
-__global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0>::NT))
+template <int UL, int T, int DEPTH, bool NT, bool SB, int TL>
+__global__ void __launch_bounds__((2 * TiledCfg<UL, T, 0, TL>::NT))
     bmmc_tiled_streamed_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                                const bmmc_pass_desc d) {
-    using C = TiledCfg<UL, T, 0>;
+    using C = TiledCfg<UL, T, 0, TL>;
     static_assert(DEPTH == 1 || DEPTH == 2, "tiles of loads in flight per loader wave");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE];
     static_assert(C::NT >= 64, "each role must be whole waves");
@@ -403,25 +403,25 @@ struct TiledArgs {
     hipStream_t s;
 };
 
-template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
-    using C = TiledCfg<UL, T, IT>;
+template <int UL, int T, int IT, bool NT, int TL> int launch_nt(const TiledArgs &a) {
+    using C = TiledCfg<UL, T, IT, TL>;
     if (a.d->launch == BMMC_LAUNCH_STREAMED) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072 && C::NT >= 64 && 2 * C::NT <= 1024) {
             const dim3 grid(1u << a.d->grid_log2), block(2 * C::NT);
             const bool small = a.d->blk_bits <= kSmallBlkBits;
             if (a.d->depth == 2) {
                 if (small)
-                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, true>), grid,
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, true, TL>), grid,
                                        block, 0, a.s, a.in, a.out, *a.d);
                 else
-                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, false>), grid,
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 2, NT, false, TL>), grid,
                                        block, 0, a.s, a.in, a.out, *a.d);
             } else {
                 if (small)
-                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, true>), grid,
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, true, TL>), grid,
                                        block, 0, a.s, a.in, a.out, *a.d);
                 else
-                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, false>), grid,
+                    hipLaunchKernelGGL((bmmc_tiled_streamed_kernel<UL, T, 1, NT, false, TL>), grid,
                                        block, 0, a.s, a.in, a.out, *a.d);
             }
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
@@ -431,7 +431,7 @@ template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
     }
     if (a.d->launch == BMMC_LAUNCH_PERSISTENT) {
         if constexpr (IT == 0 && 2 * C::TILE <= 131072) {
-            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T, NT>),
+            hipLaunchKernelGGL((bmmc_tiled_persistent_kernel<UL, T, NT, TL>),
                                dim3(1u << a.d->grid_log2), dim3(C::NT), 0, a.s, a.in, a.out,
                                *a.d);
             return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
@@ -443,15 +443,29 @@ template <int UL, int T, int IT, bool NT> int launch_nt(const TiledArgs &a) {
     const uint64_t per = max_blocks_per_launch(C::NT);
     for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
         const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
-        hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT, NT>), dim3((uint32_t)nb), dim3(C::NT),
+        hipLaunchKernelGGL((bmmc_tiled_kernel<UL, T, IT, NT, TL>), dim3((uint32_t)nb), dim3(C::NT),
                            0, a.s, a.in, a.out, *a.d, b0);
     }
     return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
 }
 
 // cache_hint 3: non-temporal loads and stores; 0: plain.
+template <int UL, int T, int IT, int TL> int launch_hint(const TiledArgs &a) {
+    return a.d->cache_hint ? launch_nt<UL, T, IT, true, TL>(a)
+                           : launch_nt<UL, T, IT, false, TL>(a);
+}
+
+// threads_log2 picks the 256- or 512-thread instantiation; the wide one is
+// compiled only where a tile has more than 256 chunks and for one tile per
+// workgroup (the iterated variant keeps 256).
 template <int UL, int T, int IT> int launch_one(const TiledArgs &a) {
-    return a.d->cache_hint ? launch_nt<UL, T, IT, true>(a) : launch_nt<UL, T, IT, false>(a);
+    constexpr int narrow = tile_threads_log2(UL, T, kTileMaxNTL);
+    if constexpr (IT == 0 && tile_threads_log2(UL, T, kTileWideNTL) > narrow) {
+        if (a.d->threads_log2 == tile_threads_log2(UL, T, kTileWideNTL))
+            return launch_hint<UL, T, IT, kTileWideNTL>(a);
+    }
+    if (a.d->threads_log2 != narrow) return BMMC_ERR_UNSUPPORTED;
+    return launch_hint<UL, T, IT, kTileMaxNTL>(a);
 }
 
 // Walks the compiled (UL, T, IT) space; `launch` = false only answers

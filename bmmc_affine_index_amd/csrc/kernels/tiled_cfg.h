@@ -6,19 +6,24 @@
 
 namespace bmmc {
 
-// log2 of the most threads one tile is moved by.  256: measured against 512
-// (within 4% either way) and 1024 (one-tile launches lose up to 55% to the
-// lower occupancy).
+// log2 of the most threads one tile is moved by: 256 by default, 512 as a
+// plan option (bmmc_plan_options.tile_threads_log2).  With 512 a wave holds
+// half as many chunks and each SIMD runs twice the waves, which hides the
+// LDS and barrier latency between a tile's loads and its stores: measured on
+// MI355X, bit reversal n = 28 on the streamed launch moves from 0.850 to
+// 0.865 of copy; one-tile launches of 64 KiB tiles lose 1% (random BMMC).
+// 1024 threads lose up to 55% on one-tile launches (occupancy).
 constexpr int kTileMaxNTL = 8;
+constexpr int kTileWideNTL = 9;
 
-template <int UL, int T, int IT> struct TiledCfg {
+template <int UL, int T, int IT, int TL = kTileMaxNTL> struct TiledCfg {
     static constexpr int U = 1 << UL;
     static constexpr int WL = (4 - UL) < T ? (4 - UL) : T;  // log2 units per chunk
     static constexpr int W = 1 << WL;
     static constexpr int CB = U << WL;                      // chunk bytes
     static constexpr int CPSL = T - WL;                     // log2 chunks per row
     static constexpr int CHL = 2 * T - WL;                  // log2 chunks per tile
-    static constexpr int NTL = CHL < kTileMaxNTL ? CHL : kTileMaxNTL;  // log2 threads
+    static constexpr int NTL = CHL < TL ? CHL : TL;        // log2 threads
     static constexpr int NT = 1 << NTL;
     static constexpr int RPPL = NTL - CPSL;                 // log2 rows per pass
     static constexpr int JL = CHL - NTL;                    // log2 passes per tile
@@ -43,6 +48,15 @@ constexpr bool tiled_config_exists(int ul, int t, int it) {
 
 template <int UL, int T, int IT> constexpr bool valid_cfg() {
     return tiled_config_exists(UL, T, IT);
+}
+
+// log2 of the threads that move one tile of 2^(2t) units of 2^ul bytes when
+// at most 2^tl may: one 16-byte chunk (or the whole row, for short rows) per
+// thread and pass.
+constexpr int tile_threads_log2(int ul, int t, int tl) {
+    const int wl = (4 - ul) < t ? (4 - ul) : t;
+    const int chl = 2 * t - wl;
+    return chl < tl ? chl : tl;
 }
 
 }  // namespace bmmc

@@ -18,6 +18,8 @@
 // written from the F2 algebra; each step says what it guarantees.
 #include "plan.h"
 
+#include "kernels/tiled_cfg.h"
+
 #include <algorithm>
 #include <cstring>
 #include <vector>
@@ -207,14 +209,13 @@ struct TileGeom {
     int rppl;          // log2 rows handled per pass by the workgroup
 };
 
-TileGeom tile_geom(int ulog2, int t) {
+TileGeom tile_geom(int ulog2, int t, int tl) {
     TileGeom g;
     g.ulog2 = ulog2;
     g.t = t;
     g.wl = std::min(4 - ulog2, t);
     g.cpsl = t - g.wl;
-    int chunks_l = 2 * t - g.wl;
-    g.ntl = std::min(8, chunks_l);
+    g.ntl = tile_threads_log2(ulog2, t, tl);
     g.rppl = g.ntl - g.cpsl;
     return g;
 }
@@ -246,6 +247,7 @@ struct LaunchChoice {
     int depth;       // streamed: tiles of loads in flight per loader wave
     bool auto_launch;  // launch style left to the planner
     int cache_hint;    // descriptor value: 3 non-temporal loads and stores, 0 plain
+    int threads_log2;  // most threads per tile, log2 (8 or 9)
 };
 
 // Highest set bit of a byte offset (-1 for 0).
@@ -397,7 +399,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
     Mat Minv;
     if (!inverse(M, Minv)) return BMMC_ERR_INVALID_ARG;
 
-    const TileGeom g = tile_geom(ulog2, t);
+    const TileGeom g = tile_geom(ulog2, t, lc.threads_log2);
     // both rows must hold whole vector chunks of the kernel's width
     if (a < g.wl || b < g.wl) return BMMC_ERR_INVALID_ARG;
     const int cpsl_in = a - g.wl, cpsl_out = b - g.wl;  // log2 chunks per row, each side
@@ -563,6 +565,7 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
     d->blk_bits = blk_bits;
     d->in_row_log2 = a;
     d->out_row_log2 = b;
+    d->threads_log2 = g.ntl;
     const u64 tile_bytes = u64(1) << (K + ulog2);
     int launch = lc.persistent;
     // Planner's choice, measured untuned with the default tile order: below
@@ -719,6 +722,11 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     // than its margin.
     lc.depth = o.depth ? o.depth : 1;
     lc.block_map = o.block_map ? o.block_map : kDefaultBlockMap;
+    if (o.tile_threads_log2 < 0 || o.tile_threads_log2 > kTileWideNTL) return BMMC_ERR_INVALID_ARG;
+    // Planner's choice: 256 threads per tile; 512 are a tuning candidate.
+    // Below 256 chunks per tile the count is the chunk count either way.
+    lc.threads_log2 = o.tile_threads_log2 ? std::max(o.tile_threads_log2, kTileMaxNTL)
+                                          : kTileMaxNTL;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);

@@ -4,7 +4,14 @@
 
 namespace bmmc {
 
-bool tiled_supported(int unit_log2, int t, int iters_log2, int launch) {
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2) {
+    if (unit_log2 < 0 || unit_log2 > 4 || t < 1) return false;
+    // the 256-thread kernels, and the 512-thread ones where a tile has more
+    // than 256 chunks and one tile per workgroup
+    const int narrow = tile_threads_log2(unit_log2, t, kTileMaxNTL);
+    const int wide = tile_threads_log2(unit_log2, t, kTileWideNTL);
+    if (threads_log2 != narrow && !(threads_log2 == wide && wide > narrow && iters_log2 == 0))
+        return false;
     if ((launch == BMMC_LAUNCH_PERSISTENT || launch == BMMC_LAUNCH_STREAMED) &&
         (iters_log2 != 0 || unit_log2 < 0 || unit_log2 > 4 || t < 1 ||
          (uint64_t(2) << (2 * t + unit_log2)) > 131072))

@@ -98,6 +98,9 @@ typedef struct bmmc_plan_options {
                        rows hold 2^(t-s) units and output rows 2^(t+s) (longer output
                        pieces for s > 0); |s| < t, and both rows must hold at least one
                        16-byte vector (or the whole row when t is small) */
+    int tile_threads_log2; /* tile pass: log2 of the most threads that move one tile,
+                              8 (256) or 9 (512); 0 = planner's choice (8).  Tiles of
+                              fewer chunks use one thread per chunk. */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */
@@ -143,7 +146,7 @@ typedef struct bmmc_plan_info {
  * and gray(k) = k XOR (k >> 1), the tiles v * 2^r XOR gray(k) (ranges) or
  * gray(k) * 2^grid_log2 XOR v (interleaved).
  * A tile is moved in chunks of 2^chunk_log2 units: chunk c = (j << T) | tid
- * (T = log2 threads per workgroup, j the pass) is loaded from input offset
+ * (T = threads_log2, j the pass) is loaded from input offset
  * tile base XOR_p ld_in[p] and written to LDS address XOR_p ld_lds[p] over
  * the set bits p of c; in the drain phase chunk c is stored at output offset
  * XOR_k out_blk[k] XOR out_c XOR_p st_out[p], its unit e read from LDS
@@ -191,6 +194,8 @@ typedef struct bmmc_pass_desc {
     int32_t in_row_log2;  /* TILED: log2 units per input row of a tile (t - skew) */
     int32_t out_row_log2; /* TILED: log2 units per output row of a tile (t + skew);
                              a tile holds 2^(in_row_log2 + out_row_log2) = 2^(2t) units */
+    int32_t threads_log2; /* TILED: log2 threads that move one tile (the thread bits of
+                             the chunk index c = (j << threads_log2) | tid) */
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */
@@ -248,7 +253,8 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * tiles per loader wave) and the block order (bmmc_plan_options.block_map 5,
  * the planner's, 1, 3 and 6, and the random orders 8 and 9), plus
  * rectangular tiles (tile_skew 1, -1, 2 and -2 at the larger side, orders 5,
- * 6 and 3): up to 72 candidates.  An option the caller fixed at plan
+ * 6 and 3) and 512 threads per tile (skew 0, 1 and -1 at the larger side on
+ * every launch style, orders 5 and 6): up to 90 candidates.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events; the candidate with the

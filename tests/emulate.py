@@ -25,11 +25,15 @@ def _xor_table(vals: np.ndarray, table, nbits: int) -> np.ndarray:
     return acc
 
 
-def tiled_geometry(unit_log2: int, t: int):
+def tiled_geometry(unit_log2: int, t: int, threads_log2: int):
+    """Chunk width, chunks per row, thread and pass bits of a tile; the
+    threads are the pass descriptor's threads_log2 (at most the chunk count)."""
     wl = min(4 - unit_log2, t)
     cpsl = t - wl
     chl = 2 * t - wl
-    ntl = min(8, chl)
+    if not 1 <= threads_log2 <= chl:
+        raise ReplayError("threads_log2 %d does not fit a tile of 2^%d chunks" % (threads_log2, chl))
+    ntl = threads_log2
     rppl = ntl - cpsl
     jl = t - rppl
     return dict(wl=wl, cpsl=cpsl, ntl=ntl, rppl=rppl, jl=jl)
@@ -75,7 +79,7 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     """Source unit index of each output unit for one TILED pass."""
     ul, t, nb = d.unit_log2, d.t, d.nbits
     U = 1 << ul
-    g = tiled_geometry(ul, t)
+    g = tiled_geometry(ul, t, d.threads_log2)
     wl, cpsl, ntl, jl = g["wl"], g["cpsl"], g["ntl"], g["jl"]
     W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
     cbits = ntl + jl
@@ -248,7 +252,7 @@ def bank_cycles(addr, nbytes: int, banks: int) -> int:
 
 def tiled_read_addresses(d):
     """LDS byte addresses of wave 0's first output-order read (unit 0)."""
-    g = tiled_geometry(d.unit_log2, d.t)
+    g = tiled_geometry(d.unit_log2, d.t, d.threads_log2)
     lane_bits = min(6, g["ntl"])
     out = []
     for l in range(1 << lane_bits):
@@ -261,7 +265,7 @@ def tiled_read_addresses(d):
 
 
 def tiled_write_addresses(d):
-    g = tiled_geometry(d.unit_log2, d.t)
+    g = tiled_geometry(d.unit_log2, d.t, d.threads_log2)
     lane_bits = min(6, g["ntl"])
     out = []
     for l in range(1 << lane_bits):
@@ -321,7 +325,7 @@ def check_pass_sampled(d, A, c, elem_log2: int, blocks, map_indices) -> int:
         raise ReplayError("no sampled replay for kernel %d" % d.kernel)
 
     t = d.t
-    g = tiled_geometry(ul, t)
+    g = tiled_geometry(ul, t, d.threads_log2)
     wl, ntl, jl = g["wl"], g["ntl"], g["jl"]
     W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
     cbits = ntl + jl

@@ -131,6 +131,8 @@ def cases():
         if rng.random() < 0.15:
             opts["no_swizzle"] = 1
         skew = int(rng.choice([1, -1, 2, -2, 3, -3]))
+        if rng.random() < 0.4:
+            opts["tile_threads_log2"] = 9
         case = Case(N_SQUARE + i, kind, n, elem, int(rng.integers(1, 1 << 30)), opts)
         A, c = case.matrix()
         while skew:

@@ -435,11 +435,18 @@ def test_replay_detects_planted_table_errors():
                                            ("bpc", 27, 16, 0), ("bitrev", 28, 4, 0),
                                            ("bitrev", 28, 4, 1), ("bitrev", 28, 4, -1),
                                            ("general", 30, 4, 1), ("bpc", 27, 16, 1),
-                                           ("transpose", 24, 4, -1)])
+                                           ("transpose", 24, 4, -1), ("bitrev", 28, 4, 9),
+                                           ("general", 30, 4, 9), ("bpc", 27, 16, 9)])
 def test_swizzle_makes_reads_conflict_free(kind, n, e, skew):
+    """skew 9 stands for 512 threads per tile (square tiles)."""
     A, c = _matrix(kind, n, 7)
-    P = bm.Plan(n, A, c, e, **(dict(tile_skew=skew, tile_log2=7 if e == 4 else 6)
-                               if skew else {}))
+    kw = {}
+    if skew:
+        kw = dict(tile_log2=7 if e == 4 else 6)
+        kw.update(dict(tile_threads_log2=9) if skew == 9 else dict(tile_skew=skew))
+    P = bm.Plan(n, A, c, e, **kw)
+    if skew == 9:
+        assert P.passes()[-1].threads_log2 == 9
     d = P.passes()[-1]
     assert d.kernel == bm.KERNEL_TILED
     U = 1 << d.unit_log2
@@ -547,6 +554,8 @@ MAX_CASES = [  # (n, elem_bytes, kind, plan options): up to 2^36 bytes per array
     (32, 16, "general", dict(tile_log2=2, launch=bm.LAUNCH_ONE_TILE)),
     (32, 4, "bitrev", dict(tile_log2=7, tile_skew=1)),
     (32, 8, "general", dict(tile_skew=-1, launch=bm.LAUNCH_PERSISTENT)),
+    (32, 4, "bitrev", dict(tile_log2=7, tile_threads_log2=9, launch=bm.LAUNCH_STREAMED)),
+    (32, 16, "general", dict(tile_threads_log2=9, launch=bm.LAUNCH_ONE_TILE)),
 ]
 
 
@@ -628,6 +637,8 @@ def _desc_bytes(d):
     ("complement", 12, 4, {}), ("general", 30, 4, dict(cache_hint=1)),
     ("bitrev", 28, 4, dict(tile_log2=7, tile_skew=1)), ("general", 24, 4, dict(tile_skew=-2)),
     ("bpc", 27, 16, dict(tile_skew=1, launch=bm.LAUNCH_PERSISTENT)),
+    ("bitrev", 28, 4, dict(tile_log2=7, tile_threads_log2=9, launch=bm.LAUNCH_STREAMED)),
+    ("general", 20, 4, dict(tile_threads_log2=9, tile_skew=1)),
 ], ids=lambda c: "%s-n%d-e%d-%s" % (c[0], c[1], c[2],
                                     "-".join("%s%s" % kv for kv in sorted(c[3].items()))))
 def test_options_rebuild_the_same_tables(case):
@@ -660,9 +671,11 @@ def test_options_rebuild_the_same_tables(case):
 # Rectangular tiles (tile_skew)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,skew", [("c3", 1), ("c3", -1), ("c4", 1), ("c4", -1), ("c2", 1),
-                                       ("c5", 1), ("c5", -1)])
-def test_skewed_tiles_at_workload_size(name, skew):
+@pytest.mark.parametrize("name,skew,threads", [("c3", 1, 8), ("c3", -1, 8), ("c4", 1, 8),
+                                               ("c4", -1, 8), ("c2", 1, 8), ("c5", 1, 8),
+                                               ("c5", -1, 8), ("c3", 0, 9), ("c3", 1, 9),
+                                               ("c4", 0, 9), ("c5", -1, 9)])
+def test_skewed_tiles_at_workload_size(name, skew, threads):
     """A skewed tile keeps the square tile's 2^(2t) units with input rows of
     2^(t - s) units and output rows of 2^(t + s); at the workloads' full
     sizes, sampled tiles replay to the oracle's map (range, exactly-once and
@@ -670,10 +683,11 @@ def test_skewed_tiles_at_workload_size(name, skew):
     w = wl.WORKLOADS[name]
     A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n)
     t = 7 if w.elem_bytes == 4 else 6
-    P = bm.Plan(w.n, A, c, w.elem_bytes, tile_log2=t, tile_skew=skew)
+    P = bm.Plan(w.n, A, c, w.elem_bytes, tile_log2=t, tile_skew=skew, tile_threads_log2=threads)
     assert P.info.passes == 1
     d = P.passes()[0]
     assert (d.t, d.in_row_log2, d.out_row_log2) == (t, t - skew, t + skew)
+    assert d.threads_log2 == threads and P.describe()["tile_threads"] == 1 << threads
     assert P.describe()["tile_skew"] == skew and P.options()["tile_skew"] == skew
     checked = check_pass_sampled(d, *P.factors()[0], w.elem_bytes.bit_length() - 1,
                                  _sampled_blocks(1 << d.blk_bits, 77), oracle.map_indices)
@@ -707,7 +721,7 @@ def test_tune_candidates_rebuild_distinct_plans():
         A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n)
         P = bm.Plan(w.n, A, c, w.elem_bytes)
         cands = bm.bmmc_plan_tune_candidates(P.handle)
-        assert 20 <= len(cands) <= 72
+        assert 20 <= len(cands) <= 90
         digests = set()
         for k, o in enumerate(cands):
             Q = bm.Plan(w.n, A, c, w.elem_bytes, **o)
@@ -717,5 +731,20 @@ def test_tune_candidates_rebuild_distinct_plans():
                 assert [_desc_bytes(d) for d in Q.passes()] == [_desc_bytes(d) for d in P.passes()]
         assert len(digests) == len(cands)
         assert {o["tile_skew"] for o in cands} >= {0, 1, -1, 2, -2}
+        assert {o["tile_threads_log2"] for o in cands} == {8, 9}
     R = bm.Plan(12, wl.identity_matrix(12), 5, 4)
     assert bm.bmmc_plan_tune_candidates(R.handle) == []
+
+
+def test_thread_count_option_errors():
+    A = wl.bit_reverse_matrix(20)
+    with pytest.raises(bm.BmmcError):
+        bm.Plan(20, A, 0, 4, tile_threads_log2=10)
+    # the wide kernels exist for one tile per workgroup only, not the
+    # iterated variant
+    with pytest.raises(bm.BmmcError):
+        bm.Plan(20, A, 0, 4, tile_log2=7, tile_threads_log2=9, launch=bm.LAUNCH_ONE_TILE,
+                iters_log2=1)
+    # tiles of at most 256 chunks use one thread per chunk whatever is asked
+    P = bm.Plan(20, A, 0, 4, tile_log2=4, tile_threads_log2=9)
+    assert P.passes()[0].threads_log2 == 2 * 4 - 2

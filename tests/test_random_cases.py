@@ -18,7 +18,7 @@ def test_cases_are_fixed_and_span_the_options():
     assert len(a) == N_CASES
     seen = {k for c in a for k in c.options}
     assert {"route", "launch", "tile_log2", "block_map", "iters_log2", "grid_log2", "walk",
-            "depth", "cache_hint", "no_swizzle", "tile_skew"} <= seen
+            "depth", "cache_hint", "no_swizzle", "tile_skew", "tile_threads_log2"} <= seen
     skews = {c.options.get("tile_skew", 0) for c in a}
     assert {1, -1, 2, -2} <= skews
     assert {c.kind for c in a} == {"general", "bpc", "bitrev", "transpose", "complement",
