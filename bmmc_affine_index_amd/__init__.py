@@ -388,6 +388,12 @@ class Plan:
         (bmmc_plan_get_options): ``Plan(n, A, c, elem_bytes, **p.options())``."""
         return bmmc_plan_get_options(self.handle)
 
+    def tune_candidates(self) -> list:
+        """Options of every plan ``tune`` would time, in order
+        (bmmc_plan_tune_candidates); each rebuilds with
+        ``Plan(n, A, c, elem_bytes, **opts)``."""
+        return bmmc_plan_tune_candidates(self.handle)
+
     def passes(self):
         return [bmmc_plan_get_pass(self.handle, k) for k in range(self.info.passes)]
 

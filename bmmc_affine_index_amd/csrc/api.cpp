@@ -176,9 +176,10 @@ int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> 
                 }
     // 512 threads per tile at the larger side (twice the waves per SIMD to
     // hide the latency between a tile's loads and its stores), square and
-    // with the output rows twice or half as long, on every launch style
+    // with the output rows 2 or 4 times as long or as short, on every launch
+    // style (the slowest random 16-byte BPC: +1% at 4 times)
     if (!p->opt.tile_threads_log2 && p->opt.iters_log2 == 0)
-        for (int skew : {0, 1, -1})
+        for (int skew : {0, 1, -1, 2, -2})
             for (int l : {BMMC_LAUNCH_AUTO, BMMC_LAUNCH_ONE_TILE, BMMC_LAUNCH_STREAMED})
                 for (int m : {bmmc::kDefaultBlockMap, 6}) {
                     if ((p->opt.launch && l != p->opt.launch) ||

@@ -253,8 +253,9 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * tiles per loader wave) and the block order (bmmc_plan_options.block_map 5,
  * the planner's, 1, 3 and 6, and the random orders 8 and 9), plus
  * rectangular tiles (tile_skew 1, -1, 2 and -2 at the larger side, orders 5,
- * 6 and 3) and 512 threads per tile (skew 0, 1 and -1 at the larger side on
- * every launch style, orders 5 and 6): up to 90 candidates.  An option the caller fixed at plan
+ * 6 and 3) and 512 threads per tile (skew 0, 1, -1, 2 and -2 at the larger
+ * side on every launch style, orders 5 and 6): up to 102 candidates, fewer
+ * where two build the same tables.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events; the candidate with the

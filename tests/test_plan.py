@@ -721,6 +721,7 @@ def test_tune_candidates_rebuild_distinct_plans():
         A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n)
         P = bm.Plan(w.n, A, c, w.elem_bytes)
         cands = bm.bmmc_plan_tune_candidates(P.handle)
+        assert P.tune_candidates() == cands
         assert 20 <= len(cands) <= 90
         digests = set()
         for k, o in enumerate(cands):
