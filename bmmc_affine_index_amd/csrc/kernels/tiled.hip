@@ -101,24 +101,25 @@ __device__ __forceinline__ void load_tile_jo(dev::Chunk<C::CB> (&v)[C::J], const
     for (int j = 0; j < C::J; ++j) v[j] = dev::gload_nt<C::CB, NT>(in + ((in_base ^ jo[j]) ^ p.in_lane));
 }
 
-// Write the tile's chunks to LDS through the swizzle.
-template <class C, int T>
+// Write the tile's chunks of passes J0 .. JN-1 to LDS through the swizzle.
+template <class C, int T, int J0 = 0, int JN = C::J>
 __device__ __forceinline__ void stage_tile(uint8_t *tile_lds, const dev::Chunk<C::CB> (&v)[C::J],
                                            const bmmc_pass_desc &d, const LaneParts &p) {
 #pragma unroll
-    for (int j = 0; j < C::J; ++j) {
+    for (int j = J0; j < JN; ++j) {
         const uint32_t wr_j = dev::xor_bits_lane<C::JL>(d.ld_lds + C::NTL, (uint32_t)j);
         dev::lds_store<C::CB>(tile_lds + (wr_j ^ p.wr_lane), v[j]);
     }
 }
 
-// Read the tile back in output order and store whole output chunks.
-template <class C, int T, bool NT>
+// Read the tile back in output order and store whole output chunks (drain
+// passes J0 .. JN-1).
+template <class C, int T, bool NT, int J0 = 0, int JN = C::J>
 __device__ __forceinline__ void drain_tile(uint8_t *out, const uint8_t *tile_lds, uint64_t obase,
                                            uint32_t rbase, const bmmc_pass_desc &d,
                                            const LaneParts &p) {
 #pragma unroll
-    for (int j = 0; j < C::J; ++j) {
+    for (int j = J0; j < JN; ++j) {
         const uint64_t out_j =
             obase ^ dev::xor_bits_lane<C::JL>(d.st_out + C::NTL, (uint32_t)j);
         const uint32_t rd_j =
@@ -164,6 +165,38 @@ __global__ void __launch_bounds__((TiledCfg<UL, T, IT, TL>::NT))
         drain_tile<C, T, NT>(out, lds + s * C::TILE, tile_base<C>(d.out_blk, blk) ^ d.out_c,
                              tile_base<C>(d.lds_blk, blk) ^ d.lds_c, d, p);
     }
+}
+
+// One workgroup per tile, staged in LDS half at a time.  The planner builds
+// the tables so that the chunks of passes j < J/2 hold one half of the tile's
+// units on the load side and on the drain side alike (each tile's drain base
+// already picks the matching half), and the LDS offsets of either half cover
+// half a tile.  With half the LDS per workgroup, twice the tiles hold LDS on a
+// compute unit at once, each with all its loads issued up front; the second
+// half's staging waits only for its own loads and for the barrier after the
+// first half's reads.
+template <int UL, int T, bool NT, int TL>
+__global__ void __launch_bounds__((TiledCfg<UL, T, 0, TL>::NT))
+    bmmc_tiled_split_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
+                            const bmmc_pass_desc d, uint64_t blk0) {
+    using C = TiledCfg<UL, T, 0, TL>;
+    static_assert(C::J >= 2, "two passes per tile at least");
+    constexpr int H = C::J / 2;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::TILE / 2];
+    const LaneParts p = lane_parts<C, T>(d, threadIdx.x);
+    const uint64_t blk = blk0 + blockIdx.x;
+
+    dev::Chunk<C::CB> v[C::J];
+    load_tile<C, T, NT>(v, in, tile_base<C>(d.in_blk, blk), d, p);
+    stage_tile<C, T, 0, H>(lds, v, d, p);
+    __syncthreads();
+    const uint64_t obase = tile_base<C>(d.out_blk, blk) ^ d.out_c;
+    const uint32_t rbase = tile_base<C>(d.lds_blk, blk) ^ d.lds_c;
+    drain_tile<C, T, NT, 0, H>(out, lds, obase, rbase, d, p);
+    __syncthreads();  // every read of the first half is done before it is overwritten
+    stage_tile<C, T, H, C::J>(lds, v, d, p);
+    __syncthreads();
+    drain_tile<C, T, NT, H, C::J>(out, lds, obase, rbase, d, p);
 }
 
 // Persistent: 2^grid_log2 workgroups; workgroup w, as walker v =
@@ -439,6 +472,20 @@ template <int UL, int T, int IT, bool NT, int TL> int launch_nt(const TiledArgs 
             return BMMC_ERR_UNSUPPORTED;
         }
     }
+    if (a.d->split_stage) {
+        if constexpr (IT == 0 && C::J >= 2) {
+            const uint64_t blocks = uint64_t(1) << a.d->blk_bits;
+            const uint64_t per = max_blocks_per_launch(C::NT);
+            for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
+                const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
+                hipLaunchKernelGGL((bmmc_tiled_split_kernel<UL, T, NT, TL>), dim3((uint32_t)nb),
+                                   dim3(C::NT), 0, a.s, a.in, a.out, *a.d, b0);
+            }
+            return hipGetLastError() == hipSuccess ? BMMC_OK : BMMC_ERR_HIP;
+        } else {
+            return BMMC_ERR_UNSUPPORTED;
+        }
+    }
     const uint64_t blocks = uint64_t(1) << (a.d->blk_bits - IT);
     const uint64_t per = max_blocks_per_launch(C::NT);
     for (uint64_t b0 = 0; b0 < blocks; b0 += per) {
@@ -496,6 +543,9 @@ int launch_tiled(const bmmc_pass_desc &d, const void *in, void *out, hipStream_t
         d.walk != BMMC_WALK_INTERLEAVED)
         return BMMC_ERR_INVALID_ARG;
     if (d.cache_hint != 0 && d.cache_hint != 3) return BMMC_ERR_UNSUPPORTED;
+    if (d.split_stage != 0 &&
+        (d.split_stage != 1 || d.launch != BMMC_LAUNCH_ONE_TILE || d.iters_log2 != 0))
+        return BMMC_ERR_INVALID_ARG;
     TiledArgs a{&d, static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), s};
     return dispatch<0, 1, 0>(d.unit_log2, d.t, d.iters_log2, &a);
 }

@@ -29,7 +29,8 @@ int noalloc_scratch(void **out);
 
 // Whether the tile kernel is compiled for this unit size, side, iteration
 // count, launch style and thread count.
-bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2);
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2,
+                     int split_stage);
 
 // The dispatch packet gives the grid size in work-items as a 32-bit count,
 // so one launch covers at most 2^31 work-items here; bigger passes are split

@@ -248,6 +248,7 @@ struct LaunchChoice {
     bool auto_launch;  // launch style left to the planner
     int cache_hint;    // descriptor value: 3 non-temporal loads and stores, 0 plain
     int threads_log2;  // most threads per tile, log2 (8 or 9)
+    bool split;        // one-tile launch staging each tile in LDS half at a time
 };
 
 // Highest set bit of a byte offset (-1 for 0).
@@ -445,11 +446,14 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
     };
     const int ideal = 8 * ideal_cycles(rbytes, 32) + 2 * ideal_cycles(rbytes, 64) +
                       ideal_cycles(wbytes, 32) + ideal_cycles(wbytes, 64);
-    auto cost = [&](const std::vector<u64> &rv, const std::vector<u64> &Sx) {
+    std::vector<u64> lvec(cbits);  // local input vector of each load position
+    for (int p = 0; p < cbits; ++p) lvec[p] = load_local(p);
+    auto cost_lv = [&](const std::vector<u64> &lv, const std::vector<u64> &rv,
+                       const std::vector<u64> &Sx) {
         uint32_t wa[64], ra[64];
         uint32_t wcol[6], rcol[6];
         for (int p = 0; p < lane_bits; ++p) {
-            wcol[p] = (uint32_t)(slot(load_local(p), Sx) << ulog2);
+            wcol[p] = (uint32_t)(slot(lv[p], Sx) << ulog2);
             rcol[p] = (uint32_t)(slot(rv[p], Sx) << ulog2);
         }
         for (int l = 0; l < lanes; ++l) {
@@ -461,6 +465,9 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
         }
         return 8 * bank_cycles(ra, lanes, rbytes, 32) + 2 * bank_cycles(ra, lanes, rbytes, 64) +
                bank_cycles(wa, lanes, wbytes, 32) + bank_cycles(wa, lanes, wbytes, 64);
+    };
+    auto cost = [&](const std::vector<u64> &rv, const std::vector<u64> &Sx) {
+        return cost_lv(lvec, rv, Sx);
     };
 
     // Drain-phase lane layout: the first `pc` thread bits stay on the low
@@ -554,7 +561,107 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
             S = best_S;
         }
     }
-    const std::vector<u64> rvec = read_vecs(rpos);
+    std::vector<u64> rvec = read_vecs(rpos), ovec(cbits);
+    for (int p = 0; p < cbits; ++p) ovec[p] = drain_local(rpos[p]);
+
+    // Split staging: the tile passes through LDS in two halves.  A linear
+    // functional g of the local input coordinates names the half of every
+    // unit; the tables are rebased so that g of a chunk is the top bit of its
+    // chunk index on both sides (for the drain, after a per-tile flip folded
+    // into the block tables), and the LDS slot drops one address bit on which
+    // g is 1, so each half fits half the LDS.  g must be 0 on the units of a
+    // chunk (on both sides), on the in-row load positions (each half still
+    // reads whole input rows) and on the drain's 128-byte lane groups.
+    const int top = cbits - 1;
+    u64 gmask = 0;   // g(x) = parity(gmask & x)
+    int qdrop = -1;  // LDS slot bit dropped
+    auto par = [](u64 m, u64 x) { return (int)__builtin_parityll(m & x); };
+    if (lc.split) {
+        if (top < g.ntl) return BMMC_ERR_INVALID_ARG;  // one pass per tile: nothing to split
+        Basis keep;
+        for (int u = 0; u < g.wl; ++u) {
+            keep.add(u64(1) << u);
+            keep.add(Minv.apply(u64(1) << u));
+        }
+        for (int p = 0; p < cpsl_in; ++p) keep.add(lvec[p]);
+        for (int p = 0; p < pc; ++p) keep.add(rvec[p]);
+        // functionals vanishing on `keep`: one per free coordinate f, e_f plus
+        // the pivots of the (fully reduced) kept vectors that have bit f
+        std::vector<u64> ns;
+        const u64 piv = keep.pivot_mask();
+        for (int f = 0; f < K; ++f) {
+            if ((piv >> f) & 1u) continue;
+            u64 gv = u64(1) << f;
+            for (int k = 0; k < keep.size(); ++k)
+                if ((keep.vec[k] >> f) & 1u) gv |= u64(1) << keep.pivot[k];
+            ns.push_back(gv);
+        }
+        // slot^-1 of each LDS address bit
+        Mat SL = Mat::zeros(K, K);
+        for (int i = 0; i < K; ++i) SL.set_col(i, slot(u64(1) << i, S));
+        Mat SLinv;
+        if (!inverse(SL, SLinv)) return BMMC_ERR_INVALID_ARG;
+        // dropped bits stay above the 256 bytes of one row of LDS banks, so
+        // the lanes of an access keep their banks
+        const int qmin = std::max(0, 8 - ulog2);
+        int best = 1 << 30, best_lt = -1, best_dt = -1;
+        const int ncomb = ns.size() > 12 ? 1 << 12 : 1 << ns.size();
+        for (int comb = 1; comb < ncomb; ++comb) {
+            u64 gm = 0;
+            for (size_t k = 0; k < ns.size(); ++k)
+                if ((comb >> k) & 1) gm ^= ns[k];
+            int q = -1;
+            for (int bq = K - 1; bq >= qmin && q < 0; --bq)
+                if (par(gm, SLinv.apply(u64(1) << bq))) q = bq;
+            // the positions that become the top one: the highest on which g
+            // is 1 (a pass bit where there is one, else a thread bit; g is 0
+            // on the positions that must keep their place)
+            int lt = -1, dt = -1;
+            for (int p = top; p >= 0 && lt < 0; --p)
+                if (par(gm, lvec[p])) lt = p;
+            for (int p = top; p >= 0 && dt < 0; --p)
+                if (par(gm, rvec[p])) dt = p;
+            if (q < 0 || lt < 0 || dt < 0) continue;
+            std::vector<u64> L = lvec, R = rvec;
+            std::swap(L[lt], L[top]);
+            std::swap(R[dt], R[top]);
+            for (int p = 0; p < top; ++p) {
+                if (par(gm, L[p])) L[p] ^= L[top];
+                if (par(gm, R[p])) R[p] ^= R[top];
+            }
+            const int cc = cost_lv(L, R, S);
+            if (cc < best) {
+                best = cc;
+                gmask = gm;
+                qdrop = q;
+                best_lt = lt;
+                best_dt = dt;
+            }
+        }
+        if (qdrop < 0) return BMMC_ERR_INVALID_ARG;
+        std::swap(lvec[best_lt], lvec[top]);
+        std::swap(rvec[best_dt], rvec[top]);
+        std::swap(ovec[best_dt], ovec[top]);
+        for (int p = 0; p < top; ++p) {
+            if (par(gmask, lvec[p])) lvec[p] ^= lvec[top];
+            if (par(gmask, rvec[p])) {
+                rvec[p] ^= rvec[top];
+                ovec[p] ^= ovec[top];
+            }
+        }
+    }
+    // byte offset in LDS of a slot (the dropped bit removed when split)
+    auto lds_off = [&](u64 sl) -> uint32_t {
+        if (qdrop >= 0) sl = (sl & low_mask(qdrop)) | ((sl >> (qdrop + 1)) << qdrop);
+        return (uint32_t)(sl << ulog2);
+    };
+    // output offset (units) of a local output vector: in-row part plus rows
+    auto out_local_of = [&](u64 ov) {
+        u64 o = ov & lo_b;
+        for (int k = 0; k < a; ++k)
+            if (((ov >> b) >> k) & 1u) o ^= gb.vec[k];
+        return o;
+    };
 
     std::memset(d, 0, sizeof(*d));
     d->kernel = BMMC_KERNEL_TILED;
@@ -594,7 +701,13 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
         d->launch = BMMC_LAUNCH_ONE_TILE;
         d->iters_log2 = iters_log2;
         d->lds_bytes = (uint32_t)(tile_bytes << iters_log2);
+        if (lc.split) {
+            if (iters_log2) return BMMC_ERR_INVALID_ARG;
+            d->split_stage = 1;
+            d->lds_bytes = (uint32_t)(tile_bytes / 2);
+        }
     }
+    if (lc.split && d->launch != BMMC_LAUNCH_ONE_TILE) return BMMC_ERR_INVALID_ARG;
     Basis vb, avb;  // the tile's span on the input side and on the output side
     for (int j = 0; j < a; ++j) vb.add(u64(1) << j);
     for (int j = 0; j < b; ++j) avb.add(u64(1) << j);
@@ -606,15 +719,27 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
     const std::vector<u64> X =
         block_basis(A, Binv, std::min(a, b), vb, avb, R, lc.block_map,
                     range_walk ? d->grid_log2 : 0);
+    // A tile's drain base is the local input vector of its in-row output
+    // offset; where g is 1 on it, the split drain takes the halves in the
+    // other order (the top drain position is XORed into the base), so that
+    // drain half h again reads the units staged in half h.
+    auto drain_base = [&](u64 zlo, u64 zhi, uint64_t &out_b, uint32_t &lds_b) {
+        u64 x = Minv.apply(zlo), o = zhi;
+        if (par(gmask, x)) {
+            x ^= rvec[top];
+            o ^= out_local_of(ovec[top]);
+        }
+        out_b = o << ulog2;
+        lds_b = lds_off(slot(x, S));
+    };
     for (int k = 0; k < blk_bits; ++k) {
         const u64 x = X[k];
         const u64 z = A.apply(x);
         d->in_blk[k] = x << ulog2;
-        d->out_blk[k] = (z & ~lo_b) << ulog2;
-        d->lds_blk[k] = (uint32_t)(slot(Minv.apply(z & lo_b), S) << ulog2);
+        drain_base(z & lo_b, z & ~lo_b, d->out_blk[k], d->lds_blk[k]);
     }
     for (int p = 0; p < cbits; ++p) {
-        const u64 lv = load_local(p);
+        const u64 lv = lvec[p];
         const u64 in_local = (lv & lo_a) | [&] {
             u64 h = lv >> a, off = 0;
             for (int k = 0; k < b; ++k)
@@ -622,18 +747,12 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
             return off;
         }();
         d->ld_in[p] = in_local << ulog2;
-        d->ld_lds[p] = (uint32_t)(slot(lv, S) << ulog2);
-        const u64 ov = drain_local(rpos[p]);
-        u64 out_local = ov & lo_b;
-        for (int k = 0; k < a; ++k)
-            if (((ov >> b) >> k) & 1u) out_local ^= gb.vec[k];
-        d->st_out[p] = out_local << ulog2;
-        d->st_lds[p] = (uint32_t)(slot(rvec[p], S) << ulog2);
+        d->ld_lds[p] = lds_off(slot(lv, S));
+        d->st_out[p] = out_local_of(ovec[p]) << ulog2;
+        d->st_lds[p] = lds_off(slot(rvec[p], S));
     }
-    for (int u = 0; u < g.wl; ++u)
-        d->st_unit[u] = (uint32_t)(slot(Minv.apply(u64(1) << u), S) << ulog2);
-    d->out_c = (c & ~lo_b) << ulog2;
-    d->lds_c = (uint32_t)(slot(Minv.apply(c & lo_b), S) << ulog2);
+    for (int u = 0; u < g.wl; ++u) d->st_unit[u] = lds_off(slot(Minv.apply(u64(1) << u), S));
+    drain_base(c & lo_b, c & ~lo_b, d->out_c, d->lds_c);
     d->cache_hint = lc.cache_hint;
     d->block_map = lc.block_map;
     remap_blocks(d, lc.block_map);
@@ -727,6 +846,13 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
     // Below 256 chunks per tile the count is the chunk count either way.
     lc.threads_log2 = o.tile_threads_log2 ? std::max(o.tile_threads_log2, kTileMaxNTL)
                                           : kTileMaxNTL;
+    // Split staging is a form of the one-tile launch.
+    if (o.split_stage < 0 || o.split_stage > 1) return BMMC_ERR_INVALID_ARG;
+    if (o.split_stage && (o.launch == BMMC_LAUNCH_PERSISTENT ||
+                          o.launch == BMMC_LAUNCH_STREAMED || o.iters_log2 != 0))
+        return BMMC_ERR_INVALID_ARG;
+    lc.split = o.split_stage == 1;
+    if (lc.split) lc.persistent = 0;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);

@@ -4,8 +4,13 @@
 
 namespace bmmc {
 
-bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2) {
+bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2,
+                     int split_stage) {
     if (unit_log2 < 0 || unit_log2 > 4 || t < 1) return false;
+    // split staging: one tile per workgroup, at least two passes per tile
+    if (split_stage && (split_stage != 1 || launch != BMMC_LAUNCH_ONE_TILE || iters_log2 != 0 ||
+                        2 * t - ((4 - unit_log2) < t ? (4 - unit_log2) : t) - threads_log2 < 1))
+        return false;
     // the 256-thread kernels, and the 512-thread ones where a tile has more
     // than 256 chunks and one tile per workgroup
     const int narrow = tile_threads_log2(unit_log2, t, kTileMaxNTL);

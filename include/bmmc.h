@@ -101,6 +101,12 @@ typedef struct bmmc_plan_options {
     int tile_threads_log2; /* tile pass: log2 of the most threads that move one tile,
                               8 (256) or 9 (512); 0 = planner's choice (8).  Tiles of
                               fewer chunks use one thread per chunk. */
+    int split_stage; /* tile pass, one-tile launch only: 1 = stage each tile in LDS half
+                        at a time (half the LDS per workgroup, so twice the tiles can
+                        hold LDS on a compute unit); 0 = planner's choice (whole tiles).
+                        Not every matrix admits it at every tile shape
+                        (BMMC_ERR_INVALID_ARG then); launch must be AUTO or ONE_TILE
+                        and iters_log2 0. */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */
@@ -196,6 +202,10 @@ typedef struct bmmc_pass_desc {
                              a tile holds 2^(in_row_log2 + out_row_log2) = 2^(2t) units */
     int32_t threads_log2; /* TILED: log2 threads that move one tile (the thread bits of
                              the chunk index c = (j << threads_log2) | tid) */
+    int32_t split_stage;  /* TILED, one-tile launch: 1 = the tile passes through LDS in
+                             two halves, the chunks whose top chunk-index bit is h in
+                             half h, on both the load and the drain side; lds_bytes is
+                             then half a tile */
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */
@@ -253,9 +263,11 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * tiles per loader wave) and the block order (bmmc_plan_options.block_map 5,
  * the planner's, 1, 3 and 6, and the random orders 8 and 9), plus
  * rectangular tiles (tile_skew 1, -1, 2 and -2 at the larger side, orders 5,
- * 6 and 3) and 512 threads per tile (skew 0, 1, -1, 2 and -2 at the larger
- * side on every launch style, orders 5 and 6): up to 102 candidates, fewer
- * where two build the same tables.  An option the caller fixed at plan
+ * 6 and 3), 512 threads per tile (skew 0, 1, -1, 2 and -2 at the larger
+ * side on every launch style, orders 5 and 6) and tiles staged in LDS half at
+ * a time (split_stage; skew 0, 1, -1 and 2, 256 and 512 threads, order 5,
+ * where the matrix admits them): up to 110 candidates, fewer where two build
+ * the same tables.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events; the candidate with the

@@ -86,10 +86,18 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     TILE = U << (2 * t)
     blk_bits = d.blk_bits
     nblk = 1 << blk_bits
+    split = int(getattr(d, "split_stage", 0))
+    if split not in (0, 1):
+        raise ReplayError("split_stage must be 0 or 1")
     if d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED):
         if d.lds_bytes != 2 * TILE or d.iters_log2 != 0:
             raise ReplayError("persistent launch needs two LDS tiles")
+        if split:
+            raise ReplayError("split staging is a one-tile launch")
         check_persistent_walk(d)
+    elif split:
+        if d.iters_log2 != 0 or 2 * d.lds_bytes != TILE or jl < 1:
+            raise ReplayError("split staging needs half a tile of LDS and two passes")
     elif d.lds_bytes != TILE << d.iters_log2:
         raise ReplayError("lds_bytes does not match the tile geometry")
     total_units = 1 << nb
@@ -100,28 +108,14 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     in_off = _xor_table(b, d.in_blk, blk_bits) ^ _xor_table(cidx, d.ld_in, cbits)
     wr = _xor_table(cidx, d.ld_lds, cbits)
     in_off, wr = np.broadcast_arrays(in_off, wr)
+    # LDS bytes one staging uses: the tile, or half of it when split
+    LT = TILE >> split
     if np.any(in_off % np.uint64(CB)) or np.any(wr % np.uint64(CB)):
         raise ReplayError("misaligned chunk")
-    if np.any(wr + np.uint64(CB) > np.uint64(TILE)):
+    if np.any(wr + np.uint64(CB) > np.uint64(LT)):
         raise ReplayError("LDS write out of range")
     if np.any(in_off + np.uint64(CB) > np.uint64(total_units * U)):
         raise ReplayError("global read out of range")
-
-    # LDS of every block, holding source unit indices
-    lds = np.full((nblk, TILE // U), -1, dtype=np.int64)
-    bidx = np.broadcast_to(np.arange(nblk)[:, None], in_off.shape)
-    for e in range(W):
-        slot = (wr // np.uint64(U) + np.uint64(e)).astype(np.int64)
-        src = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
-        if np.any(lds[bidx, slot] != -1):
-            raise ReplayError("LDS slot written twice")
-        lds[bidx, slot] = src
-    if np.any(lds < 0):
-        raise ReplayError("LDS slot never written")
-    read_in = np.zeros(total_units, dtype=np.int64)
-    np.add.at(read_in, lds.reshape(-1), 1)
-    if np.any(read_in != 1):
-        raise ReplayError("input unit not read exactly once")
 
     out_off = (_xor_table(b, d.out_blk, blk_bits) ^ np.uint64(d.out_c)
                ^ _xor_table(cidx, d.st_out, cbits))
@@ -132,20 +126,41 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
         raise ReplayError("misaligned output chunk")
     if np.any(out_off + np.uint64(CB) > np.uint64(total_units * U)):
         raise ReplayError("global write out of range")
+
+    # stagings: every chunk at once, or the chunks whose top chunk-index bit
+    # is h in half h (loads and drain alike)
+    allc = np.arange(NT * J)
+    stagings = [allc] if not split else [allc[((allc >> (cbits - 1)) & 1) == h] for h in (0, 1)]
+    read_in = np.zeros(total_units, dtype=np.int64)
     result = np.full(total_units, -1, dtype=np.int64)
-    reads = np.zeros((nblk, TILE // U), dtype=np.int64)
-    for e in range(W):
-        rd = rbase ^ _xor_table(np.uint64(e), d.st_unit, wl)
-        if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(TILE)):
-            raise ReplayError("LDS read misaligned or out of range")
-        slot = (rd // np.uint64(U)).astype(np.int64)
-        np.add.at(reads, (bidx, slot), 1)
-        dst = (out_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
-        if np.any(result[dst] != -1):
-            raise ReplayError("output unit written twice")
-        result[dst] = lds[bidx, slot]
-    if np.any(reads != 1):
-        raise ReplayError("LDS slot not read exactly once")
+    for cols in stagings:
+        # LDS of every block, holding source unit indices
+        lds = np.full((nblk, LT // U), -1, dtype=np.int64)
+        bidx = np.broadcast_to(np.arange(nblk)[:, None], (nblk, cols.size))
+        for e in range(W):
+            slot = (wr[:, cols] // np.uint64(U) + np.uint64(e)).astype(np.int64)
+            src = (in_off[:, cols] // np.uint64(U) + np.uint64(e)).astype(np.int64)
+            if np.any(lds[bidx, slot] != -1):
+                raise ReplayError("LDS slot written twice")
+            lds[bidx, slot] = src
+        if np.any(lds < 0):
+            raise ReplayError("LDS slot never written")
+        np.add.at(read_in, lds.reshape(-1), 1)
+        reads = np.zeros((nblk, LT // U), dtype=np.int64)
+        for e in range(W):
+            rd = rbase[:, cols] ^ _xor_table(np.uint64(e), d.st_unit, wl)
+            if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(LT)):
+                raise ReplayError("LDS read misaligned or out of range")
+            slot = (rd // np.uint64(U)).astype(np.int64)
+            np.add.at(reads, (bidx, slot), 1)
+            dst = (out_off[:, cols] // np.uint64(U) + np.uint64(e)).astype(np.int64)
+            if np.any(result[dst] != -1):
+                raise ReplayError("output unit written twice")
+            result[dst] = lds[bidx, slot]
+        if np.any(reads != 1):
+            raise ReplayError("LDS slot not read exactly once")
+    if np.any(read_in != 1):
+        raise ReplayError("input unit not read exactly once")
     if np.any(result < 0):
         raise ReplayError("output unit never written")
 
@@ -330,36 +345,46 @@ def check_pass_sampled(d, A, c, elem_log2: int, blocks, map_indices) -> int:
     W, CB, NT, J = 1 << wl, U << wl, 1 << ntl, 1 << jl
     cbits = ntl + jl
     TILE = U << (2 * t)
+    split = int(getattr(d, "split_stage", 0))
+    if split and (d.launch != LAUNCH_ONE_TILE or d.iters_log2 != 0 or 2 * d.lds_bytes != TILE
+                  or jl < 1):
+        raise ReplayError("split staging needs a one-tile launch, half a tile of LDS and two passes")
+    LT = TILE >> split  # LDS bytes of one staging
     cidx = np.arange(NT * J, dtype=np.uint64)
     ld_in = _xor_table(cidx, d.ld_in, cbits)
     ld_lds = _xor_table(cidx, d.ld_lds, cbits)
     st_out = _xor_table(cidx, d.st_out, cbits)
     st_lds = _xor_table(cidx, d.st_lds, cbits)
-    if np.any(ld_lds % np.uint64(CB)) or np.any(ld_lds + np.uint64(CB) > np.uint64(TILE)):
+    if np.any(ld_lds % np.uint64(CB)) or np.any(ld_lds + np.uint64(CB) > np.uint64(LT)):
         raise ReplayError("LDS write misaligned or out of range")
+    allc = np.arange(NT * J)
+    stagings = [allc] if not split else [allc[((allc >> (cbits - 1)) & 1) == h] for h in (0, 1)]
     for b in blocks:
-        in_off = _xor_table(b, d.in_blk, d.blk_bits) ^ ld_in
-        if np.any(in_off % np.uint64(CB)) or np.any(in_off + np.uint64(CB) > total_bytes):
+        in_off_all = _xor_table(b, d.in_blk, d.blk_bits) ^ ld_in
+        if np.any(in_off_all % np.uint64(CB)) or np.any(in_off_all + np.uint64(CB) > total_bytes):
             raise ReplayError("global read misaligned or out of range")
-        lds = np.full(TILE // U, -1, dtype=np.int64)
-        for e in range(W):
-            slot = (ld_lds // np.uint64(U) + np.uint64(e)).astype(np.int64)
-            if np.any(lds[slot] != -1):
-                raise ReplayError("LDS slot written twice")
-            lds[slot] = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
-        out_off = (_xor_table(b, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)) ^ st_out
-        rbase = (_xor_table(b, d.lds_blk, d.blk_bits) ^ np.uint64(d.lds_c)) ^ st_lds
-        if np.any(out_off % np.uint64(CB)) or np.any(out_off + np.uint64(CB) > total_bytes):
+        out_all = (_xor_table(b, d.out_blk, d.blk_bits) ^ np.uint64(d.out_c)) ^ st_out
+        rbase_all = (_xor_table(b, d.lds_blk, d.blk_bits) ^ np.uint64(d.lds_c)) ^ st_lds
+        if np.any(out_all % np.uint64(CB)) or np.any(out_all + np.uint64(CB) > total_bytes):
             raise ReplayError("global write misaligned or out of range")
-        reads = np.zeros(TILE // U, dtype=np.int64)
-        for e in range(W):
-            rd = rbase ^ _xor_table(np.uint64(e), d.st_unit, wl)
-            if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(TILE)):
-                raise ReplayError("LDS read misaligned or out of range")
-            slot = (rd // np.uint64(U)).astype(np.int64)
-            np.add.at(reads, slot, 1)
-            expect(lds[slot], out_off // np.uint64(U) + np.uint64(e))
-            checked += slot.size
-        if np.any(reads != 1) or np.any(lds < 0):
-            raise ReplayError("LDS slot not written and read exactly once")
+        for cols in stagings:
+            in_off, wr = in_off_all[cols], ld_lds[cols]
+            lds = np.full(LT // U, -1, dtype=np.int64)
+            for e in range(W):
+                slot = (wr // np.uint64(U) + np.uint64(e)).astype(np.int64)
+                if np.any(lds[slot] != -1):
+                    raise ReplayError("LDS slot written twice")
+                lds[slot] = (in_off // np.uint64(U) + np.uint64(e)).astype(np.int64)
+            out_off, rbase = out_all[cols], rbase_all[cols]
+            reads = np.zeros(LT // U, dtype=np.int64)
+            for e in range(W):
+                rd = rbase ^ _xor_table(np.uint64(e), d.st_unit, wl)
+                if np.any(rd % np.uint64(U)) or np.any(rd + np.uint64(U) > np.uint64(LT)):
+                    raise ReplayError("LDS read misaligned or out of range")
+                slot = (rd // np.uint64(U)).astype(np.int64)
+                np.add.at(reads, slot, 1)
+                expect(lds[slot], out_off // np.uint64(U) + np.uint64(e))
+                checked += slot.size
+            if np.any(reads != 1) or np.any(lds < 0):
+                raise ReplayError("LDS slot not written and read exactly once")
     return checked

@@ -20,9 +20,11 @@ KINDS = ("general", "bpc", "bitrev", "transpose", "complement", "blockperm", "lo
 ELEMS = (1, 2, 4, 8, 16)
 N_SQUARE = 600
 N_SKEW = 180   # rectangular tiles (tile_skew), drawn from a stream of their own
-N_CASES = N_SQUARE + N_SKEW
+N_SPLIT = 160  # one-tile launches staged in LDS half at a time (split_stage)
+N_CASES = N_SQUARE + N_SKEW + N_SPLIT
 MASTER_SEED = 0x5EED_B44C
 SKEW_SEED = 0x5EED_5CE7
+SPLIT_SEED = 0x5EED_5B17
 
 
 @dataclass
@@ -143,6 +145,50 @@ def cases():
                 skew -= 1 if skew > 0 else -1
         if skew:
             case.options["tile_skew"] = skew
+        out.append(case)
+    # split staging: one-tile launches whose tiles pass through LDS half at a
+    # time, over both routes, tile shapes and thread counts; where the library
+    # refuses the split for the drawn shape, the skew is brought towards 0,
+    # and a case it refuses at every skew is kept unsplit
+    rng = np.random.Generator(np.random.PCG64(SPLIT_SEED))
+    tiled_kinds = ("general", "bpc", "bitrev", "transpose", "blockperm", "lowkeep")
+    for i in range(N_SPLIT):
+        kind = tiled_kinds[int(rng.integers(len(tiled_kinds)))]
+        elem = ELEMS[int(rng.integers(len(ELEMS)))]
+        n = int(rng.integers(10, 19))
+        opts = {}
+        route = int(rng.choice([bm.ROUTE_AUTO, bm.ROUTE_FUSED, bm.ROUTE_TWO_PASS]))
+        if route:
+            opts["route"] = route
+        if rng.random() < 0.5:
+            opts["launch"] = bm.LAUNCH_ONE_TILE
+        t = int(rng.choice([0, 0, 5, 6, 7]))
+        if t:
+            opts["tile_log2"] = t
+        bmap = int(rng.choice([0, 1, 3, 5, 6, 8, 12]))
+        if bmap:
+            opts["block_map"] = bmap
+        hint = int(rng.choice([0, 0, 1, 2]))
+        if hint:
+            opts["cache_hint"] = hint
+        if rng.random() < 0.1:
+            opts["no_swizzle"] = 1
+        if rng.random() < 0.4:
+            opts["tile_threads_log2"] = 9
+        skew = int(rng.choice([0, 0, 1, -1, 2, -2])) if route != bm.ROUTE_TWO_PASS else 0
+        case = Case(N_SQUARE + N_SKEW + i, kind, n, elem, int(rng.integers(1, 1 << 30)), opts)
+        A, c = case.matrix()
+        while True:
+            try:
+                bm.Plan(n, A, c, elem, tile_skew=skew, split_stage=1, **opts)
+                case.options["split_stage"] = 1
+                if skew:
+                    case.options["tile_skew"] = skew
+                break
+            except bm.BmmcError:
+                if not skew:
+                    break
+                skew -= 1 if skew > 0 else -1
         out.append(case)
     return out
 

@@ -12,7 +12,7 @@ import bmmc_affine_index_amd as bm
 from bmmc_affine_index_amd import workloads as wl
 
 from emulate import (ReplayError, bank_cycles, check_pass_sampled, run_plan_on_host,
-                     tiled_read_addresses, tiled_write_addresses)
+                     tiled_geometry, tiled_read_addresses, tiled_write_addresses)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -556,6 +556,11 @@ MAX_CASES = [  # (n, elem_bytes, kind, plan options): up to 2^36 bytes per array
     (32, 8, "general", dict(tile_skew=-1, launch=bm.LAUNCH_PERSISTENT)),
     (32, 4, "bitrev", dict(tile_log2=7, tile_threads_log2=9, launch=bm.LAUNCH_STREAMED)),
     (32, 16, "general", dict(tile_threads_log2=9, launch=bm.LAUNCH_ONE_TILE)),
+    (32, 4, "bitrev", dict(tile_log2=7, split_stage=1)),
+    (32, 16, "general", dict(split_stage=1, tile_skew=1)),
+    (32, 1, "general", dict(split_stage=1, route=bm.ROUTE_TWO_PASS)),
+    (31, 8, "bpc", dict(split_stage=1, tile_threads_log2=9, tile_skew=-1)),
+    (32, 2, "transpose", dict(split_stage=1, launch=bm.LAUNCH_ONE_TILE, block_map=6)),
 ]
 
 
@@ -733,6 +738,7 @@ def test_tune_candidates_rebuild_distinct_plans():
         assert len(digests) == len(cands)
         assert {o["tile_skew"] for o in cands} >= {0, 1, -1, 2, -2}
         assert {o["tile_threads_log2"] for o in cands} == {8, 9}
+        assert {o["split_stage"] for o in cands} == {0, 1}
     R = bm.Plan(12, wl.identity_matrix(12), 5, 4)
     assert bm.bmmc_plan_tune_candidates(R.handle) == []
 
@@ -749,3 +755,111 @@ def test_thread_count_option_errors():
     # tiles of at most 256 chunks use one thread per chunk whatever is asked
     P = bm.Plan(20, A, 0, 4, tile_log2=4, tile_threads_log2=9)
     assert P.passes()[0].threads_log2 == 2 * 4 - 2
+
+
+# --------------------------------------------------------------------------
+# Split staging: one-tile launches whose tiles pass LDS half at a time
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(launch=bm.LAUNCH_PERSISTENT), dict(launch=bm.LAUNCH_STREAMED),
+    dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=1)])
+def test_split_stage_needs_one_tile_per_workgroup(kw):
+    A, c = wl.random_bmmc(20, 5, lambda r: oracle.rank(r) == 20)
+    with pytest.raises(bm.BmmcError) as e:
+        bm.Plan(20, A, c, 4, split_stage=1, **kw)
+    assert e.value.status == bm.ERR_INVALID_ARG
+
+
+def test_split_stage_argument_errors():
+    A, c = wl.random_bmmc(20, 5, lambda r: oracle.rank(r) == 20)
+    for bad in (-1, 2):
+        with pytest.raises(bm.BmmcError) as e:
+            bm.Plan(20, A, c, 4, split_stage=bad)
+        assert e.value.status == bm.ERR_INVALID_ARG
+    # a tile of at most 256 chunks is one pass per thread: nothing to split
+    with pytest.raises(bm.BmmcError) as e:
+        bm.Plan(20, A, c, 4, split_stage=1, tile_log2=4)
+    assert e.value.status == bm.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kind,n,e,kw", [
+    ("bitrev", 18, 4, dict(tile_log2=7)),
+    ("bitrev", 18, 4, dict(tile_log2=7, tile_skew=1, tile_threads_log2=9)),
+    ("general", 20, 4, {}),
+    ("general", 19, 4, dict(tile_skew=1)),
+    ("general", 18, 16, dict(tile_skew=2)),
+    ("bpc", 18, 16, dict(tile_threads_log2=9)),
+    ("transpose", 18, 4, dict(block_map=6)),
+    ("general", 16, 2, dict(route=bm.ROUTE_TWO_PASS)),
+    ("general", 17, 8, dict(cache_hint=1, block_map=9)),
+])
+def test_split_stage_plans_replay(kind, n, e, kw):
+    """Split plans: a one-tile launch with half a tile of LDS whose kernel
+    tables, replayed half by half on the host (every LDS slot of a half
+    written and read once, in range), reproduce the oracle's permutation;
+    the options rebuild the same tables."""
+    A, c = _max_matrix(kind, n, 40 + n)
+    P = bm.Plan(n, A, c, e, split_stage=1, **kw)
+    tiled = [d for d in P.passes() if d.kernel == bm.KERNEL_TILED]
+    assert tiled and all(d.split_stage == 1 and d.launch == bm.LAUNCH_ONE_TILE for d in tiled)
+    for d in tiled:
+        assert 2 * d.lds_bytes == (1 << d.unit_log2) << (2 * d.t)
+    assert P.describe()["split_stage"] == 1
+    x = wl.fill_random_bytes(n, e, 77)
+    assert np.array_equal(run_plan_on_host(P, x), oracle.apply(A, c, x))
+    o = P.options()
+    assert o["split_stage"] == 1
+    Q = bm.Plan(n, A, c, e, **o)
+    assert [_desc_bytes(d) for d in Q.passes()] == [_desc_bytes(d) for d in P.passes()]
+
+
+def test_split_stage_keeps_bank_costs_and_coalescing():
+    """On the benchmark's large workloads the split tables keep the lanes'
+    LDS banks of the whole-tile tables at the tuned shapes (the chosen
+    functional leaves the lane bits' costs unchanged) and pass the replay's
+    coalescing check at full size on sampled tiles."""
+    for name, perm, kw in (("c4", 0, dict(tile_log2=7)),
+                           ("c3", 0, dict(tile_log2=7, tile_skew=1, tile_threads_log2=9)),
+                           ("c5", 10, dict(tile_log2=6, tile_skew=2)),
+                           ("c2", 0, dict(tile_log2=7, tile_skew=1))):
+        w = wl.WORKLOADS[name]
+        A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == w.n, perm_index=perm)
+        whole = bm.Plan(w.n, A, c, w.elem_bytes, launch=bm.LAUNCH_ONE_TILE, **kw)
+        half = bm.Plan(w.n, A, c, w.elem_bytes, split_stage=1, **kw)
+        d0, d1 = whole.passes()[0], half.passes()[0]
+        U = 1 << d0.unit_log2
+        CB = U << min(4 - d0.unit_log2, d0.t)
+        for addrs, size in ((tiled_read_addresses, U), (tiled_write_addresses, CB)):
+            for banks in (32, 64):
+                assert bank_cycles(addrs(d1), size, banks) <= bank_cycles(addrs(d0), size, banks), name
+        fa, fc = half.factors()[0]
+        assert check_pass_sampled(d1, fa, fc, w.elem_bytes.bit_length() - 1,
+                                  _sampled_blocks(1 << d1.blk_bits, 3), oracle.map_indices) > 0
+
+
+def test_split_replay_catches_planted_mistakes():
+    """The half-by-half replay rejects split tables run as one staging, whole
+    tables run as two halves, and a pass bit moved out of the top position."""
+    A, c = wl.random_bmmc(18, 3, lambda r: oracle.rank(r) == 18)
+    from emulate import replay_pass
+    P = bm.Plan(18, A, c, 4, split_stage=1, tile_log2=7)
+    d = P.passes()[0]
+    replay_pass(d)
+    bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+    bad.split_stage = 0
+    with pytest.raises(ReplayError):
+        replay_pass(bad)
+    W = bm.Plan(18, A, c, 4, launch=bm.LAUNCH_ONE_TILE, tile_log2=7).passes()[0]
+    bad = bm.bmmc_pass_desc.from_buffer_copy(W)
+    bad.split_stage = 1
+    bad.lds_bytes //= 2
+    with pytest.raises(ReplayError):
+        replay_pass(bad)
+    g = tiled_geometry(d.unit_log2, d.t, d.threads_log2)
+    top = g["ntl"] + g["jl"] - 1
+    bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+    for tab in (bad.ld_in, bad.ld_lds):
+        tab[top], tab[top - 1] = tab[top - 1], tab[top]
+    with pytest.raises(ReplayError):
+        replay_pass(bad)

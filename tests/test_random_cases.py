@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import bmmc_affine_index_amd as bm
 from emulate import run_plan_on_host
 from random_cases import N_CASES, cases, plan_or_none
 
@@ -18,9 +19,21 @@ def test_cases_are_fixed_and_span_the_options():
     assert len(a) == N_CASES
     seen = {k for c in a for k in c.options}
     assert {"route", "launch", "tile_log2", "block_map", "iters_log2", "grid_log2", "walk",
-            "depth", "cache_hint", "no_swizzle", "tile_skew", "tile_threads_log2"} <= seen
+            "depth", "cache_hint", "no_swizzle", "tile_skew", "tile_threads_log2",
+            "split_stage"} <= seen
     skews = {c.options.get("tile_skew", 0) for c in a}
     assert {1, -1, 2, -2} <= skews
+    split = [c for c in a if c.options.get("split_stage")]
+    assert len(split) >= 100
+    assert {c.options.get("tile_skew", 0) for c in split} >= {0, 1, -1}
+    assert {c.options.get("route", 0) for c in split} >= {0, 2, 3}
+    assert {c.elem for c in split} == {1, 2, 4, 8, 16}
+    staged_in_halves = 0
+    for c in split:
+        A, cc = c.matrix()
+        P = bm.Plan(c.n, A, cc, c.elem, **c.options)
+        staged_in_halves += any(d.kernel == bm.KERNEL_TILED and d.split_stage for d in P.passes())
+    assert staged_in_halves >= 80
     assert {c.kind for c in a} == {"general", "bpc", "bitrev", "transpose", "complement",
                                    "blockperm", "lowkeep"}
     assert {c.elem for c in a} == {1, 2, 4, 8, 16}
