@@ -455,7 +455,16 @@ def plan_brief(plan):
     d = plan.describe()
     return {"route": d["route"], "passes": d["passes"], "kernels": d["kernels"],
             "tile_log2": d["tile_log2"], "tile_skew": d["tile_skew"],
+            "tile_threads": d["tile_threads"], "split_stage": d["split_stage"],
             "block_map": d["block_map"], "unit_bytes": d["unit_bytes"]}
+
+
+def plan_label(d):
+    """One line naming a tile plan's launch and shape, from Plan.describe()."""
+    return "%s t=%s skew %s%s%s order %s" % (
+        d["kernels"][-1], d["tile_log2"], d["tile_skew"],
+        " threads %d" % d["tile_threads"] if d.get("tile_threads") not in (None, 256) else "",
+        " split" if d.get("split_stage") else "", d["block_map"])
 
 
 def measure_case(run, name, route, x=None, bufs=None, A=None, c=None):
@@ -516,9 +525,7 @@ def measure_c5(run):
         ok, parity = run.parity(plan, A, c, x, bufs)
         okays += ok
         vals.append(r["gbs"])
-        d = plan.describe()
-        plans.append("%s t=%s skew %s order %s" % (d["kernels"][-1], d["tile_log2"],
-                                                   d["tile_skew"], d["block_map"]))
+        plans.append(plan_label(plan.describe()))
         options.append(plan.options())
         log("c5 perm %d: %.1f GB/s (%.3f of copy) %s, %s" % (k, r["gbs"], r["gbs"] / cp["gbs"],
                                                           plans[-1], parity))
@@ -745,10 +752,7 @@ def main():
             okk, park = run.parity(pk, Ak, ck, x, bufs)
             okays += okk
             vals.append(rk["gbs"])
-            dk = pk.describe()
-            log("perm %d: %.1f GB/s (%s t=%s skew %s order %s) %s" % (
-                k, vals[-1], dk["kernels"][-1], dk["tile_log2"], dk["tile_skew"],
-                dk["block_map"], park))
+            log("perm %d: %.1f GB/s (%s) %s" % (k, vals[-1], plan_label(pk.describe()), park))
         sv = sorted(vals)
         pmed = 0.5 * (sv[(len(sv) - 1) // 2] + sv[len(sv) // 2])
         perm_stats = {"perms": len(vals), "min_gbs": round(sv[0], 2),

@@ -140,3 +140,15 @@ def test_sampled_parity_on_host_tensors():
         bad, _ = bench.sampled_parity(torch, A, c, x, torch.from_numpy(w2.reshape(-1).copy()),
                                       samples=1 << 12)
         assert bad >= 2
+
+
+def test_plan_label_names_shape_threads_and_split():
+    import bmmc_affine_index_amd as bm
+    from bmmc_affine_index_amd import workloads as wl
+    P = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4, split_stage=1, tile_log2=7,
+                tile_threads_log2=9, tile_skew=1)
+    assert bench.plan_label(P.describe()) == "one_tile t=7 skew 1 threads 512 split order 5"
+    Q = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4, launch=bm.LAUNCH_STREAMED, tile_log2=7)
+    assert bench.plan_label(Q.describe()) == "streamed t=7 skew 0 order 5"
+    brief = bench.plan_brief(P)
+    assert brief["tile_threads"] == 512 and brief["split_stage"] == 1 and brief["tile_skew"] == 1
