@@ -421,6 +421,14 @@ def test_workload_c3_bitrev28_full():
         assert P.info.passes == 1 and P.info.kind == bm.KIND_BPC
         assert np.array_equal(got, want), P.describe()
         del got
+    # staged in LDS half at a time, with the shapes the tuning tries
+    for kw in (dict(tile_log2=7), dict(tile_log2=7, tile_skew=1, tile_threads_log2=9),
+               dict(tile_log2=7, tile_skew=2)):
+        _note("c3: gpu split %s" % kw)
+        got, P = _device_run(name, A, c, x, split_stage=1, **kw)
+        assert P.describe()["split_stage"] == 1
+        assert np.array_equal(got, want), P.describe()
+        del got
 
 
 def test_workload_c4_general30():
@@ -517,6 +525,10 @@ GPU_MAX_CASES = [  # (n, elem_bytes, kind, plan options, tune)
     # the naive pass: 2^24 one-byte groups of 256 lanes, also split in two launches
     (32, 1, "general", dict(route=bm.ROUTE_NAIVE), False),
     (32, 4, "reverse", {}, False),                        # complement only: chunk kernel
+    # tiles staged in LDS half at a time
+    (32, 4, "bitrev", dict(split_stage=1, tile_log2=7), False),          # 16 GiB
+    (31, 8, "bpc", dict(split_stage=1, tile_threads_log2=9), False),     # 16 GiB
+    (32, 16, "general", dict(split_stage=1, tile_skew=1), False),        # 64 GiB
 ]
 
 
