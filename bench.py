@@ -460,7 +460,10 @@ def plan_brief(plan):
 
 
 def plan_label(d):
-    """One line naming a tile plan's launch and shape, from Plan.describe()."""
+    """One line naming a tile plan's launch and shape (or a plan's kernels,
+    when it has no tile pass), from Plan.describe()."""
+    if d.get("tile_skew") is None:
+        return "+".join(d["kernels"])
     return "%s t=%s skew %s%s%s order %s" % (
         d["kernels"][-1], d["tile_log2"], d["tile_skew"],
         " threads %d" % d["tile_threads"] if d.get("tile_threads") not in (None, 256) else "",
@@ -547,6 +550,109 @@ def measure_c5(run):
     return e, okays == len(vals)
 
 
+# Tensor front-end workloads: float32 tensors of 2^28 elements (1 GiB), the
+# dimension permutations and flips of the Futhark page's LMAD layouts, as
+# transformer-style shapes.
+FRONTEND_CASES = [
+    # (name, shape, perm, flip)
+    ("batched_transpose", (64, 64, 256, 256), (0, 1, 3, 2), ()),
+    ("heads_to_front", (16, 2048, 32, 256), (0, 2, 1, 3), ()),
+    ("reverse_dims", (256, 256, 64, 64), (3, 2, 1, 0), ()),
+    ("transpose_flip", (16384, 16384), (1, 0), (1,)),
+]
+
+
+def run_frontend(args, torch):
+    """The tensor front-end (permute_dims, parm) on 1 GiB float32 tensors:
+    each call as a user makes it (planning included, eager), against
+    torch's own strided copy of the same view and bmmc_copy of the same
+    bytes, all timed with events on the current stream; every output is
+    compared with torch's.  parm's permutation by its matrix is timed alone
+    as well and checked against the oracle on sampled elements.  One JSON
+    line (not the headline)."""
+    stream = torch.cuda.current_stream()
+    h = int(stream.cuda_stream)
+    n = 28
+    nbytes = 4 << n
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(2024)
+    src = torch.rand(1 << n, device="cuda:0", generator=gen)
+    dst = torch.empty_like(src)
+    steps = max(5, args.steps)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(args.replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b) / steps)
+        return replay_stats(ms, 2.0 * nbytes)
+
+    def copy():
+        if bm.bmmc_copy(src, dst, nbytes, h) != bm.OK:
+            raise bm.BmmcError(bm.ERR_HIP, "bmmc_copy")
+    cp = timed(copy)["gbs"]
+    entries = []
+    ok_all = True
+    for name, shape, perm, flip in FRONTEND_CASES:
+        t = src.view(shape)
+        view = t.flip(list(flip)) if flip else t
+        view = view.permute(*perm)
+        ours = timed(lambda: bm.permute_dims(t, perm, flip))
+        theirs = timed(lambda: dst.view(view.shape).copy_(view))
+        got = bm.permute_dims(t, perm, flip)
+        want = view.contiguous()
+        ok = bool(torch.equal(got, want))
+        ok_all &= ok
+        A, c, nb = bm.bmmc_tensor_permute_matrix([s.bit_length() - 1 for s in shape],
+                                                 list(perm), sum(1 << d for d in flip))
+        plan = bm.Plan(nb, A, c, (4 << n) >> nb)
+        entries.append({"op": "permute_dims", "case": name, "shape": list(shape),
+                        "perm": list(perm), "flip": list(flip), "dtype": "float32",
+                        "gbs": round(ours["gbs"], 2), "frac_of_copy": round(ours["gbs"] / cp, 4),
+                        "torch_gbs": round(theirs["gbs"], 2),
+                        "vs_torch": round(ours["gbs"] / theirs["gbs"], 3),
+                        "plan": plan_label(plan.describe()),
+                        "parity": "bit-exact vs torch" if ok else "MISMATCH vs torch"})
+        log("frontend %s: %.1f GB/s (%.3f of copy), torch %.1f GB/s, %s" % (
+            name, ours["gbs"], ours["gbs"] / cp, theirs["gbs"], entries[-1]["parity"]))
+        del got, want
+    # parm: the permutation by its matrix alone (tuned, as the library's
+    # pass), then the whole call with f the identity
+    mask = 0b1011 | (1 << 20)
+    A = bm.bmmc_parm_matrix(n, mask)
+    plan = bm.Plan(n, A, 0, 4)
+    plan.tune(src, dst, stream=h)
+    r = timed(lambda: plan(src, dst, h))
+    x_host = src.cpu().numpy()
+    plan(src, dst, h)
+    torch.cuda.synchronize()
+    bad, checked = sampled_parity(torch, A, 0, x_host, dst)
+    ok_all &= bad == 0
+    whole = timed(lambda: bm.parm(src, mask, lambda y: y))
+    entries.append({"op": "parm", "n": n, "mask": mask, "dtype": "float32",
+                    "gbs": round(r["gbs"], 2), "frac_of_copy": round(r["gbs"] / cp, 4),
+                    "plan": plan_label(plan.describe()),
+                    "parm_call_ms": round(whole["ms_per_step"], 4),
+                    "parm_call_vs_copies": round(whole["ms_per_step"] / (2.0 * nbytes / (cp * 1e9) * 1e3), 3),
+                    "parity": "bit-exact vs oracle (%d sampled elements)" % checked if not bad
+                              else "MISMATCH vs oracle (%d of %d)" % (bad, checked)})
+    log("frontend parm permutation: %.1f GB/s (%.3f of copy), %s; whole call %.3f ms" % (
+        r["gbs"], r["gbs"] / cp, entries[-1]["parity"], whole["ms_per_step"]))
+    print(json.dumps({"metric": "frontend", "unit": "GB/s", "copy_gbs": round(cp, 2),
+                      "steps": steps, "replays": args.replays, "entries": entries}))
+    sys.stdout.flush()
+    if not ok_all:
+        sys.exit(3)
+
+
 def run_candidates(torch, args, run, plan, n, A, c, elem, x, bufs, workload_name):
     """Every plan bmmc_plan_tune_pairs would time, in its order: one
     bmmc_copy of the array, then --steps executions of the candidate, on the
@@ -631,6 +737,9 @@ def main():
                     help="the paper's Figure 9/11 variants over kinds and sizes, "
                          "one JSON line each (not the headline line)")
     ap.add_argument("--sizes", default="20,24,28", help="ablation: comma-separated n")
+    ap.add_argument("--frontend", action="store_true",
+                    help="the tensor front-end (permute_dims on 1 GiB float32 tensors, parm) "
+                         "against torch's strided copy, as one JSON line (not the headline)")
     ap.add_argument("--candidates", action="store_true",
                     help="run every plan the tuning would time for the workload, each "
                          "--steps times after one bmmc_copy of the array (a separator for "
@@ -659,6 +768,9 @@ def main():
 
     if args.ablation:
         run_ablation(args, torch)
+        return
+    if args.frontend:
+        run_frontend(args, torch)
         return
 
     name = args.workload

@@ -150,5 +150,25 @@ def test_plan_label_names_shape_threads_and_split():
     assert bench.plan_label(P.describe()) == "one_tile t=7 skew 1 threads 512 split order 5"
     Q = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4, launch=bm.LAUNCH_STREAMED, tile_log2=7)
     assert bench.plan_label(Q.describe()) == "streamed t=7 skew 0 order 5"
+    R = bm.Plan(20, wl.identity_matrix(20), (1 << 20) - 1, 4)
+    assert bench.plan_label(R.describe()) == "chunk_scatter"
     brief = bench.plan_brief(P)
     assert brief["tile_threads"] == 512 and brief["split_stage"] == 1 and brief["tile_skew"] == 1
+
+
+def test_frontend_cases_are_one_gib_and_plan_on_the_host():
+    """The front-end benchmark's tensors hold 2^28 float32 elements, and the
+    library plans each dimension permutation as one bit-permute-complement."""
+    import bmmc_affine_index_amd as bm
+    for name, shape, perm, flip in bench.FRONTEND_CASES:
+        total = 1
+        for s in shape:
+            assert s & (s - 1) == 0
+            total *= s
+        assert total == 1 << 28, name
+        assert sorted(perm) == list(range(len(shape)))
+        A, c, n = bm.bmmc_tensor_permute_matrix([s.bit_length() - 1 for s in shape], list(perm),
+                                                sum(1 << d for d in flip))
+        P = bm.Plan(n, A, c, (4 << 28) >> n)
+        assert P.info.kind in (bm.KIND_BPC, bm.KIND_IDENTITY)
+        assert P.info.passes == 1
