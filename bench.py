@@ -564,10 +564,10 @@ FRONTEND_CASES = [
 
 def run_frontend(args, torch):
     """The tensor front-end (permute_dims, parm) on 1 GiB float32 tensors:
-    each call as a user makes it (planning included, eager), against
-    torch's own strided copy of the same view and bmmc_copy of the same
-    bytes, all timed with events on the current stream; every output is
-    compared with torch's.  parm's permutation by its matrix is timed alone
+    each call as a user makes it (eager; the front-end plans on the first
+    call and keeps the plan), against torch's own strided copy of the same
+    view and bmmc_copy of the same bytes, all timed with events on the
+    current stream; every output is compared with torch's.  parm's permutation by its matrix is timed alone
     as well and checked against the oracle on sampled elements.  One JSON
     line (not the headline)."""
     stream = torch.cuda.current_stream()

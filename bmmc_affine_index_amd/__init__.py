@@ -11,8 +11,10 @@ bit 0 = least significant index bit), as in include/bmmc.h.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
+import threading
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -499,12 +501,45 @@ def _ordered(run, tensors, stream) -> None:
     cur.wait_stream(side)
 
 
+# Plans the front-end made, most recently used last: planning costs tens of
+# microseconds to a millisecond on the host, a single-pass plan holds no
+# device memory and its tables do not change while it runs, so one plan
+# serves every later call with the same map, element size and options, on
+# any stream.  Plans with a scratch array (the two-pass route) are not kept.
+_PLAN_CACHE = collections.OrderedDict()
+_PLAN_CACHE_SIZE = 32
+_PLAN_CACHE_LOCK = threading.Lock()
+
+
+def _cached_plan(n: int, A: Sequence[int], c: int, elem: int, plan_kw: dict) -> "Plan":
+    key = (n, tuple(int(a) for a in A), int(c), int(elem), tuple(sorted(plan_kw.items())))
+    with _PLAN_CACHE_LOCK:
+        plan = _PLAN_CACHE.get(key)
+        if plan is not None:
+            _PLAN_CACHE.move_to_end(key)
+            return plan
+    plan = Plan(n, A, c, elem, **plan_kw)
+    if plan.info.scratch_bytes == 0:
+        with _PLAN_CACHE_LOCK:
+            _PLAN_CACHE[key] = plan
+            while len(_PLAN_CACHE) > _PLAN_CACHE_SIZE:
+                _PLAN_CACHE.popitem(last=False)
+    return plan
+
+
+def clear_plan_cache() -> None:
+    """Drop the plans kept by permute, parm, permute_dims, flip and transpose2d."""
+    with _PLAN_CACHE_LOCK:
+        _PLAN_CACHE.clear()
+
+
 def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw):
     """out[A.i XOR c] = inp[i] over the first axis of a contiguous device
     tensor with 2^n rows (a row is one element).  With a `stream` other than
     torch's current one, the permutation runs there, ordered after the work
     already queued on the current stream and before the work queued on it
-    afterwards."""
+    afterwards.  Single-pass plans are kept for later calls with the same
+    map (clear_plan_cache drops them)."""
     import torch
     n = len(A)
     if inp.shape[0] != (1 << n):
@@ -512,7 +547,7 @@ def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw)
     elem = inp.numel() * inp.element_size() >> n
     if out is None:
         out = torch.empty_like(inp)
-    plan = Plan(n, A, c, elem, **plan_kw)
+    plan = _cached_plan(n, A, c, elem, plan_kw)
     _ordered(lambda h: plan(inp, out, h), [inp, out], stream)
     return out
 

@@ -106,3 +106,26 @@ def test_tensor_permute_matrix_errors():
                          ([2, 3], [1, 0], 4), ([-1, 2], [1, 0], 0)]:
         with pytest.raises(bm.BmmcError):
             bm.bmmc_tensor_permute_matrix(dl, perm, fm)
+
+
+def test_plan_cache_keeps_single_pass_plans_only():
+    """The front-end keeps one plan per (map, element size, options) and
+    hands the same one back; two-pass plans (which own a scratch array) are
+    not kept; the cache is bounded and can be cleared."""
+    import bmmc_affine_index_amd as bmi
+    bmi.clear_plan_cache()
+    A = wl.bit_reverse_matrix(12)
+    p1 = bmi._cached_plan(12, A, 0, 4, {})
+    assert bmi._cached_plan(12, list(A), 0, 4, {}) is p1
+    assert bmi._cached_plan(12, A, 1, 4, {}) is not p1
+    assert bmi._cached_plan(12, A, 0, 8, {}) is not p1
+    assert bmi._cached_plan(12, A, 0, 4, {"block_map": 1}) is not p1
+    R, c = wl.random_bmmc(14, 3, lambda r: oracle.rank(r) == 14)
+    two = bmi._cached_plan(14, R, c, 4, {"route": bm.ROUTE_TWO_PASS})
+    assert two.info.passes == 2 and two.info.scratch_bytes > 0
+    assert bmi._cached_plan(14, R, c, 4, {"route": bm.ROUTE_TWO_PASS}) is not two
+    for k in range(bmi._PLAN_CACHE_SIZE + 5):
+        bmi._cached_plan(12, A, k, 2, {})
+    assert len(bmi._PLAN_CACHE) == bmi._PLAN_CACHE_SIZE
+    bmi.clear_plan_cache()
+    assert len(bmi._PLAN_CACHE) == 0
