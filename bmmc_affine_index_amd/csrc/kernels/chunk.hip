@@ -47,6 +47,21 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
     const uint64_t first = (blk0 + blockIdx.x) << (kChunkNTL + kChunkCPTL);
     const uint64_t *tab = GATHER ? d.in_blk : d.out_blk;
     const uint64_t lane_off = dev::xor_bits_lane<kChunkNTL>(tab, tid);
+    // A gather needs the wave-uniform part of each group's source offset
+    // before its loads: the whole wave computes it (lane k loads entry k, a
+    // wave XOR reduction keeps the entries of the set bits; the bits of xu
+    // below kChunkNTL are 0), one vector load instead of a chain of scalar
+    // loads, with every lane active, before the guard on the array's end
+    // (measured on MI355X: a 4 MiB block permutation +7%).  A scatter
+    // computes its output base from scalar loads after issuing its loads,
+    // which hides them (the wave form cost a 4 MiB reversal 10%).
+    uint64_t ubase[CPT] = {};
+    if constexpr (GATHER) {
+        const uint64_t entry = dev::wave_load(tab);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            ubase[k] = dev::wave_select_xor(entry, first + ((uint64_t)k << kChunkNTL)) ^ d.in_c;
+    }
 
     dev::Chunk<CB> v[CPT];
 #pragma unroll
@@ -54,8 +69,7 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
         const uint64_t xu = first + ((uint64_t)k << kChunkNTL);
         const uint64_t x = xu + tid;
         if (x >= nchunks) continue;
-        const uint64_t src =
-            GATHER ? (dev::xor_bits_uniform(d.in_blk, xu) ^ lane_off ^ d.in_c) : x * CB;
+        const uint64_t src = GATHER ? (ubase[k] ^ lane_off) : x * CB;
         v[k] = dev::gload_nt<CB, NT>(in + src);
     }
     const uint32_t ux = (uint32_t)d.unit_xor;
