@@ -348,11 +348,41 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     // every run takes the next pair, across candidates, so that with enough
     // pairs each run meets data that has left the caches since its last use
     int next = 0;
-    auto run = [&](const bmmc_plan &q) {
+    auto run_on = [&](const bmmc_plan &q, hipStream_t on) {
         const int k = next;
         next = (next + 1) % npairs;
-        return run_passes(q.pass, q.npasses, ins[k], outs[k], scratch, s);
+        return run_passes(q.pass, q.npasses, ins[k], outs[k], scratch, on);
     };
+    auto run = [&](const bmmc_plan &q) { return run_on(q, s); };
+    // Passes of a few microseconds are timed as graph replays: launched one
+    // by one from the host, their launches, not the kernels, would set the
+    // pace (a 4 MiB pass runs for about as long as a launch takes), and every
+    // candidate would time alike.  Each candidate's `reps` runs are captured
+    // once on a private stream and the graph is replayed on `s`; if capture
+    // is not available, every candidate is timed from eager launches.
+    const bool short_runs = 2.0 * (double)bytes / 5e12 < 100e-6;
+    std::vector<hipGraphExec_t> graphs;
+    if (short_runs) {
+        hipStream_t cs = nullptr;
+        bool ok = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) == hipSuccess;
+        for (size_t i = 0; ok && i < cand.size(); ++i) {
+            hipGraph_t g = nullptr;
+            hipGraphExec_t ge = nullptr;
+            ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
+            int cst2 = BMMC_OK;
+            for (int r = 0; ok && r < reps && cst2 == BMMC_OK; ++r) cst2 = run_on(*cand[i], cs);
+            if (ok) ok = hipStreamEndCapture(cs, &g) == hipSuccess && cst2 == BMMC_OK && g;
+            if (ok) ok = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) == hipSuccess;
+            if (g) (void)hipGraphDestroy(g);
+            if (ok) graphs.push_back(ge);
+        }
+        if (cs) (void)hipStreamDestroy(cs);
+        if (!ok) {
+            for (hipGraphExec_t ge : graphs) (void)hipGraphExecDestroy(ge);
+            graphs.clear();
+            (void)hipGetLastError();
+        }
+    }
     // every candidate is timed in kTuneRounds rounds, the candidates
     // interleaved within a round, and judged by its median round
     constexpr int kTuneRounds = 5;
@@ -361,9 +391,17 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
     for (int round = 0; round < kTuneRounds && st == BMMC_OK; ++round)
         for (size_t i = 0; i < cand.size() && st == BMMC_OK; ++i) {
             const bmmc_plan &q = *cand[i];
-            st = run(q);  // warm-up
-            if (st == BMMC_OK && hipEventRecord(e0, s) != hipSuccess) st = BMMC_ERR_HIP;
-            for (int r = 0; r < reps && st == BMMC_OK; ++r) st = run(q);
+            if (!graphs.empty()) {
+                // the first replay of each round warms up (its first one
+                // also uploads the graph)
+                if (hipGraphLaunch(graphs[i], s) != hipSuccess ||
+                    hipEventRecord(e0, s) != hipSuccess || hipGraphLaunch(graphs[i], s) != hipSuccess)
+                    st = BMMC_ERR_HIP;
+            } else {
+                st = run(q);  // warm-up
+                if (st == BMMC_OK && hipEventRecord(e0, s) != hipSuccess) st = BMMC_ERR_HIP;
+                for (int r = 0; r < reps && st == BMMC_OK; ++r) st = run(q);
+            }
             float ms = 0.f;
             if (st == BMMC_OK &&
                 (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
@@ -371,6 +409,7 @@ int bmmc_plan_tune_pairs(bmmc_plan *p, const void *const *ins, void *const *outs
                 st = BMMC_ERR_HIP;
             if (st == BMMC_OK) times[i].push_back(ms);
         }
+    for (hipGraphExec_t ge : graphs) (void)hipGraphExecDestroy(ge);
     std::vector<float> best(cand.size(), 1e30f);
     for (size_t i = 0; i < cand.size(); ++i) {
         std::vector<float> &v = times[i];

@@ -270,8 +270,11 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * the same tables.  An option the caller fixed at plan
  * creation is kept.  Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
- * interleave the candidates, timed with HIP events; the candidate with the
- * fastest median round replaces the plan's kernel tables if it beats the
+ * interleave the candidates, timed with HIP events (for arrays below about
+ * 250 MB each candidate's runs are captured once into a HIP graph on a
+ * private stream and the graph is replayed on `stream`, so that launch costs
+ * do not mask the kernels; eager launches if capture fails); the candidate
+ * with the fastest median round replaces the plan's kernel tables if it beats the
  * planner's own choice by more than 2%, and the chosen tables are then run
  * once on ins[0] -> outs[0].
  *
