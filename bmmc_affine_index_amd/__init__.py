@@ -511,14 +511,21 @@ _PLAN_CACHE_SIZE = 32
 _PLAN_CACHE_LOCK = threading.Lock()
 
 
-def _cached_plan(n: int, A: Sequence[int], c: int, elem: int, plan_kw: dict) -> "Plan":
-    key = (n, tuple(int(a) for a in A), int(c), int(elem), tuple(sorted(plan_kw.items())))
+def _cached_plan(n: int, A: Sequence[int], c: int, elem: int, plan_kw: dict,
+                 tuned: bool = False, tune_fn=None) -> "Plan":
+    """The kept plan for this map, element size and options (tuned ones are
+    kept apart from untuned ones), or a new one; a new plan for a tuned call
+    is tuned by tune_fn(plan) before it is kept."""
+    key = (n, tuple(int(a) for a in A), int(c), int(elem), tuple(sorted(plan_kw.items())),
+           bool(tuned))
     with _PLAN_CACHE_LOCK:
         plan = _PLAN_CACHE.get(key)
         if plan is not None:
             _PLAN_CACHE.move_to_end(key)
             return plan
     plan = Plan(n, A, c, elem, **plan_kw)
+    if tuned and tune_fn is not None:
+        tune_fn(plan)
     if plan.info.scratch_bytes == 0:
         with _PLAN_CACHE_LOCK:
             _PLAN_CACHE[key] = plan
@@ -533,13 +540,16 @@ def clear_plan_cache() -> None:
         _PLAN_CACHE.clear()
 
 
-def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw):
+def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, tune: bool = False,
+            **plan_kw):
     """out[A.i XOR c] = inp[i] over the first axis of a contiguous device
     tensor with 2^n rows (a row is one element).  With a `stream` other than
     torch's current one, the permutation runs there, ordered after the work
     already queued on the current stream and before the work queued on it
     afterwards.  Single-pass plans are kept for later calls with the same
-    map (clear_plan_cache drops them)."""
+    map (clear_plan_cache drops them).  tune=True tunes a new plan on this
+    call's tensors (bmmc_plan_tune) before it is kept, so later tuned calls
+    with the same map run the tuned plan without timing."""
     import torch
     n = len(A)
     if inp.shape[0] != (1 << n):
@@ -547,7 +557,10 @@ def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw)
     elem = inp.numel() * inp.element_size() >> n
     if out is None:
         out = torch.empty_like(inp)
-    plan = _cached_plan(n, A, c, elem, plan_kw)
+
+    def tune_fn(plan):
+        _ordered(lambda h: plan.tune(inp, out, stream=h), [inp, out], stream)
+    plan = _cached_plan(n, A, c, elem, plan_kw, tuned=tune, tune_fn=tune_fn)
     _ordered(lambda h: plan(inp, out, h), [inp, out], stream)
     return out
 
@@ -556,7 +569,7 @@ def permute(inp, A: Sequence[int], c: int = 0, out=None, stream=None, **plan_kw)
 # Users of the permutation: parm and tensor dimensions
 # ---------------------------------------------------------------------------
 
-def parm(x, mask: int, f, stream=None):
+def parm(x, mask: int, f, stream=None, tune: bool = False):
     """parm mask f x: split the 2^n rows of x by the F2 dot product i.mask,
     apply f to the part with i.mask = 0 and to the other part (each in
     increasing index order, as a tensor of 2^(n-1) rows), and stitch the
@@ -568,17 +581,19 @@ def parm(x, mask: int, f, stream=None):
     if rows != (1 << n) or n < 1:
         raise ValueError("the first axis must have 2^n entries, n >= 1")
     A = bmmc_parm_matrix(n, mask)
-    y = permute(x, A, 0, stream=stream)
+    y = permute(x, A, 0, stream=stream, tune=tune)
     half = rows // 2
     z = torch.empty_like(y)
     z[:half] = f(y[:half])
     z[half:] = f(y[half:])
-    return permute(z, bmmc_matrix_inverse(A), 0, stream=stream)
+    return permute(z, bmmc_matrix_inverse(A), 0, stream=stream, tune=tune)
 
 
-def permute_dims(t, perm: Sequence[int], flip: Sequence[int] = (), stream=None):
+def permute_dims(t, perm: Sequence[int], flip: Sequence[int] = (), stream=None,
+                 tune: bool = False):
     """t.flip(flip).permute(perm).contiguous() for a contiguous device tensor
-    whose dimensions are powers of two, as one BPC permutation."""
+    whose dimensions are powers of two, as one BPC permutation (tune as in
+    permute)."""
     shape = list(t.shape)
     dl = []
     for s in shape:
@@ -593,14 +608,14 @@ def permute_dims(t, perm: Sequence[int], flip: Sequence[int] = (), stream=None):
     if n == 0:
         return t.clone().reshape(out_shape)
     flat = t.reshape(1 << n, -1) if t.numel() else t
-    return permute(flat, A, c, stream=stream).reshape(out_shape)
+    return permute(flat, A, c, stream=stream, tune=tune).reshape(out_shape)
 
 
-def flip(t, dims: Sequence[int], stream=None):
+def flip(t, dims: Sequence[int], stream=None, tune: bool = False):
     """t.flip(dims) for power-of-two dimensions, as one BPC permutation."""
-    return permute_dims(t, list(range(t.dim())), flip=dims, stream=stream)
+    return permute_dims(t, list(range(t.dim())), flip=dims, stream=stream, tune=tune)
 
 
-def transpose2d(t, stream=None):
+def transpose2d(t, stream=None, tune: bool = False):
     """The transpose of a 2^a x 2^b matrix (a rotation of the index bits)."""
-    return permute_dims(t, [1, 0], stream=stream)
+    return permute_dims(t, [1, 0], stream=stream, tune=tune)

@@ -120,6 +120,12 @@ def test_plan_cache_keeps_single_pass_plans_only():
     assert bmi._cached_plan(12, A, 1, 4, {}) is not p1
     assert bmi._cached_plan(12, A, 0, 8, {}) is not p1
     assert bmi._cached_plan(12, A, 0, 4, {"block_map": 1}) is not p1
+    # tuned plans are kept apart from untuned ones; a new one is tuned once
+    calls = []
+    t1 = bmi._cached_plan(12, A, 0, 4, {}, tuned=True, tune_fn=calls.append)
+    assert t1 is not p1 and calls == [t1]
+    assert bmi._cached_plan(12, A, 0, 4, {}, tuned=True, tune_fn=calls.append) is t1
+    assert calls == [t1]
     R, c = wl.random_bmmc(14, 3, lambda r: oracle.rank(r) == 14)
     two = bmi._cached_plan(14, R, c, 4, {"route": bm.ROUTE_TWO_PASS})
     assert two.info.passes == 2 and two.info.scratch_bytes > 0

@@ -98,3 +98,29 @@ def test_side_stream_is_ordered_with_current_stream(as_handle):
         assert torch.equal(got2, want), rep
         assert torch.equal(pg2, pw), rep
         assert torch.equal(pw.cpu(), x.cpu().flip([1]).permute(2, 0, 1).contiguous())
+
+
+def test_tuned_front_end_calls_keep_one_tuned_plan():
+    """tune=True tunes a new plan on the call's tensors and keeps it: the
+    result equals torch's on the first and on a later call, the later call
+    reuses the kept (tuned) plan, and an untuned call keeps its own."""
+    torch = _torch()
+    bm.clear_plan_cache()
+    x = torch.rand(16, 32, 64, 64, device="cuda:0")
+    want = x.permute(0, 3, 2, 1).contiguous()
+    a = bm.permute_dims(x, (0, 3, 2, 1), tune=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, want)
+    n_kept = len(bm._PLAN_CACHE)
+    b = bm.permute_dims(x, (0, 3, 2, 1), tune=True)
+    torch.cuda.synchronize()
+    assert torch.equal(b, want) and len(bm._PLAN_CACHE) == n_kept
+    c = bm.permute_dims(x, (0, 3, 2, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(c, want) and len(bm._PLAN_CACHE) == n_kept + 1
+    y = torch.arange(1 << 18, dtype=torch.int32, device="cuda:0")
+    z = bm.parm(y, 0b1011, lambda t: t.flip(0), tune=True)
+    torch.cuda.synchronize()
+    ref = _parm_reference(y.cpu().numpy(), 0b1011, lambda t: t[::-1])
+    assert np.array_equal(z.cpu().numpy(), ref)
+    bm.clear_plan_cache()
