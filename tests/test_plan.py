@@ -863,3 +863,31 @@ def test_split_replay_catches_planted_mistakes():
         tab[top], tab[top - 1] = tab[top - 1], tab[top]
     with pytest.raises(ReplayError):
         replay_pass(bad)
+
+
+@pytest.mark.parametrize("fixed", [
+    dict(launch=bm.LAUNCH_STREAMED), dict(tile_skew=1), dict(tile_threads_log2=9),
+    dict(split_stage=1), dict(block_map=6), dict(route=bm.ROUTE_TWO_PASS), dict(tile_log2=6)])
+def test_tune_candidates_keep_what_the_caller_fixed(fixed):
+    """Every candidate keeps an option the caller set at plan creation; the
+    options left open still vary."""
+    n = 28
+    A, c = wl.workload_matrix("c3")
+    if "route" in fixed:  # a general matrix, so that the two-pass route applies
+        n = 24
+        A, c = wl.random_bmmc(n, 24, lambda r: oracle.rank(r) == n)
+    P = bm.Plan(n, A, c, 4, **fixed)
+    cands = P.tune_candidates()
+    assert cands
+    for k, v in fixed.items():
+        if k == "route":
+            assert all(o["tile_skew"] == 0 for o in cands)
+            assert all(bm.Plan(n, A, c, 4, **o).info.passes == 2 for o in cands)
+        else:
+            assert {o[k] for o in cands} == {v}, k
+    if "block_map" not in fixed:
+        assert len({o["block_map"] for o in cands}) >= 4
+    if "split_stage" in fixed:
+        assert {o["launch"] for o in cands} == {bm.LAUNCH_ONE_TILE}
+    if fixed.get("launch") == bm.LAUNCH_STREAMED:
+        assert {o["split_stage"] for o in cands} == {0}
