@@ -267,8 +267,8 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * side on every launch style, orders 5 and 6) and tiles staged in LDS half at
  * a time (split_stage; skew 0, 1, -1 and 2, 256 and 512 threads, order 5,
  * where the matrix admits them): up to 110 candidates, fewer where two build
- * the same tables.  An option the caller fixed at plan
- * creation is kept.  Each candidate runs `reps` times (0 = enough runs
+ * the same tables.  An option the caller fixed at plan creation is kept.
+ * Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events (for arrays below about
  * 250 MB each candidate's runs are captured once into a HIP graph on a
@@ -323,7 +323,8 @@ int bmmc_plan_get_info(const bmmc_plan *plan, bmmc_plan_info *info);
 
 /* The options that rebuild this plan's current kernel tables: the caller's
  * options with every choice the planner or bmmc_plan_tune made written out
- * (tile side, launch style, grid, walk, depth, tile order, cache hint), so
+ * (tile side, tile skew, threads per tile, split staging, launch style, grid,
+ * walk, depth, tile order, cache hint), so
  * bmmc_plan_create_ex(n, A, c, elem_bytes, opt) gives the same tables without
  * timing anything again.  Host-only. */
 int bmmc_plan_get_options(const bmmc_plan *plan, bmmc_plan_options *opt);
