@@ -102,8 +102,10 @@ typedef struct bmmc_plan_options {
                               8 (256) or 9 (512); 0 = planner's choice (8).  Tiles of
                               fewer chunks use one thread per chunk. */
     int split_stage; /* tile pass, one-tile launch only: 1 = stage each tile in LDS half
-                        at a time (half the LDS per workgroup, so twice the tiles can
-                        hold LDS on a compute unit); 0 = planner's choice (whole tiles).
+                        at a time (half the LDS per workgroup, so more tiles can hold
+                        LDS on a compute unit at once: up to five 32 KiB halves of
+                        64 KiB tiles against two whole ones); 0 = planner's choice
+                        (whole tiles).
                         Not every matrix admits it at every tile shape
                         (BMMC_ERR_INVALID_ARG then); launch must be AUTO or ONE_TILE
                         and iters_log2 0. */
