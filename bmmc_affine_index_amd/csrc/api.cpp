@@ -198,6 +198,25 @@ int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> 
                     const int st = add(o);
                     if (st != BMMC_OK) return st;
                 }
+    // one tile per workgroup at the planner's side too, rectangular and with
+    // 512 threads (random 16-byte BPCs, whose planner side holds 2^10 units:
+    // measured on MI355X, +1% to +7% on the slower permutations)
+    if (!p->opt.tile_skew && !p->opt.tile_threads_log2 && p->opt.iters_log2 == 0 &&
+        (!p->opt.launch || p->opt.launch == BMMC_LAUNCH_ONE_TILE) &&
+        p->opt.route != BMMC_ROUTE_TWO_PASS && p->opt.route != BMMC_ROUTE_NAIVE)
+        for (int skew : {0, 1, -1, 2, -2})
+            for (int tl : {bmmc::kTileMaxNTL, bmmc::kTileWideNTL})
+                for (int m : {bmmc::kDefaultBlockMap, 6}) {
+                    if (p->opt.block_map && m != p->opt.block_map) continue;
+                    bmmc_plan_options o = p->opt;
+                    o.tile_log2 = tiles.front();
+                    o.launch = BMMC_LAUNCH_ONE_TILE;
+                    o.block_map = m;
+                    o.tile_skew = skew;
+                    o.tile_threads_log2 = tl;
+                    const int st = add(o);
+                    if (st != BMMC_OK) return st;
+                }
     // one-tile launches staged in LDS half at a time, at the larger side
     // (measured on MI355X against whole tiles of the same shape: from -4% to
     // +1.4% on random 16-byte BPCs, level on bit reversal and random BMMC);
