@@ -131,6 +131,16 @@ int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> 
         if (bmmc::build_plan(p->n, p->A, p->c, (size_t)p->elem_bytes, &o, q.get()) != BMMC_OK ||
             !supported(*q))
             return BMMC_OK;
+        // rectangular tiles whose shorter rows hold less than a 128-byte line
+        // are left out: a 64-byte input row reads every line twice (measured
+        // with FETCH_SIZE: 1.5 times the array's bytes per pass)
+        if (o.tile_skew)
+            for (int k = 0; k < q->npasses; ++k) {
+                const bmmc_pass_desc &d = q->pass[k];
+                if (d.kernel == BMMC_KERNEL_TILED &&
+                    std::min(d.in_row_log2, d.out_row_log2) + d.unit_log2 < 7)
+                    return BMMC_OK;
+            }
         q->opt = o;
         // the next larger side (rows twice as long), once the planner's side
         // is known; the planner clamps it to what the LDS and the index bits

@@ -270,7 +270,8 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * planner's side with skew 0, 1, -1, 2 and -2 and 256 or 512 threads (orders
  * 5 and 6), and tiles staged in LDS half at a time (split_stage; skew 0, 1,
  * -1 and 2, 256 and 512 threads, order 5, where the matrix admits them): up
- * to 130 candidates, fewer where two build the same tables.  An option the caller fixed at plan creation is kept.
+ * to 130 candidates, fewer where two build the same tables or where a
+ * rectangular tile's shorter rows would hold less than 128 bytes.  An option the caller fixed at plan creation is kept.
  * Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events (for arrays below about
