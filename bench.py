@@ -454,7 +454,8 @@ def plan_brief(plan):
     return {"route": d["route"], "passes": d["passes"], "kernels": d["kernels"],
             "tile_log2": d["tile_log2"], "tile_skew": d["tile_skew"],
             "tile_threads": d["tile_threads"], "split_stage": d["split_stage"],
-            "block_map": d["block_map"], "unit_bytes": d["unit_bytes"]}
+            "buffer_loads": d["buffer_loads"], "block_map": d["block_map"],
+            "unit_bytes": d["unit_bytes"]}
 
 
 def plan_label(d):
@@ -462,10 +463,11 @@ def plan_label(d):
     when it has no tile pass), from Plan.describe()."""
     if d.get("tile_skew") is None:
         return "+".join(d["kernels"])
-    return "%s t=%s skew %s%s%s order %s" % (
+    return "%s t=%s skew %s%s%s%s order %s" % (
         d["kernels"][-1], d["tile_log2"], d["tile_skew"],
         " threads %d" % d["tile_threads"] if d.get("tile_threads") not in (None, 256) else "",
-        " split" if d.get("split_stage") else "", d["block_map"])
+        " split" if d.get("split_stage") else "",
+        " buffer loads" if d.get("buffer_loads") else "", d["block_map"])
 
 
 def measure_case(run, name, route, x=None, bufs=None, A=None, c=None):

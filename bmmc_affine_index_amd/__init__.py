@@ -64,7 +64,8 @@ class bmmc_plan_options(ctypes.Structure):
                 ("launch", ctypes.c_int), ("grid_log2", ctypes.c_int),
                 ("walk", ctypes.c_int), ("depth", ctypes.c_int), ("cache_hint", ctypes.c_int),
                 ("block_map", ctypes.c_int), ("tile_skew", ctypes.c_int),
-                ("tile_threads_log2", ctypes.c_int), ("split_stage", ctypes.c_int)]
+                ("tile_threads_log2", ctypes.c_int), ("split_stage", ctypes.c_int),
+                ("buffer_loads", ctypes.c_int)]
 
 
 class bmmc_plan_info(ctypes.Structure):
@@ -93,7 +94,8 @@ class bmmc_pass_desc(ctypes.Structure):
                 ("st_lds", ctypes.c_uint32 * MAX_CHUNK_BITS),
                 ("st_unit", ctypes.c_uint32 * 4), ("in_c", ctypes.c_uint64),
                 ("in_row_log2", ctypes.c_int32), ("out_row_log2", ctypes.c_int32),
-                ("threads_log2", ctypes.c_int32), ("split_stage", ctypes.c_int32)]
+                ("threads_log2", ctypes.c_int32), ("split_stage", ctypes.c_int32),
+                ("buffer_loads", ctypes.c_int32)]
 
 
 class BmmcError(RuntimeError):
@@ -224,11 +226,12 @@ def bmmc_plan_create_ex(n: int, A: Sequence[int], c: int, elem_bytes: int,
                         iters_log2: int = 0, launch: int = LAUNCH_AUTO,
                         grid_log2: int = 0, walk: int = WALK_AUTO, block_map: int = 0,
                         depth: int = 0, cache_hint: int = 0, tile_skew: int = 0,
-                        tile_threads_log2: int = 0, split_stage: int = 0) -> int:
+                        tile_threads_log2: int = 0, split_stage: int = 0,
+                        buffer_loads: int = 0) -> int:
     _, arr = _rows(A)
     opt = bmmc_plan_options(route, tile_log2, no_swizzle, iters_log2, launch, grid_log2, walk,
                             depth, cache_hint, block_map, tile_skew, tile_threads_log2,
-                            split_stage)
+                            split_stage, buffer_loads)
     return lib().bmmc_plan_create_ex(int(n), arr, int(c), int(elem_bytes),
                                      ctypes.byref(opt)) or 0
 
@@ -372,13 +375,13 @@ class Plan:
                  iters_log2: int = 0, launch: int = LAUNCH_AUTO, grid_log2: int = 0,
                  walk: int = WALK_AUTO, block_map: int = 0, depth: int = 0,
                  cache_hint: int = 0, tile_skew: int = 0, tile_threads_log2: int = 0,
-                 split_stage: int = 0):
+                 split_stage: int = 0, buffer_loads: int = 0):
         self.n, self.elem_bytes = int(n), int(elem_bytes)
         self.A, self.c = [int(a) for a in A], int(c)
         self.handle = bmmc_plan_create_ex(n, A, c, elem_bytes, route, tile_log2,
                                           int(bool(no_swizzle)), iters_log2, launch, grid_log2,
                                           walk, block_map, depth, cache_hint, tile_skew,
-                                          tile_threads_log2, split_stage)
+                                          tile_threads_log2, split_stage, buffer_loads)
         if not self.handle:
             raise BmmcError(bmmc_last_error(), "bmmc_plan_create")
         self.info = bmmc_plan_get_info(self.handle)
@@ -458,6 +461,7 @@ class Plan:
         skew = [d.out_row_log2 - d.t for d in self.passes() if d.kernel == KERNEL_TILED]
         thr = [d.threads_log2 for d in self.passes() if d.kernel == KERNEL_TILED]
         split = [d.split_stage for d in self.passes() if d.kernel == KERNEL_TILED]
+        bufld = [d.buffer_loads for d in self.passes() if d.kernel == KERNEL_TILED]
         return {"n": i.n, "elem_bytes": i.elem_bytes, "kind": KIND_NAMES[i.kind],
                 "route": ROUTE_NAMES[i.route], "passes": i.passes, "unit_bytes": i.unit_bytes,
                 "unit_bits": i.unit_bits, "tile_log2": i.tile_log2, "n_over": i.n_over,
@@ -467,7 +471,8 @@ class Plan:
                 "block_map": bmap[0] if bmap else None,
                 "tile_skew": skew[-1] if skew else None,
                 "tile_threads": (1 << thr[-1]) if thr else None,
-                "split_stage": split[-1] if split else None}
+                "split_stage": split[-1] if split else None,
+                "buffer_loads": bufld[-1] if bufld else None}
 
 
 def copy(inp, out, nbytes: Optional[int] = None, stream=None) -> None:

@@ -102,6 +102,36 @@ __device__ __forceinline__ void gstore_nt(uint8_t *p, const Chunk<BYTES> &c) {
     }
 }
 
+// Buffer loads: the base address and the byte size of the array sit in a
+// four-dword resource in scalar registers, and each lane supplies only a
+// 32-bit byte offset.  Word 3 of the resource: raw (untyped) access with the
+// 32-bit data format, stride 0, so the size field counts bytes and a load
+// past it returns zero instead of touching memory.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t *base,
+                                                              uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)bytes,
+                                             kBufferRsrcWord3);
+}
+
+// One chunk of 4, 8 or 16 bytes at byte offset `off`, with the non-temporal
+// policy when NT (the operand is an immediate of the instruction).
+template <int BYTES, bool NT>
+__device__ __forceinline__ Chunk<BYTES> bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    constexpr int kPolicy = NT ? 2 : 0;  // the nt bit of the cache-policy operand
+    if constexpr (BYTES == 16) {
+        const nt_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicy);
+        return Chunk<16>{{v.x, v.y, v.z, v.w}};
+    } else if constexpr (BYTES == 8) {
+        const nt_u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicy);
+        return Chunk<8>{{v.x, v.y}};
+    } else {
+        static_assert(BYTES == 4, "buffer loads move chunks of 4, 8 or 16 bytes");
+        return Chunk<4>{{__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicy)}};
+    }
+}
+
 // ---- LDS ----------------------------------------------------------------
 template <int BYTES> __device__ __forceinline__ void lds_store(uint8_t *p, const Chunk<BYTES> &c) {
     if constexpr (BYTES == 16)

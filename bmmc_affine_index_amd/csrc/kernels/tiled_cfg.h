@@ -16,6 +16,11 @@ namespace bmmc {
 constexpr int kTileMaxNTL = 8;
 constexpr int kTileWideNTL = 9;
 
+// Buffer loads (bmmc_plan_options.buffer_loads) address the input by 32-bit
+// byte offsets within a buffer whose size field holds the array's bytes:
+// arrays of at most 2^31 bytes.
+constexpr int kBufferLoadMaxLog2 = 31;
+
 template <int UL, int T, int IT, int TL = kTileMaxNTL> struct TiledCfg {
     static constexpr int U = 1 << UL;
     static constexpr int WL = (4 - UL) < T ? (4 - UL) : T;  // log2 units per chunk

@@ -28,9 +28,9 @@ int execute_with_scratch(const bmmc_plan *p, const void *in, void *out, void *sc
 int noalloc_scratch(void **out);
 
 // Whether the tile kernel is compiled for this unit size, side, iteration
-// count, launch style and thread count.
+// count, launch style, thread count, staging and load form.
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2,
-                     int split_stage);
+                     int split_stage, int buffer_loads);
 
 // The dispatch packet gives the grid size in work-items as a 32-bit count,
 // so one launch covers at most 2^31 work-items here; bigger passes are split

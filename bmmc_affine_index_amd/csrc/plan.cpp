@@ -249,6 +249,7 @@ struct LaunchChoice {
     int cache_hint;    // descriptor value: 3 non-temporal loads and stores, 0 plain
     int threads_log2;  // most threads per tile, log2 (8 or 9)
     bool split;        // one-tile launch staging each tile in LDS half at a time
+    bool buffer_loads; // one-tile launch reading the input with buffer loads
 };
 
 // Highest set bit of a byte offset (-1 for 0).
@@ -708,6 +709,15 @@ int build_tiled(const Mat &A, u64 c, int ulog2, int a, int b, const std::vector<
         }
     }
     if (lc.split && d->launch != BMMC_LAUNCH_ONE_TILE) return BMMC_ERR_INVALID_ARG;
+    // Buffer loads address the input by 32-bit offsets from its base: whole
+    // tiles of 4-byte units or larger, one per workgroup, in arrays of at
+    // most 2^31 bytes (the offsets stay below the buffer's size limit).
+    if (lc.buffer_loads) {
+        if (d->launch != BMMC_LAUNCH_ONE_TILE || d->iters_log2 || d->split_stage ||
+            ulog2 < 2 || nb + ulog2 > kBufferLoadMaxLog2)
+            return BMMC_ERR_INVALID_ARG;
+        d->buffer_loads = 1;
+    }
     Basis vb, avb;  // the tile's span on the input side and on the output side
     for (int j = 0; j < a; ++j) vb.add(u64(1) << j);
     for (int j = 0; j < b; ++j) avb.add(u64(1) << j);
@@ -853,6 +863,14 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         return BMMC_ERR_INVALID_ARG;
     lc.split = o.split_stage == 1;
     if (lc.split) lc.persistent = 0;
+    // Buffer loads are a form of the one-tile launch of whole tiles.
+    if (o.buffer_loads < 0 || o.buffer_loads > 1) return BMMC_ERR_INVALID_ARG;
+    if (o.buffer_loads && (o.launch == BMMC_LAUNCH_PERSISTENT ||
+                           o.launch == BMMC_LAUNCH_STREAMED || o.iters_log2 != 0 ||
+                           o.split_stage))
+        return BMMC_ERR_INVALID_ARG;
+    lc.buffer_loads = o.buffer_loads == 1;
+    if (lc.buffer_loads) lc.persistent = 0;
     const int e = __builtin_ctzll((u64)elem_bytes);
     if (n + e > BMMC_MAX_BITS) return BMMC_ERR_INVALID_ARG;
     const u64 hi = ~low_mask(n);

@@ -5,8 +5,12 @@
 namespace bmmc {
 
 bool tiled_supported(int unit_log2, int t, int iters_log2, int launch, int threads_log2,
-                     int split_stage) {
+                     int split_stage, int buffer_loads) {
     if (unit_log2 < 0 || unit_log2 > 4 || t < 1) return false;
+    // buffer loads: one whole tile per workgroup, units of 4 bytes or more
+    if (buffer_loads && (buffer_loads != 1 || launch != BMMC_LAUNCH_ONE_TILE ||
+                         iters_log2 != 0 || split_stage != 0 || unit_log2 < 2))
+        return false;
     // split staging: one tile per workgroup, at least two passes per tile
     if (split_stage && (split_stage != 1 || launch != BMMC_LAUNCH_ONE_TILE || iters_log2 != 0 ||
                         2 * t - ((4 - unit_log2) < t ? (4 - unit_log2) : t) - threads_log2 < 1))

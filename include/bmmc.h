@@ -109,6 +109,14 @@ typedef struct bmmc_plan_options {
                         Not every matrix admits it at every tile shape
                         (BMMC_ERR_INVALID_ARG then); launch must be AUTO or ONE_TILE
                         and iters_log2 0. */
+    int buffer_loads; /* tile pass, one-tile launch of whole tiles only: 1 = read the
+                         input with buffer loads, whose per-lane address is a 32-bit
+                         offset from a base held in scalar registers, instead of
+                         64-bit global addresses (same bytes, same cache policy; which
+                         form is faster depends on the matrix); 0 = planner's choice
+                         (global loads).  Needs units of 4 bytes or more and an array
+                         of at most 2^31 bytes, launch AUTO or ONE_TILE, iters_log2 0
+                         and split_stage 0 (BMMC_ERR_INVALID_ARG otherwise). */
 } bmmc_plan_options;
 
 /* Tile orders of the persistent launch. */
@@ -208,6 +216,9 @@ typedef struct bmmc_pass_desc {
                              two halves, the chunks whose top chunk-index bit is h in
                              half h, on both the load and the drain side; lds_bytes is
                              then half a tile */
+    int32_t buffer_loads; /* TILED, one-tile launch: 1 = the input is read with buffer
+                             loads (32-bit offsets from the array's base; the array
+                             holds at most 2^31 bytes), 0 = global loads */
 } bmmc_pass_desc;
 
 typedef struct bmmc_plan bmmc_plan; /* opaque; changed after creation only by bmmc_plan_tune */
@@ -269,9 +280,12 @@ int bmmc_execute_noalloc(const bmmc_plan *plan, const void *in, void *out, void 
  * side on every launch style, orders 5 and 6), one tile per workgroup at the
  * planner's side with skew 0, 1, -1, 2 and -2 and 256 or 512 threads (orders
  * 5 and 6), and tiles staged in LDS half at a time (split_stage; skew 0, 1,
- * -1 and 2, 256 and 512 threads, order 5, where the matrix admits them): up
- * to 130 candidates, fewer where two build the same tables or where a
- * rectangular tile's shorter rows would hold less than 128 bytes.  An option the caller fixed at plan creation is kept.
+ * -1 and 2, 256 and 512 threads, order 5, where the matrix admits them), and
+ * for arrays of at most 2^31 bytes of 4-byte units or larger, each one-tile
+ * candidate of whole tiles again with buffer loads (buffer_loads): up to
+ * 130 candidates, and up to about 60 more with buffer loads, fewer where two
+ * build the same tables or where a rectangular tile's shorter rows would
+ * hold less than 128 bytes.  An option the caller fixed at plan creation is kept.
  * Each candidate runs `reps` times (0 = enough runs
  * for about 2 ms of work, 3 to 200) on `stream`, in five rounds that
  * interleave the candidates, timed with HIP events (for arrays below about

@@ -75,6 +75,21 @@ def check_persistent_walk(d):
         raise ReplayError("persistent walk does not visit every tile once")
 
 
+def check_buffer_loads(d) -> None:
+    """A pass that reads its input with buffer loads addresses it by 32-bit
+    offsets: one whole tile per workgroup, units of 4 bytes or more and at
+    most 2^31 bytes of array (the input offsets themselves are range-checked
+    with every other access)."""
+    bl = int(getattr(d, "buffer_loads", 0))
+    if bl not in (0, 1):
+        raise ReplayError("buffer_loads must be 0 or 1")
+    if bl and (d.launch != LAUNCH_ONE_TILE or d.iters_log2 != 0 or
+               int(getattr(d, "split_stage", 0)) or d.unit_log2 < 2 or
+               d.nbits + d.unit_log2 > 31):
+        raise ReplayError("buffer loads need one whole tile per workgroup, units of 4 bytes "
+                          "or more and at most 2^31 bytes")
+
+
 def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     """Source unit index of each output unit for one TILED pass."""
     ul, t, nb = d.unit_log2, d.t, d.nbits
@@ -89,6 +104,7 @@ def replay_tiled(d, check_coalescing: bool = True) -> np.ndarray:
     split = int(getattr(d, "split_stage", 0))
     if split not in (0, 1):
         raise ReplayError("split_stage must be 0 or 1")
+    check_buffer_loads(d)
     if d.launch in (LAUNCH_PERSISTENT, LAUNCH_STREAMED):
         if d.lds_bytes != 2 * TILE or d.iters_log2 != 0:
             raise ReplayError("persistent launch needs two LDS tiles")
@@ -349,6 +365,7 @@ def check_pass_sampled(d, A, c, elem_log2: int, blocks, map_indices) -> int:
     if split and (d.launch != LAUNCH_ONE_TILE or d.iters_log2 != 0 or 2 * d.lds_bytes != TILE
                   or jl < 1):
         raise ReplayError("split staging needs a one-tile launch, half a tile of LDS and two passes")
+    check_buffer_loads(d)
     LT = TILE >> split  # LDS bytes of one staging
     cidx = np.arange(NT * J, dtype=np.uint64)
     ld_in = _xor_table(cidx, d.ld_in, cbits)

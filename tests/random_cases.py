@@ -21,10 +21,12 @@ ELEMS = (1, 2, 4, 8, 16)
 N_SQUARE = 600
 N_SKEW = 180   # rectangular tiles (tile_skew), drawn from a stream of their own
 N_SPLIT = 160  # one-tile launches staged in LDS half at a time (split_stage)
-N_CASES = N_SQUARE + N_SKEW + N_SPLIT
+N_BUF = 120    # one-tile launches that read the input with buffer loads (buffer_loads)
+N_CASES = N_SQUARE + N_SKEW + N_SPLIT + N_BUF
 MASTER_SEED = 0x5EED_B44C
 SKEW_SEED = 0x5EED_5CE7
 SPLIT_SEED = 0x5EED_5B17
+BUF_SEED = 0x5EED_B0FF
 
 
 @dataclass
@@ -189,6 +191,47 @@ def cases():
                 if not skew:
                     break
                 skew -= 1 if skew > 0 else -1
+        out.append(case)
+    # buffer loads: one-tile launches of whole tiles whose input is read by
+    # 32-bit offsets, over both routes, tile shapes, thread counts and orders;
+    # mostly units of 4 bytes or more (1- and 2-byte elements get there when
+    # the matrix keeps low bits); a case the library refuses them for is kept
+    # without
+    rng = np.random.Generator(np.random.PCG64(BUF_SEED))
+    for i in range(N_BUF):
+        kind = tiled_kinds[int(rng.integers(len(tiled_kinds)))]
+        elem = int(rng.choice([1, 2, 4, 4, 8, 16, 16]))
+        n = int(rng.integers(10, 19))
+        opts = {}
+        route = int(rng.choice([bm.ROUTE_AUTO, bm.ROUTE_FUSED, bm.ROUTE_TWO_PASS]))
+        if route:
+            opts["route"] = route
+        if rng.random() < 0.5:
+            opts["launch"] = bm.LAUNCH_ONE_TILE
+        t = int(rng.choice([0, 0, 4, 5, 6, 7]))
+        if t:
+            opts["tile_log2"] = t
+        bmap = int(rng.choice([0, 1, 2, 3, 5, 6, 8, 12]))
+        if bmap:
+            opts["block_map"] = bmap
+        hint = int(rng.choice([0, 0, 1, 2]))
+        if hint:
+            opts["cache_hint"] = hint
+        if rng.random() < 0.1:
+            opts["no_swizzle"] = 1
+        if rng.random() < 0.4:
+            opts["tile_threads_log2"] = 9
+        skew = int(rng.choice([0, 0, 1, -1, 2, -2])) if route != bm.ROUTE_TWO_PASS else 0
+        if skew:
+            opts["tile_skew"] = skew
+        case = Case(N_SQUARE + N_SKEW + N_SPLIT + i, kind, n, elem,
+                    int(rng.integers(1, 1 << 30)), opts)
+        A, c = case.matrix()
+        try:
+            bm.Plan(n, A, c, elem, buffer_loads=1, **opts)
+            case.options["buffer_loads"] = 1
+        except bm.BmmcError:
+            pass
         out.append(case)
     return out
 

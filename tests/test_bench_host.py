@@ -142,7 +142,7 @@ def test_sampled_parity_on_host_tensors():
         assert bad >= 2
 
 
-def test_plan_label_names_shape_threads_and_split():
+def test_plan_label_names_shape_threads_split_and_loads():
     import bmmc_affine_index_amd as bm
     from bmmc_affine_index_amd import workloads as wl
     P = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4, split_stage=1, tile_log2=7,
@@ -154,6 +154,10 @@ def test_plan_label_names_shape_threads_and_split():
     assert bench.plan_label(R.describe()) == "chunk_scatter"
     brief = bench.plan_brief(P)
     assert brief["tile_threads"] == 512 and brief["split_stage"] == 1 and brief["tile_skew"] == 1
+    assert brief["buffer_loads"] == 0
+    B = bm.Plan(20, wl.bit_reverse_matrix(20), 0, 4, buffer_loads=1, tile_log2=6, block_map=8)
+    assert bench.plan_label(B.describe()) == "one_tile t=6 skew 0 buffer loads order 8"
+    assert bench.plan_brief(B)["buffer_loads"] == 1
 
 
 def test_frontend_cases_are_one_gib_and_plan_on_the_host():

@@ -398,7 +398,9 @@ def test_workload_full_check(name):
         assert np.array_equal(A, wl.workload_matrix(name, accept=_lib_accepts(n))[0])
     x = wl.workload_data(name)
     want = oracle.apply(A, c, x, threads=HOST_THREADS)
-    routes = [{}, dict(tune=True)] + ([dict(route=bm.ROUTE_TWO_PASS)] if name == "c1a" else [])
+    routes = [{}, dict(tune=True), dict(buffer_loads=1)] + (
+        [dict(route=bm.ROUTE_TWO_PASS), dict(route=bm.ROUTE_TWO_PASS, buffer_loads=1)]
+        if name == "c1a" else [])
     for kw in routes:
         _note("%s %s" % (name, kw))
         got, P = _device_run(name, A, c, x, **kw)
@@ -427,6 +429,14 @@ def test_workload_c3_bitrev28_full():
         _note("c3: gpu split %s" % kw)
         got, P = _device_run(name, A, c, x, split_stage=1, **kw)
         assert P.describe()["split_stage"] == 1
+        assert np.array_equal(got, want), P.describe()
+        del got
+    # the input read with buffer loads
+    for kw in (dict(), dict(tile_log2=7, tile_skew=1, tile_threads_log2=9),
+               dict(tile_log2=6, tile_skew=-1, block_map=8)):
+        _note("c3: gpu buffer loads %s" % kw)
+        got, P = _device_run(name, A, c, x, buffer_loads=1, **kw)
+        assert P.describe()["buffer_loads"] == 1
         assert np.array_equal(got, want), P.describe()
         del got
 
@@ -475,6 +485,42 @@ def test_workload_c4_every_tuning_candidate():
         got = d_out.view(torch.int32).index_select(0, pos).cpu().numpy().view(x.dtype)
         bad = np.flatnonzero(got != want)
         assert bad.size == 0, (k, opts, int(idx[bad[0]]), P.describe())
+
+
+def test_workload_c5_buffer_loads():
+    """c5's slowest permutation (10) with the input read by buffer loads:
+    the whole 2 GiB array (the largest the form allows) against the oracle
+    for two shapes, and every buffer-load plan the tuning would time on
+    sampled indices."""
+    torch = _torch()
+    name = "c5"
+    n = 27
+    x = wl.workload_data(name)
+    A, c = wl.workload_matrix(name, perm_index=10)
+    d_in = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    d_out = torch.empty_like(d_in)
+    want = oracle.apply(A, c, x, threads=HOST_THREADS).view(np.uint32).reshape(-1)
+    for kw in (dict(tile_log2=5, tile_skew=2, tile_threads_log2=9), dict()):
+        _note("c5 perm 10 buffer loads %s" % kw)
+        P = bm.Plan(n, A, c, 16, buffer_loads=1, **kw)
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(d_out.cpu().numpy().view(np.uint32), want), P.describe()
+    del want
+    idx = _sample_idx(n, 1 << 18, 32)
+    pos = torch.from_numpy(oracle.map_indices(A, c, idx).astype(np.int64)).to("cuda:0")
+    exp = torch.from_numpy(x.reshape(1 << n, 4)[idx.astype(np.int64)].view(np.int32)).to("cuda:0")
+    cands = [o for o in bm.Plan(n, A, c, 16).tune_candidates() if o["buffer_loads"]]
+    assert len(cands) >= 20
+    for k, opts in enumerate(cands):
+        _note("c5 perm 10 buffer-load candidate %d %s" % (k, opts))
+        P = bm.Plan(n, A, c, 16, **opts)
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        got = d_out.view(torch.int32).view(1 << n, 4).index_select(0, pos)
+        assert bool((got == exp).all()), (k, opts, P.describe())
+    del d_in, d_out
 
 
 _C5_DATA = {}
@@ -529,6 +575,12 @@ GPU_MAX_CASES = [  # (n, elem_bytes, kind, plan options, tune)
     (32, 4, "bitrev", dict(split_stage=1, tile_log2=7), False),          # 16 GiB
     (31, 8, "bpc", dict(split_stage=1, tile_threads_log2=9), False),     # 16 GiB
     (32, 16, "general", dict(split_stage=1, tile_skew=1), False),        # 64 GiB
+    # the input read with buffer loads, at the 2^31 bytes they allow
+    (29, 4, "general", dict(buffer_loads=1), False),
+    (28, 8, "bitrev", dict(buffer_loads=1, tile_skew=1), False),
+    (27, 16, "bpc", dict(buffer_loads=1, tile_log2=5, tile_skew=2, tile_threads_log2=9),
+     False),
+    (29, 4, "general", {}, True),   # tuned: the buffer-load candidates included
 ]
 
 

@@ -727,7 +727,7 @@ def test_tune_candidates_rebuild_distinct_plans():
         P = bm.Plan(w.n, A, c, w.elem_bytes)
         cands = bm.bmmc_plan_tune_candidates(P.handle)
         assert P.tune_candidates() == cands
-        assert 20 <= len(cands) <= 130
+        assert 20 <= len(cands) <= 160
         digests = set()
         for k, o in enumerate(cands):
             Q = bm.Plan(w.n, A, c, w.elem_bytes, **o)
@@ -739,6 +739,12 @@ def test_tune_candidates_rebuild_distinct_plans():
         assert {o["tile_skew"] for o in cands} >= {0, 1, -1, 2, -2}
         assert {o["tile_threads_log2"] for o in cands} == {8, 9}
         assert {o["split_stage"] for o in cands} == {0, 1}
+        # buffer loads where the array holds at most 2^31 bytes (c4 holds 2^32)
+        assert {o["buffer_loads"] for o in cands} == ({0} if name == "c4" else {0, 1})
+        for o in cands:
+            if o["buffer_loads"]:
+                assert o["launch"] == bm.LAUNCH_ONE_TILE and o["split_stage"] == 0
+                assert dict(o, buffer_loads=0) in cands
     R = bm.Plan(12, wl.identity_matrix(12), 5, 4)
     assert bm.bmmc_plan_tune_candidates(R.handle) == []
 
@@ -865,9 +871,105 @@ def test_split_replay_catches_planted_mistakes():
         replay_pass(bad)
 
 
+# --------------------------------------------------------------------------
+# Buffer loads: one-tile launches that read the input by 32-bit offsets
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(launch=bm.LAUNCH_PERSISTENT), dict(launch=bm.LAUNCH_STREAMED),
+    dict(launch=bm.LAUNCH_ONE_TILE, iters_log2=1), dict(split_stage=1)])
+def test_buffer_loads_need_one_whole_tile_per_workgroup(kw):
+    A, c = wl.random_bmmc(20, 5, lambda r: oracle.rank(r) == 20)
+    with pytest.raises(bm.BmmcError) as e:
+        bm.Plan(20, A, c, 4, buffer_loads=1, **kw)
+    assert e.value.status == bm.ERR_INVALID_ARG
+
+
+def test_buffer_loads_argument_errors():
+    A = wl.bit_reverse_matrix(20)
+    for bad in (-1, 2):
+        with pytest.raises(bm.BmmcError) as e:
+            bm.Plan(20, A, 0, 4, buffer_loads=bad)
+        assert e.value.status == bm.ERR_INVALID_ARG
+    # units of 1 and 2 bytes (bit reversal merges no element bits into a unit)
+    for elem in (1, 2):
+        with pytest.raises(bm.BmmcError) as e:
+            bm.Plan(20, A, 0, elem, buffer_loads=1)
+        assert e.value.status == bm.ERR_INVALID_ARG
+    # 32-bit offsets: arrays of at most 2^31 bytes
+    with pytest.raises(bm.BmmcError) as e:
+        bm.Plan(30, wl.bit_reverse_matrix(30), 0, 4, buffer_loads=1)
+    assert e.value.status == bm.ERR_INVALID_ARG
+    with pytest.raises(bm.BmmcError) as e:
+        bm.Plan(28, wl.bit_reverse_matrix(28), 0, 16, buffer_loads=1)
+    assert e.value.status == bm.ERR_INVALID_ARG
+    for n, elem in ((29, 4), (27, 16), (28, 8)):
+        P = bm.Plan(n, wl.bit_reverse_matrix(n), 0, elem, buffer_loads=1)
+        d = P.passes()[0]
+        assert d.buffer_loads == 1 and d.launch == bm.LAUNCH_ONE_TILE
+        assert d.nbits + d.unit_log2 == 31
+    # the launch left to the planner becomes one tile per workgroup
+    P = bm.Plan(20, A, 0, 4, buffer_loads=1)
+    assert P.describe()["kernels"] == ["one_tile"] and P.describe()["buffer_loads"] == 1
+
+
+@pytest.mark.parametrize("kind,n,e,kw", [
+    ("bitrev", 18, 4, dict(tile_log2=7)),
+    ("bitrev", 18, 4, dict(tile_log2=7, tile_skew=1, tile_threads_log2=9)),
+    ("general", 20, 4, {}),
+    ("general", 19, 8, dict(tile_skew=-1)),
+    ("bpc", 18, 16, dict(tile_log2=5, tile_skew=2, tile_threads_log2=9)),
+    ("transpose", 18, 4, dict(block_map=8)),
+    ("general", 16, 4, dict(route=bm.ROUTE_TWO_PASS)),
+    ("general", 17, 8, dict(cache_hint=1, block_map=9)),
+])
+def test_buffer_load_plans_replay(kind, n, e, kw):
+    """A buffer-load plan has the tables of the global-load plan of the same
+    options (only the load form differs), replays to the oracle's
+    permutation on the host, and its options rebuild it."""
+    A, c = _max_matrix(kind, n, 60 + n)
+    P = bm.Plan(n, A, c, e, buffer_loads=1, **kw)
+    G = bm.Plan(n, A, c, e, launch=bm.LAUNCH_ONE_TILE, **kw)
+    tiled = [d for d in P.passes() if d.kernel == bm.KERNEL_TILED]
+    assert tiled and all(d.buffer_loads == 1 for d in tiled)
+    plain = []
+    for d in P.passes():
+        q = bm.bmmc_pass_desc.from_buffer_copy(d)
+        q.buffer_loads = 0
+        plain.append(_desc_bytes(q))
+    assert plain == [_desc_bytes(d) for d in G.passes()]
+    x = wl.fill_random_bytes(n, e, 78)
+    assert np.array_equal(run_plan_on_host(P, x), oracle.apply(A, c, x))
+    o = P.options()
+    assert o["buffer_loads"] == 1
+    Q = bm.Plan(n, A, c, e, **o)
+    assert [_desc_bytes(d) for d in Q.passes()] == [_desc_bytes(d) for d in P.passes()]
+
+
+def test_buffer_load_replay_rejects_bad_descriptors():
+    """The replay refuses buffer loads on a launch or an array they do not
+    serve."""
+    from emulate import replay_pass
+    A, c = wl.random_bmmc(18, 3, lambda r: oracle.rank(r) == 18)
+    d = bm.Plan(18, A, c, 4, buffer_loads=1).passes()[0]
+    replay_pass(d)
+    for field, value in (("buffer_loads", 2), ("iters_log2", 1), ("unit_log2", 1),
+                         ("nbits", 30)):
+        bad = bm.bmmc_pass_desc.from_buffer_copy(d)
+        setattr(bad, field, value)
+        with pytest.raises(ReplayError):
+            replay_pass(bad)
+    P = bm.Plan(18, A, c, 4, launch=bm.LAUNCH_PERSISTENT)
+    bad = bm.bmmc_pass_desc.from_buffer_copy(P.passes()[0])
+    bad.buffer_loads = 1
+    with pytest.raises(ReplayError):
+        replay_pass(bad)
+
+
 @pytest.mark.parametrize("fixed", [
     dict(launch=bm.LAUNCH_STREAMED), dict(tile_skew=1), dict(tile_threads_log2=9),
-    dict(split_stage=1), dict(block_map=6), dict(route=bm.ROUTE_TWO_PASS), dict(tile_log2=6)])
+    dict(split_stage=1), dict(block_map=6), dict(route=bm.ROUTE_TWO_PASS), dict(tile_log2=6),
+    dict(buffer_loads=1)])
 def test_tune_candidates_keep_what_the_caller_fixed(fixed):
     """Every candidate keeps an option the caller set at plan creation; the
     options left open still vary."""
@@ -890,4 +992,8 @@ def test_tune_candidates_keep_what_the_caller_fixed(fixed):
     if "split_stage" in fixed:
         assert {o["launch"] for o in cands} == {bm.LAUNCH_ONE_TILE}
     if fixed.get("launch") == bm.LAUNCH_STREAMED:
+        assert {o["split_stage"] for o in cands} == {0}
+        assert {o["buffer_loads"] for o in cands} == {0}
+    if "buffer_loads" in fixed:
+        assert {o["launch"] for o in cands} == {bm.LAUNCH_ONE_TILE}
         assert {o["split_stage"] for o in cands} == {0}

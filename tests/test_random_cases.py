@@ -20,7 +20,7 @@ def test_cases_are_fixed_and_span_the_options():
     seen = {k for c in a for k in c.options}
     assert {"route", "launch", "tile_log2", "block_map", "iters_log2", "grid_log2", "walk",
             "depth", "cache_hint", "no_swizzle", "tile_skew", "tile_threads_log2",
-            "split_stage"} <= seen
+            "split_stage", "buffer_loads"} <= seen
     skews = {c.options.get("tile_skew", 0) for c in a}
     assert {1, -1, 2, -2} <= skews
     split = [c for c in a if c.options.get("split_stage")]
@@ -34,6 +34,16 @@ def test_cases_are_fixed_and_span_the_options():
         P = bm.Plan(c.n, A, cc, c.elem, **c.options)
         staged_in_halves += any(d.kernel == bm.KERNEL_TILED and d.split_stage for d in P.passes())
     assert staged_in_halves >= 80
+    buf = [c for c in a if c.options.get("buffer_loads")]
+    assert len(buf) >= 80
+    assert {c.options.get("route", 0) for c in buf} >= {0, 2, 3}
+    assert {c.options.get("tile_skew", 0) for c in buf} >= {0, 1, -1, 2, -2}
+    assert {c.options.get("tile_threads_log2", 0) for c in buf} == {0, 9}
+    assert {c.elem for c in buf} >= {4, 8, 16}
+    for c in buf:
+        A, cc = c.matrix()
+        P = bm.Plan(c.n, A, cc, c.elem, **c.options)
+        assert all(d.buffer_loads == 1 for d in P.passes() if d.kernel == bm.KERNEL_TILED)
     assert {c.kind for c in a} == {"general", "bpc", "bitrev", "transpose", "complement",
                                    "blockperm", "lowkeep"}
     assert {c.elem for c in a} == {1, 2, 4, 8, 16}
