@@ -176,3 +176,105 @@ def test_frontend_cases_are_one_gib_and_plan_on_the_host():
         P = bm.Plan(n, A, c, (4 << 28) >> n)
         assert P.info.kind in (bm.KIND_BPC, bm.KIND_IDENTITY)
         assert P.info.passes == 1
+
+
+def _write_counter_csv(path, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+            "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+            "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+            "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for k, (name, counter, value) in enumerate(rows):
+            r = dict.fromkeys(cols, "0")
+            r.update(Dispatch_Id=str(k + 1), Process_Id="7", Kernel_Name=name,
+                     Counter_Name=counter, Counter_Value=repr(value))
+            w.writerow([r[c] for c in cols])
+
+
+def test_traffic_summary_round_trip(tmp_path, monkeypatch):
+    """bench_profiles.py turns two counter runs of --candidates into entries
+    that read_traffic finds for exactly the plans counted: copies separate
+    the candidates, torch's kernels are left out, each counter is scaled by
+    the copy's reading, and the dispatches of a candidate are averaged over
+    its timed runs and its parity run."""
+    import bench_profiles
+    nbytes = 1 << 26
+    A, c = wl.workload_matrix("c2")
+    P = bm.Plan(24, A, c, 4)
+    cands = []
+    for k, o in enumerate(bm.bmmc_plan_tune_candidates(P.handle)[:3]):
+        Q = bm.Plan(24, A, c, 4, **o)
+        cands.append({"index": k, "plan_options": Q.options(),
+                      "plan_tables_digest": bench.plan_tables_digest(Q),
+                      "kernels": Q.describe()["kernels"], "parity": "bit-exact"})
+    line = {"workload": "transpose4096x4096_fp32_n24",
+            "kernel_source_digest": bench.kernel_source_digest(), "bytes": nbytes,
+            "runs_per_candidate": 3, "candidates": cands}
+    copy_read_kib, copy_write_kib = nbytes / 2048.0, nbytes / 1024.0  # reads counted at half
+    dirs = []
+    for counter, copy_kib in (("FETCH_SIZE", copy_read_kib), ("WRITE_SIZE", copy_write_kib)):
+        d = tmp_path / counter
+        rows = [("at::native::fill", counter, 123.0)]
+        for k in range(len(cands)):
+            rows.append(("bmmc::bmmc_copy_kernel<0>", counter, copy_kib))
+            for _ in range(4):  # 3 timed runs + the parity run
+                rows.append(("bmmc::bmmc_tiled_kernel<2, 7, 0, true, 8>", counter,
+                             copy_kib * (1.0 + 0.01 * k)))
+                rows.append(("at::native::vectorized_gather_kernel", counter, 99.0))
+        _write_counter_csv(str(d / "host" / "run_counter_collection.csv"), rows)
+        (d / "candidates.json").write_text("log line\n" + json.dumps(line) + "\n")
+        dirs.append(str(d))
+    text = bench_profiles.traffic_summary("c2", [tuple(dirs)], ["cmd"])
+    assert text.count("[entry]") == 3
+    f = tmp_path / "hbm_traffic_c2.txt"
+    f.write_text(text)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic_%s.txt"))
+    for k, cand in enumerate(cands):
+        got = bench.read_traffic("c2", cand["plan_options"], cand["plan_tables_digest"])
+        assert got == pytest.approx(2 * nbytes * (1.0 + 0.01 * k), rel=1e-6)
+    # a plan that was not counted has no traffic
+    assert bench.read_traffic("c2", cands[0]["plan_options"], "0" * 16) is None
+    # candidates that do not match the runs' copies are refused
+    bad = dict(line, candidates=cands[:2])
+    (tmp_path / "FETCH_SIZE" / "candidates.json").write_text(json.dumps(bad) + "\n")
+    (tmp_path / "WRITE_SIZE" / "candidates.json").write_text(json.dumps(bad) + "\n")
+    with pytest.raises(SystemExit):
+        bench_profiles.traffic_summary("c2", [tuple(dirs)], ["cmd"])
+
+
+def test_trace_summary_finds_the_timed_window(tmp_path):
+    """The headline's timed dispatches are the steps x replays library
+    dispatches right before the copy ceiling's first run of warm-up + upload
+    + timed copies of one grid."""
+    import csv
+    import bench_profiles
+    steps, warmup, replays = 4, 2, 3
+    disp = [("bmmc::bmmc_copy_kernel<0>", 32, 100)] * 500  # a smaller array's copies
+    disp += [("bmmc::bmmc_tiled_kernel<2, 6, 0, true, 9>", 64, 5000)] * 7  # tuning
+    disp += [("bmmc::bmmc_tiled_kernel<2, 6, 0, true, 8>", 64, 1000)] * (warmup + steps)
+    disp += [("at::native::fill", 8, 10)]
+    disp += [("bmmc::bmmc_tiled_kernel<2, 6, 0, true, 8>", 64, 2000 + k)
+             for k in range(replays * steps)]
+    disp += [("bmmc::bmmc_copy_kernel<0>", 128, 1400)] * warmup
+    disp += [("at::native::fill", 8, 10)]
+    disp += [("bmmc::bmmc_copy_kernel<0>", 128, 1500)] * steps
+    disp += [("bmmc::bmmc_copy_kernel<0>", 128, 1600 + k) for k in range(replays * steps)]
+    disp += [("bmmc::bmmc_copy_kernel<0>", 32, 100)] * 50
+    d = tmp_path / "trace"
+    os.makedirs(d / "h")
+    with open(d / "h" / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Grid_Size_Y",
+                    "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for k, (name, grid, dur) in enumerate(disp):
+            w.writerow(["KERNEL_DISPATCH", k + 1, name, grid, 1, 1, t, t + dur])
+            t += dur + 10
+    timed, copies = bench_profiles.headline_window(
+        bench_profiles.trace_dispatches(str(d)), steps, warmup, replays, 128)
+    assert [t for _, _, t in timed] == [2000 + k for k in range(replays * steps)]
+    assert [t for _, _, t in copies] == [1600 + k for k in range(replays * steps)]
