@@ -340,7 +340,10 @@ def trace_summary(d: str, commands) -> str:
         out.append("| `%s` | %d | %.2f | %.2f | %.2f |" % (short_name(name), calls, avg_ns / 1e3,
                                                          mn / 1e3, mx / 1e3))
     if "configs" in b:
-        out += ["", "**Configurations of the same run** (its `configs` object):", "",
+        out += ["", "**Configurations of the same run** (its `configs` object; under the tracer "
+                "each dispatch carries the profiler's own cost, which the arrays of a few MiB "
+                "(c1) feel most: their kernels and their copy alike run several times slower "
+                "than untraced, so their fractions here are not the bench line's):", "",
                 "| configuration | plan | GB/s (median of 5) | frac of copy | frac of 8 TB/s "
                 "| parity |", "|---|---|---|---|---|---|"]
         for key, e in b["configs"].items():
