@@ -34,7 +34,16 @@ constexpr int kChunkNTL = 8;  // 256 threads
 // (more, smaller workgroups; the copy ceiling behaves the same way).
 constexpr int kChunkCPTL = 0;
 
-template <int UL, int WL, bool NT, bool GATHER>
+// Gathers of at most 2^(kChunkNTL + kSmallChunkBlkBits) chunks (16 MiB of
+// 16-byte chunks) have a variant that takes the workgroup's source base from
+// scalar loads of the table entries above the lane bits, all issued with the
+// pass's other parameters and then selected by the workgroup's index bits, so
+// that the data loads wait for one round trip in all (as the copy's do).  The
+// wave's vector load of the table costs a second round trip, which a pass of
+// a few microseconds pays in full.
+constexpr int kSmallChunkBlkBits = 12;
+
+template <int UL, int WL, bool NT, bool GATHER, bool SB = false>
 __global__ void __launch_bounds__(1 << kChunkNTL)
     bmmc_chunk_kernel(const uint8_t *__restrict__ in, uint8_t *__restrict__ out,
                       const bmmc_pass_desc d, uint64_t blk0) {
@@ -42,10 +51,32 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
     constexpr int W = 1 << WL;
     constexpr int CB = U << WL;
     constexpr int CPT = 1 << kChunkCPTL;
+    static_assert(!SB || GATHER, "the scalar form serves gathers");
     const uint32_t tid = threadIdx.x;
     const uint64_t nchunks = uint64_t(1) << d.blk_bits;
-    const uint64_t first = (blk0 + blockIdx.x) << (kChunkNTL + kChunkCPTL);
     const uint64_t *tab = GATHER ? d.in_blk : d.out_blk;
+    uint64_t b0 = blk0;
+    uint64_t e[SB ? kSmallChunkBlkBits : 1];
+    if constexpr (SB) {
+#pragma unroll
+        for (int k = 0; k < kSmallChunkBlkBits; ++k) e[k] = d.in_blk[kChunkNTL + k];
+        // An empty asm that takes every entry, the lane bits' entries and the
+        // input pointer keeps their loads here, where they wait together with
+        // the parameters'; blk0 passes through it, so that nothing computed
+        // from it is scheduled between the loads (the compiler would otherwise
+        // wait for the first loads before issuing the rest, or issue the lane
+        // bits' loads behind the guard on the array's end: a second round
+        // trip either way).
+        static_assert(kSmallChunkBlkBits == 12 && kChunkNTL == 8, "operand list below");
+        asm volatile(""
+                     : "+s"(b0)
+                     : "s"(e[0]), "s"(e[1]), "s"(e[2]), "s"(e[3]), "s"(e[4]), "s"(e[5]),
+                       "s"(e[6]), "s"(e[7]), "s"(e[8]), "s"(e[9]), "s"(e[10]), "s"(e[11]),
+                       "s"(tab[0]), "s"(tab[1]), "s"(tab[2]), "s"(tab[3]), "s"(tab[4]),
+                       "s"(tab[5]), "s"(tab[6]), "s"(tab[7]), "s"(in), "s"(d.in_c),
+                       "s"(d.blk_bits));
+    }
+    const uint64_t first = (b0 + blockIdx.x) << (kChunkNTL + kChunkCPTL);
     const uint64_t lane_off = dev::xor_bits_lane<kChunkNTL>(tab, tid);
     // A gather needs the wave-uniform part of each group's source offset
     // before its loads: the whole wave computes it (lane k loads entry k, a
@@ -56,7 +87,16 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
     // computes its output base from scalar loads after issuing its loads,
     // which hides them (the wave form cost a 4 MiB reversal 10%).
     uint64_t ubase[CPT] = {};
-    if constexpr (GATHER) {
+    if constexpr (SB) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const uint64_t xu = (first + ((uint64_t)k << kChunkNTL)) >> kChunkNTL;
+            uint64_t acc = d.in_c;
+#pragma unroll
+            for (int b = 0; b < kSmallChunkBlkBits; ++b) acc ^= ((xu >> b) & 1u) ? e[b] : 0;
+            ubase[k] = acc;
+        }
+    } else if constexpr (GATHER) {
         const uint64_t entry = dev::wave_load(tab);
 #pragma unroll
         for (int k = 0; k < CPT; ++k)
@@ -112,7 +152,10 @@ int launch_chunk_t(const bmmc_pass_desc &d, const uint8_t *in, uint8_t *out, hip
         const uint64_t nb = blocks - b0 < per ? blocks - b0 : per;
         // chunk passes gather, chunk scatters scatter, both with non-temporal
         // hints; the naive pass scatters with plain accesses
-        if (d.kernel == BMMC_KERNEL_CHUNK)
+        if (d.kernel == BMMC_KERNEL_CHUNK && d.blk_bits <= kChunkNTL + kSmallChunkBlkBits)
+            hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL, true, true, true>), dim3((uint32_t)nb),
+                               dim3(1 << kChunkNTL), 0, s, in, out, d, b0);
+        else if (d.kernel == BMMC_KERNEL_CHUNK)
             hipLaunchKernelGGL((bmmc_chunk_kernel<UL, WL, true, true>), dim3((uint32_t)nb),
                                dim3(1 << kChunkNTL), 0, s, in, out, d, b0);
         else if (d.kernel == BMMC_KERNEL_CHUNK_SCATTER)
