@@ -132,6 +132,43 @@ def test_small_parity(case):
     assert np.array_equal(got, want), P.describe()
 
 
+def _block_permutation(n, seg_log2, seed):
+    """A BMMC that moves whole segments of 2^seg_log2 elements: the identity on
+    the low bits, a random invertible matrix on the segment index."""
+    Q, _ = _inv(n - seg_log2, seed)
+    return np.array([1 << r for r in range(seg_log2)] + [int(q) << seg_log2 for q in Q],
+                    dtype=np.uint64)
+
+
+# Chunk gathers on both sides of the size up to which a workgroup takes its
+# source base from scalar loads (2^20 chunks), and below one workgroup.
+CHUNK_BOUNDARY = [(16, 7, 5), (16, 9, 6), (16, 20, 6), (16, 21, 6), (4, 22, 8), (4, 23, 8),
+                  (1, 24, 10), (1, 25, 10), (8, 20, 7), (2, 23, 9)]
+
+
+@pytest.mark.parametrize("case", CHUNK_BOUNDARY, ids=lambda c: "e%d-n%d-seg%d" % c)
+def test_chunk_gather_size_boundary(case):
+    e, n, sl = case
+    A = _block_permutation(n, sl, 40 + n)
+    c = (5 << sl) & ((1 << n) - 1)
+    x = wl.fill_random_bytes(n, e, seed=900 + n)
+    _note("chunk gather e=%d n=%d seg=%d" % case)
+    got, P = _run(A, c, x)
+    assert P.describe()["kernels"] == ["chunk"], P.describe()
+    assert np.array_equal(got, oracle.apply(A, c, x)), P.describe()
+
+
+@pytest.mark.parametrize("n", [22, 23])
+def test_two_pass_relabel_size_boundary(n):
+    """The two-pass route's segment relabel just inside and just past 2^20
+    chunks."""
+    A, c = _inv(n, 3)
+    x = wl.fill_index_int32(n)
+    got, P = _run(A, c, x, route=bm.ROUTE_TWO_PASS)
+    assert P.info.passes == 2
+    assert np.array_equal(got, oracle.apply(A, c, x)), P.describe()
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_general_sweep(seed):
     """Random sizes and matrices over both general routes."""
