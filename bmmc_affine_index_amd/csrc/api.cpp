@@ -185,6 +185,22 @@ int tune_candidates(const bmmc_plan *p, std::vector<std::unique_ptr<bmmc_plan>> 
                     const int st = add(o);
                     if (st != BMMC_OK) return st;
                 }
+    // rectangular tiles at the planner's side on the planner's launch, with
+    // the output-dense order and a random one (measured on MI355X: bit
+    // reversal of 4 MiB on the streamed launch +1.1-1.6% with output rows half
+    // as long; 512 threads per tile there lost 7%)
+    if (!p->opt.tile_skew && tiles.size() > 1 && p->opt.route != BMMC_ROUTE_TWO_PASS &&
+        p->opt.route != BMMC_ROUTE_NAIVE)
+        for (int skew : {1, -1})
+            for (int m : {bmmc::kDefaultBlockMap, 9}) {
+                if (p->opt.block_map && m != p->opt.block_map) continue;
+                bmmc_plan_options o = p->opt;
+                o.tile_log2 = tiles.front();
+                o.block_map = m;
+                o.tile_skew = skew;
+                const int st = add(o);
+                if (st != BMMC_OK) return st;
+            }
     // 512 threads per tile at the larger side (twice the waves per SIMD to
     // hide the latency between a tile's loads and its stores), square and
     // with the output rows 2 or 4 times as long or as short, on every launch
