@@ -132,27 +132,30 @@ u64 pad_rows(const Mat &A, u64 S, int a, int b, bool near_out) {
 }
 
 // The pages' factorisation route, rebuilt from the algebra: with B = A^{-1},
-// take an independent subset of the high parts of B's first t columns and
-// complete it by unit vectors to a basis Q_hh of the high coordinates.  With
-// Q = diag(I_t, Q_hh): T2 = Q^{-1} only relabels 2^t-unit segments, and
-// T1 = A.Q has its tile rows inside {t, ..., 2t-1}, because Q^{-1} maps each
-// such high part into the span of the first chosen vectors.  A = T1.T2.
-bool factorize(const Mat &A, int t, Mat &T1, Mat &T2) {
+// take an independent subset of the high parts (above the a in-row bits) of
+// B's first b columns and complete it by unit vectors to a basis Q_hh of the
+// high coordinates.  With Q = diag(I_a, Q_hh): T2 = Q^{-1} only relabels
+// 2^a-unit segments, and T1 = A.Q is tiled with input rows of 2^a units and
+// output rows of 2^b, its tile rows inside {a, ..., a+b-1}: T1^{-1} = Q^{-1}.B
+// keeps the low parts of B's first b columns and maps each high part into the
+// span of the first chosen vectors, at most b of them.  A = T1.T2.  The
+// pages' tiles are square (a = b = t).
+bool factorize(const Mat &A, int a, int b, Mat &T1, Mat &T2) {
     const int n = A.rows;
     Mat B;
     if (!inverse(A, B)) return false;
     Basis chosen;
     std::vector<u64> qcols;
-    for (int j = 0; j < t; ++j) {
-        u64 v = B.col(j) & ~low_mask(t);
+    for (int j = 0; j < b; ++j) {
+        u64 v = B.col(j) & ~low_mask(a);
         if (chosen.add(v)) qcols.push_back(v);
     }
     Basis all = chosen;
-    for (int m = t; m < n; ++m)
+    for (int m = a; m < n; ++m)
         if (all.add(u64(1) << m)) qcols.push_back(u64(1) << m);
-    if ((int)qcols.size() != n - t) return false;
+    if ((int)qcols.size() != n - a) return false;
     Mat Q = Mat::identity(n);
-    for (int k = 0; k < n - t; ++k) Q.set_col(t + k, qcols[k]);
+    for (int k = 0; k < n - a; ++k) Q.set_col(a + k, qcols[k]);
     if (!inverse(Q, T2)) return false;
     T1 = mul(A, Q);
     return true;
@@ -960,21 +963,20 @@ int build_plan(int n, const uint64_t *Arows, uint64_t c, size_t elem_bytes,
         return BMMC_OK;
     }
     if (o.route == BMMC_ROUTE_TWO_PASS) {
-        if (o.tile_skew) return BMMC_ERR_INVALID_ARG;  // square tiles only
         Mat T1, T2;
-        if (!factorize(m.A, t, T1, T2)) return BMMC_ERR_INVALID_ARG;
-        // pass 0: T2 relabels segments (complement 0)
-        const int wl = std::min(4 - m.ulog2, t);
+        if (!factorize(m.A, a, b, T1, T2)) return BMMC_ERR_INVALID_ARG;
+        // pass 0: T2 relabels 2^a-unit segments (complement 0)
+        const int wl = std::min(4 - m.ulog2, a);
         build_chunk(T2, 0, m.ulog2, wl, BMMC_KERNEL_CHUNK, &p->pass[0]);
-        // pass 1: T1 is tiled with rows inside {t, ..., 2t-1}
+        // pass 1: T1 is tiled with rows inside {a, ..., a+b-1}
         Mat T1inv;
         inverse(T1, T1inv);
-        u64 H = pad_rows(T1, tile_rows(T1inv, t, t), t, t, false);
-        if (popcount(H) != t) return BMMC_ERR_INVALID_ARG;
+        u64 H = pad_rows(T1, tile_rows(T1inv, a, b), a, b, false);
+        if (popcount(H) != b) return BMMC_ERR_INVALID_ARG;
         std::vector<u64> W;
-        for (int r = t; r < m.nb; ++r)
+        for (int r = a; r < m.nb; ++r)
             if ((H >> r) & 1u) W.push_back(u64(1) << r);
-        int st = build_tiled(T1, m.c, m.ulog2, t, t, W, lc, swz, &p->pass[1]);
+        int st = build_tiled(T1, m.c, m.ulog2, a, b, W, lc, swz, &p->pass[1]);
         if (st != BMMC_OK) return st;
         p->npasses = 2;
         info.passes = 2;

@@ -22,11 +22,13 @@ N_SQUARE = 600
 N_SKEW = 180   # rectangular tiles (tile_skew), drawn from a stream of their own
 N_SPLIT = 160  # one-tile launches staged in LDS half at a time (split_stage)
 N_BUF = 120    # one-tile launches that read the input with buffer loads (buffer_loads)
-N_CASES = N_SQUARE + N_SKEW + N_SPLIT + N_BUF
+N_SKEW2 = 60   # the two-pass route with rectangular tiles
+N_CASES = N_SQUARE + N_SKEW + N_SPLIT + N_BUF + N_SKEW2
 MASTER_SEED = 0x5EED_B44C
 SKEW_SEED = 0x5EED_5CE7
 SPLIT_SEED = 0x5EED_5B17
 BUF_SEED = 0x5EED_B0FF
+SKEW2_SEED = 0x5EED_2BA5
 
 
 @dataclass
@@ -232,6 +234,39 @@ def cases():
             case.options["buffer_loads"] = 1
         except bm.BmmcError:
             pass
+        out.append(case)
+    # the two-pass route with rectangular tiles: the relabel moves segments as
+    # long as the tile's input rows; a skew the library refuses for the
+    # drawn size is brought towards 0 until it accepts one
+    rng = np.random.Generator(np.random.PCG64(SKEW2_SEED))
+    for i in range(N_SKEW2):
+        elem = ELEMS[int(rng.integers(len(ELEMS)))]
+        n = int(rng.integers(10, 19))
+        opts = {"route": bm.ROUTE_TWO_PASS}
+        launch = int(rng.choice([bm.LAUNCH_AUTO, bm.LAUNCH_ONE_TILE, bm.LAUNCH_PERSISTENT,
+                                 bm.LAUNCH_STREAMED]))
+        if launch:
+            opts["launch"] = launch
+        t = int(rng.choice([0, 0, 4, 5, 6, 7]))
+        if t:
+            opts["tile_log2"] = t
+        bmap = int(rng.choice([0, 1, 3, 5, 6, 8]))
+        if bmap:
+            opts["block_map"] = bmap
+        if rng.random() < 0.4:
+            opts["tile_threads_log2"] = 9
+        skew = int(rng.choice([1, -1, 2, -2]))
+        case = Case(N_SQUARE + N_SKEW + N_SPLIT + N_BUF + i, "general", n, elem,
+                    int(rng.integers(1, 1 << 30)), opts)
+        A, c = case.matrix()
+        while skew:
+            try:
+                bm.Plan(n, A, c, elem, tile_skew=skew, **opts)
+                break
+            except bm.BmmcError:
+                skew -= 1 if skew > 0 else -1
+        if skew:
+            case.options["tile_skew"] = skew
         out.append(case)
     return out
 

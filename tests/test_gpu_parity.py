@@ -485,7 +485,9 @@ def test_workload_c4_general30():
     x = wl.workload_data(name)
     _note("c4: oracle")
     want = oracle.apply(A, c, x, threads=HOST_THREADS)
-    for kw in ({}, dict(tune=True), dict(route=bm.ROUTE_TWO_PASS)):
+    for kw in ({}, dict(tune=True), dict(route=bm.ROUTE_TWO_PASS),
+               dict(route=bm.ROUTE_TWO_PASS, tile_log2=7, tile_skew=1, tile_threads_log2=9),
+               dict(route=bm.ROUTE_TWO_PASS, tile_log2=6, tile_skew=-2)):
         _note("c4 %s" % kw)
         got, P = _device_run(name, A, c, x, **kw)
         assert P.info.kind == bm.KIND_GENERAL

@@ -330,6 +330,30 @@ def test_two_pass_factors_multiply_back(n, seed):
         assert d.kernel == (bm.KERNEL_CHUNK if k == 0 else bm.KERNEL_TILED)
 
 
+@pytest.mark.parametrize("skew", [1, -1, 2, -2])
+@pytest.mark.parametrize("n,seed", [(16, 1), (20, 2), (24, 3), (30, 4)])
+def test_two_pass_rectangular_factors(n, seed, skew):
+    """With tiles of input rows of 2^a units and output rows of 2^b (a = t - s,
+    b = t + s), A = T1.T2 still holds, T2 keeps every 2^a-element segment
+    together and T1's tile rows lie in {a, ..., a+b-1}."""
+    A, c = _inv(n, seed)
+    t = 6
+    P = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS, tile_log2=t, tile_skew=skew)
+    assert P.info.passes == 2
+    a, b = t - skew, t + skew
+    (A2, c2), (A1, c1) = P.factors()
+    assert np.array_equal((_dense(A1, n) @ _dense(A2, n)) % 2, _dense(A, n))
+    assert c2 == 0 and c1 == c
+    D2 = _dense(A2, n)
+    assert np.array_equal(D2[:a, :a], np.eye(a, dtype=np.int64))
+    assert not D2[:a, a:].any() and not D2[a:, :a].any()
+    B1 = _dense(oracle.inverse(A1), n)
+    assert not B1[a + b:, :b].any()
+    d0, d1 = P.passes()
+    assert d0.kernel == bm.KERNEL_CHUNK and d1.kernel == bm.KERNEL_TILED
+    assert (d1.in_row_log2, d1.out_row_log2) == (a, b)
+
+
 # --------------------------------------------------------------------------
 # Host replay of the kernel tables against the oracle
 # --------------------------------------------------------------------------
@@ -708,11 +732,17 @@ def test_skew_argument_errors():
     # rows shorter than the kernel's 16-byte chunk are refused
     with pytest.raises(bm.BmmcError):
         bm.Plan(n, A, 0, 4, tile_log2=6, tile_skew=5)
-    # the two-pass route of a general matrix has square tiles only; a BPC
+    # the two-pass route of a general matrix takes rectangular tiles too (its
+    # relabel then moves segments as long as the tile's input rows); a BPC
     # takes one tile pass whatever the route asks, skewed if asked
     G, c = _inv(n, 3)
+    for skew in (1, -1, 2):
+        P = bm.Plan(n, G, c, 4, tile_log2=6, tile_skew=skew, route=bm.ROUTE_TWO_PASS)
+        assert P.info.passes == 2 and P.describe()["tile_skew"] == skew
+        d = P.passes()[1]
+        assert (d.in_row_log2, d.out_row_log2) == (6 - skew, 6 + skew)
     with pytest.raises(bm.BmmcError):
-        bm.Plan(n, G, c, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
+        bm.Plan(n, G, c, 4, tile_log2=6, tile_skew=6, route=bm.ROUTE_TWO_PASS)
     P = bm.Plan(n, A, 0, 4, tile_skew=1, route=bm.ROUTE_TWO_PASS)
     assert P.info.passes == 1 and P.describe()["tile_skew"] == 1
 
@@ -983,8 +1013,10 @@ def test_tune_candidates_keep_what_the_caller_fixed(fixed):
     assert cands
     for k, v in fixed.items():
         if k == "route":
-            assert all(o["tile_skew"] == 0 for o in cands)
+            # two passes each, square and rectangular tiles
+            assert {o["route"] for o in cands} == {v}
             assert all(bm.Plan(n, A, c, 4, **o).info.passes == 2 for o in cands)
+            assert {o["tile_skew"] for o in cands} >= {0, 1, -1}
         else:
             assert {o[k] for o in cands} == {v}, k
     if "block_map" not in fixed:
