@@ -267,6 +267,13 @@ def cases():
                 skew -= 1 if skew > 0 else -1
         if skew:
             case.options["tile_skew"] = skew
+        # some one-tile launches read their input with buffer loads
+        if launch == bm.LAUNCH_ONE_TILE and rng.random() < 0.5:
+            try:
+                bm.Plan(n, A, c, elem, buffer_loads=1, **case.options)
+                case.options["buffer_loads"] = 1
+            except bm.BmmcError:
+                pass
         out.append(case)
     return out
 
