@@ -526,6 +526,54 @@ def test_workload_c4_every_tuning_candidate():
         assert bad.size == 0, (k, opts, int(idx[bad[0]]), P.describe())
 
 
+def test_workload_c4_every_two_pass_candidate():
+    """Every plan the tuning of the pages' two-pass route would time (square
+    and rectangular tiles, thread counts, launches and orders) at the full
+    n = 30 size, on sampled indices gathered on the device."""
+    torch = _torch()
+    name = "c4"
+    n = 30
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == n)
+    x = wl.workload_data(name)
+    d_in = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    d_out = torch.empty_like(d_in)
+    idx = _sample_idx(n, 1 << 18, 32)
+    pos = torch.from_numpy(oracle.map_indices(A, c, idx).astype(np.int64)).to("cuda:0")
+    want = x.reshape(-1)[idx.astype(np.int64)]
+    cands = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS).tune_candidates()
+    assert {o["tile_skew"] for o in cands} >= {0, 1, -1}
+    for k, opts in enumerate(cands):
+        _note("c4 two-pass candidate %d %s" % (k, opts))
+        P = bm.Plan(n, A, c, 4, **opts)
+        assert P.info.passes == 2
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        got = d_out.view(torch.int32).index_select(0, pos).cpu().numpy().view(x.dtype)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (k, opts, int(idx[bad[0]]), P.describe())
+
+
+def test_workload_c1a_every_two_pass_candidate():
+    """Every two-pass tuning candidate of c1a (n = 20), over the whole array."""
+    torch = _torch()
+    name = "c1a"
+    n = 20
+    A, c = wl.workload_matrix(name, accept=lambda r: oracle.rank(r) == n)
+    x = wl.workload_data(name)
+    want = oracle.apply(A, c, x, threads=HOST_THREADS)
+    d_in = torch.from_numpy(x.reshape(-1).view(np.uint8)).to("cuda:0")
+    d_out = torch.empty_like(d_in)
+    cands = bm.Plan(n, A, c, 4, route=bm.ROUTE_TWO_PASS).tune_candidates()
+    assert any(o["buffer_loads"] for o in cands) and any(o["tile_skew"] for o in cands)
+    for k, opts in enumerate(cands):
+        _note("c1a two-pass candidate %d %s" % (k, opts))
+        P = bm.Plan(n, A, c, 4, **opts)
+        d_out.fill_(SENTINEL)
+        P(d_in, d_out)
+        got = d_out.cpu().numpy().view(x.dtype).reshape(x.shape)
+        assert np.array_equal(got, want), (k, opts, P.describe())
+
+
 def test_workload_c5_buffer_loads():
     """c5's slowest permutation (10) with the input read by buffer loads:
     the whole 2 GiB array (the largest the form allows) against the oracle
