@@ -753,7 +753,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+        print("bench.py: the library runs on one GPU only (no sharding or collectives); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.replays < 1:

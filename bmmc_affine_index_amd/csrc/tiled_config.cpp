@@ -1,4 +1,4 @@
-// tiled_config.cpp -- which tile-pass launches this build can run (host-only).
+// tiled_config.cpp -- which tile-pass launches the compiled kernels cover (host-only).
 #include "kernels/tiled_cfg.h"
 #include "launch.h"
 

@@ -38,7 +38,7 @@ extern "C" {
 #define BMMC_OK 0
 #define BMMC_ERR_INVALID_ARG 1   /* n, elem_bytes, stray bits, NULL, alignment */
 #define BMMC_ERR_SINGULAR 2      /* A is not invertible over F2 */
-#define BMMC_ERR_UNSUPPORTED 3   /* a valid request this build cannot run */
+#define BMMC_ERR_UNSUPPORTED 3   /* a valid request no compiled kernel serves */
 #define BMMC_ERR_ALIAS 4         /* the in and out byte ranges overlap */
 #define BMMC_ERR_OUT_OF_MEMORY 5 /* scratch allocation failed */
 #define BMMC_ERR_HIP 6           /* a HIP runtime call or kernel launch failed */
