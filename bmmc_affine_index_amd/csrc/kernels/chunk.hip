@@ -79,11 +79,12 @@ __global__ void __launch_bounds__(1 << kChunkNTL)
     const uint64_t first = (b0 + blockIdx.x) << (kChunkNTL + kChunkCPTL);
     const uint64_t lane_off = dev::xor_bits_lane<kChunkNTL>(tab, tid);
     // A gather needs the wave-uniform part of each group's source offset
-    // before its loads: the whole wave computes it (lane k loads entry k, a
-    // wave XOR reduction keeps the entries of the set bits; the bits of xu
-    // below kChunkNTL are 0), one vector load instead of a chain of scalar
-    // loads, with every lane active, before the guard on the array's end
-    // (measured on MI355X: a 4 MiB block permutation +7%).  A scatter
+    // before its loads.  Past the scalar form's size the whole wave computes
+    // it (lane k loads entry k, a wave XOR reduction keeps the entries of the
+    // set bits; the bits of xu below kChunkNTL are 0), one vector load instead
+    // of a chain of dependent scalar loads, with every lane active, before the
+    // guard on the array's end (measured on MI355X against that chain: a 4 MiB
+    // block permutation +7%).  A scatter
     // computes its output base from scalar loads after issuing its loads,
     // which hides them (the wave form cost a 4 MiB reversal 10%).
     uint64_t ubase[CPT] = {};
