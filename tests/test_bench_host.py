@@ -238,6 +238,12 @@ def test_traffic_summary_round_trip(tmp_path, monkeypatch):
         assert got == pytest.approx(2 * nbytes * (1.0 + 0.01 * k), rel=1e-6)
     # a plan that was not counted has no traffic
     assert bench.read_traffic("c2", cands[0]["plan_options"], "0" * 16) is None
+    # the compact form: one table row per candidate with its ratio, no entries
+    compact = bench_profiles.traffic_summary("c2", [tuple(dirs)], ["cmd"], compact=True)
+    assert "[entry]" not in compact
+    ratios = [float(line.rsplit("|", 2)[1]) for line in compact.splitlines()
+              if line.startswith("| ") and line[2].isdigit()]
+    assert ratios == pytest.approx([1.0 + 0.01 * k for k in range(len(cands))], rel=1e-5)
     # candidates that do not match the runs' copies are refused
     bad = dict(line, candidates=cands[:2])
     (tmp_path / "FETCH_SIZE" / "candidates.json").write_text(json.dumps(bad) + "\n")
